@@ -1,0 +1,179 @@
+"""fp64 CPU oracle of the gated DeltaNet token mixer (ctypes over gdn_oracle.c).
+
+TEST INFRASTRUCTURE. Only the test suite, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package. It shares no code
+with the HIP library and imports nothing from it; it takes plain numpy arrays.
+
+The arithmetic lives in ``gdn_oracle.c`` (fp64, libm only). This wrapper only
+converts arrays to contiguous fp64, allocates outputs and calls the C entry
+points; ``layer`` chains the three steps in the order the xwen CLAUDE.md page
+lists them (section "Architecture cheat sheet", gated DeltaNet paragraph).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdn_oracle.c")
+_LIB = os.path.join(_HERE, "libgdn_oracle.so")
+
+CONV_K = 4
+L2_EPS = 1e-6
+NORM_EPS = 1e-6
+
+_lib = None
+
+
+def build(force: bool = False, src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the oracle with gcc (plain -O2, IEEE semantics, no fast-math)."""
+    if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(src):
+        tmp = out + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", "-O2", "-std=c99", "-fno-fast-math", "-ffp-contract=off",
+                        "-shared", "-fPIC", "-o", tmp, src, "-lm"], check=True)
+        os.replace(tmp, out)
+    return out
+
+
+_D = ctypes.POINTER(ctypes.c_double)
+_I = ctypes.POINTER(ctypes.c_int)
+
+
+def load(path: Optional[str] = None):
+    """Load (building if needed) the oracle library. ``path`` loads another build."""
+    global _lib
+    if path is None and _lib is not None:
+        return _lib
+    lib = ctypes.CDLL(path or build())
+    lib.gdno_conv_gate_prep.argtypes = [ctypes.c_int, _I, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        _D, _D, _D, _D, _D, _D, _D, ctypes.c_double,
+                                        _D, _D, _D, _D, _D, _D]
+    lib.gdno_conv_gate_prep.restype = None
+    lib.gdno_delta_rule.argtypes = [ctypes.c_int, _I, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    _D, _D, _D, _D, _D, _D, _D, _D, _I, _D]
+    lib.gdno_delta_rule.restype = None
+    lib.gdno_gated_rmsnorm.argtypes = [ctypes.c_long, ctypes.c_int, _D, _D, _D, ctypes.c_double, _D]
+    lib.gdno_gated_rmsnorm.restype = None
+    for f in ("gdno_sigmoid", "gdno_softplus", "gdno_silu"):
+        getattr(lib, f).argtypes = [ctypes.c_double]
+        getattr(lib, f).restype = ctypes.c_double
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _f64(x) -> np.ndarray:
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _p(x: np.ndarray):
+    return x.ctypes.data_as(_D)
+
+
+def _cu(cu) -> np.ndarray:
+    return np.ascontiguousarray(cu, dtype=np.int32)
+
+
+class Oracle:
+    """Bound to one build of the oracle library (the default, or a test variant)."""
+
+    def __init__(self, path: Optional[str] = None):
+        self.lib = load(path)
+
+    def sigmoid(self, x: float) -> float:
+        return self.lib.gdno_sigmoid(float(x))
+
+    def softplus(self, x: float) -> float:
+        return self.lib.gdno_softplus(float(x))
+
+    def silu(self, x: float) -> float:
+        return self.lib.gdno_silu(float(x))
+
+    def conv_gate_prep(self, cu, n_qk_heads: int, n_v_heads: int, head_dim: int,
+                       qkv, b, a, conv_w, dt_bias, A_log, conv_in, l2_eps: float = L2_EPS):
+        """Conv + SiLU + split + L2 clamp-norm + gates. Returns a dict of fp64 arrays."""
+        cu = _cu(cu)
+        N, T = len(cu) - 1, int(cu[-1])
+        Hqk, Hv, d = n_qk_heads, n_v_heads, head_dim
+        C = d * (2 * Hqk + Hv)
+        qkv, b, a = _f64(qkv).reshape(T, C), _f64(b).reshape(T, Hv), _f64(a).reshape(T, Hv)
+        conv_w, dt_bias, A_log = _f64(conv_w).reshape(C, CONV_K), _f64(dt_bias), _f64(A_log)
+        conv_in = _f64(conv_in).reshape(N, CONV_K - 1, C)
+        out = dict(conv_out=np.empty((N, CONV_K - 1, C)), q=np.empty((T, Hqk, d)),
+                   k=np.empty((T, Hqk, d)), v=np.empty((T, Hv, d)),
+                   beta=np.empty((T, Hv)), g=np.empty((T, Hv)))
+        self.lib.gdno_conv_gate_prep(N, cu.ctypes.data_as(_I), Hqk, Hv, d, _p(qkv), _p(b), _p(a),
+                                     _p(conv_w), _p(dt_bias), _p(A_log), _p(conv_in), float(l2_eps),
+                                     _p(out["conv_out"]), _p(out["q"]), _p(out["k"]), _p(out["v"]),
+                                     _p(out["beta"]), _p(out["g"]))
+        return out
+
+    def delta_rule(self, cu, n_qk_heads: int, n_v_heads: int, head_dim: int,
+                   q, k, v, beta, g, S_in, heads: Optional[Sequence[int]] = None):
+        """Recurrent delta rule. Returns (o [T,Hv,d], S_out [N,Hv,d,d]).
+
+        ``heads``: compute only these V-heads (others of o / S_out are NaN).
+        """
+        cu = _cu(cu)
+        N, T = len(cu) - 1, int(cu[-1])
+        Hqk, Hv, d = n_qk_heads, n_v_heads, head_dim
+        q, k = _f64(q).reshape(T, Hqk, d), _f64(k).reshape(T, Hqk, d)
+        v, beta, g = _f64(v).reshape(T, Hv, d), _f64(beta).reshape(T, Hv), _f64(g).reshape(T, Hv)
+        S_in = _f64(S_in).reshape(N, Hv, d, d)
+        o = np.full((T, Hv, d), np.nan)
+        S_out = np.full((N, Hv, d, d), np.nan)
+        sel = None
+        if heads is not None:
+            sel = np.zeros(Hv, np.int32)
+            sel[list(heads)] = 1
+        work = np.empty(d * d + 2 * d)
+        self.lib.gdno_delta_rule(N, cu.ctypes.data_as(_I), Hqk, Hv, d, _p(q), _p(k), _p(v),
+                                 _p(beta), _p(g), _p(S_in), _p(S_out), _p(o),
+                                 sel.ctypes.data_as(_I) if sel is not None else None, _p(work))
+        return o, S_out
+
+    def gated_rmsnorm(self, o, z, w, eps: float = NORM_EPS):
+        """Gated RMSNorm over the last axis (length d). Returns y, same shape as o."""
+        o = _f64(o)
+        d = o.shape[-1]
+        z = _f64(z).reshape(o.shape)
+        w = _f64(w)
+        y = np.empty_like(o)
+        self.lib.gdno_gated_rmsnorm(o.size // d, d, _p(o), _p(z), _p(w), float(eps), _p(y))
+        return y
+
+    def layer(self, cu, n_qk_heads: int, n_v_heads: int, head_dim: int, qkv, z, b, a,
+              conv_w, dt_bias, A_log, norm_w, conv_in, S_in, heads=None,
+              l2_eps: float = L2_EPS, norm_eps: float = NORM_EPS):
+        """The whole mixer: prep, recurrent delta rule, gated RMSNorm. fp64 dict out."""
+        r = self.conv_gate_prep(cu, n_qk_heads, n_v_heads, head_dim, qkv, b, a, conv_w,
+                                dt_bias, A_log, conv_in, l2_eps)
+        o, S_out = self.delta_rule(cu, n_qk_heads, n_v_heads, head_dim, r["q"], r["k"], r["v"],
+                                   r["beta"], r["g"], S_in, heads=heads)
+        T = int(_cu(cu)[-1])
+        zz = _f64(z).reshape(T, n_v_heads, head_dim)
+        if heads is None:
+            y = self.gated_rmsnorm(o, zz, norm_w, norm_eps)
+        else:
+            y = np.full_like(o, np.nan)
+            hs = list(heads)
+            y[:, hs] = self.gated_rmsnorm(o[:, hs], zz[:, hs], norm_w, norm_eps)
+        r.update(o=o, S_out=S_out, y=y)
+        return r
+
+
+_default: Optional[Oracle] = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default
+
+
+__all__ = ["Oracle", "default", "build", "load", "CONV_K", "L2_EPS", "NORM_EPS"]
