@@ -1,0 +1,223 @@
+"""Benchmark of the gated DeltaNet token mixer on one MI355X.
+
+One step = one pass of the whole mixer over the prefill workload
+(T = 4096 tokens, 16 K-heads, 48 V-heads, bf16 activations, one sequence):
+gdn_conv_gate_prep -> gdn_prefill_chunked -> gdn_gated_rmsnorm, inputs
+already resident in HBM. ``value`` is tokens per second over exactly
+``--steps`` timed steps after ``--warmup`` untimed ones.
+
+The same run also times the decode path (gdn_conv_gate_prep ->
+gdn_decode_step -> gdn_gated_rmsnorm per token) on the batch-1 workload
+(32 V-heads, 1024 consecutive steps) and the batch-64 workload (256 steps),
+and reports them under "decode".
+
+Rooflines use the kernels' algorithmic work, timed with HIP events recorded
+on the stream the kernels run on:
+  * chunked delta rule (gdn_prefill_chunked): 9,000,277 flop per
+    (chunk of 64, V-head) -- 5 CH^2 d + 6 CH d^2 + CH^3/3 with CH = 64,
+    d = 128, triangles counted once -- against the bf16 dense MFMA peak;
+  * decode step (gdn_decode_step): bytes of S read + written, q, k, v, beta,
+    g read and o written, against 8 TB/s HBM.
+The CPU baseline is the fp64 oracle, single-threaded, over the whole prefill
+workload once.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+from gated_deltanet_layer_amd import binding as B  # noqa: E402
+from gated_deltanet_layer_amd import layer as Lyr  # noqa: E402
+from gated_deltanet_layer_amd import workloads as wl  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+CHUNK = 64
+FLOP_PER_CHUNK_HEAD = 5 * CHUNK ** 2 * 128 + 6 * CHUNK * 128 ** 2 + CHUNK ** 3 // 3   # 9,000,277
+
+
+def dev(x: np.ndarray) -> torch.Tensor:
+    if x.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def bench_prefill(steps: int, warmup: int):
+    w = wl.WORKLOADS[3]
+    x = wl.generate(w)
+    t = {k: dev(v) for k, v in x.items()}
+    cfg = B.make_config(w.n_qk_heads, w.n_v_heads, w.act)
+    T = int(x["cu_seqlens"][-1])
+    run = Lyr.Prefill(cfg, 1, T)
+    conv_out = torch.empty_like(t["conv0"])
+    S_out = torch.empty_like(t["S0"])
+    args = (t["cu_seqlens"], t["qkv"], t["b"], t["a"], t["conv_w"], t["dt_bias"], t["A_log"], t["conv0"], conv_out)
+
+    def step(evs=None):
+        run.prep(*args)
+        if evs is not None:
+            evs[0].record()
+        run.core(t["cu_seqlens"], t["S0"], S_out)
+        if evs is not None:
+            evs[1].record()
+        run.norm(t["z"], t["norm_w"])
+
+    for _ in range(warmup):
+        step()
+    core_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        step(core_ev[i])
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    core_ms = float(np.mean([a.elapsed_time(b) for a, b in core_ev]))
+    n_chunk_heads = ((T + CHUNK - 1) // CHUNK) * w.n_v_heads
+    flops = FLOP_PER_CHUNK_HEAD * n_chunk_heads
+    achieved = flops / (core_ms * 1e-3) / 1e12
+    return dict(total_ms=total_ms, ms_per_step=total_ms / steps, tokens=T, core_ms=core_ms,
+                roofline={"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+                          "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                          "kernel": "gdn_prefill_chunked (chunk_local + chunk_state)",
+                          "flop_per_launch": flops, "avg_launch_us": round(core_ms * 1e3, 2)})
+
+
+def decode_kernel_bytes(w: wl.Workload) -> int:
+    N, Hqk, Hv, d = w.n_seqs, w.n_qk_heads, w.n_v_heads, w.head_dim
+    act = 2 if w.act == "bf16" else 4
+    return (2 * N * Hv * d * d * 4 + 2 * N * Hqk * d * 4 + N * Hv * d * 4 + 2 * N * Hv * 4
+            + N * Hv * d * act)
+
+
+def bench_decode(wid: int, warmup_steps: int = 32):
+    w = wl.WORKLOADS[wid]
+    x = wl.generate(w)
+    t = {k: dev(v) for k, v in x.items()}
+    cfg = B.make_config(w.n_qk_heads, w.n_v_heads, w.act)
+    run = Lyr.Decode(cfg, w.n_seqs)
+    conv, S = t["conv0"].clone(), t["S0"].clone()
+    ys = torch.empty_like(t["z"])
+    steps = w.steps
+
+    def one(s, evs=None):
+        B.gdn_conv_gate_prep(cfg, w.n_seqs, w.n_seqs, run.cu, t["qkv"][s], t["b"][s], t["a"][s], t["conv_w"],
+                             t["dt_bias"], t["A_log"], conv, conv, run.q, run.k, run.v, run.beta, run.g)
+        if evs is not None:
+            evs[0].record()
+        B.gdn_decode_step(cfg, w.n_seqs, run.q, run.k, run.v, run.beta, run.g, S, S, run.o)
+        if evs is not None:
+            evs[1].record()
+        B.gdn_gated_rmsnorm(cfg, w.n_seqs * w.n_v_heads, run.o, t["z"][s], t["norm_w"], ys[s])
+
+    for s in range(min(warmup_steps, steps)):
+        one(s)
+    conv.copy_(t["conv0"])
+    S.copy_(t["S0"])
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for s in range(steps):
+        one(s, evs[s])
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    nbytes = decode_kernel_bytes(w)
+    gbs = nbytes / (k_ms * 1e-3) / 1e9
+    return {"workload": w.name, "tokens_per_s": round(w.n_seqs * steps / (total_ms * 1e-3), 1),
+            "us_per_step": round(total_ms * 1e3 / steps, 2),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "gdn_decode_step",
+                         "bytes_per_launch": nbytes, "avg_launch_us": round(k_ms * 1e3, 2)}}
+
+
+def cpu_baseline():
+    import oracle
+    w = wl.WORKLOADS[3]
+    x = wl.generate(w)
+    xf = {}
+    for k, v in x.items():
+        if k in ("qkv", "z", "b", "a", "conv0"):
+            xf[k] = wl.as_f32(v, w.act).astype(np.float64)
+        elif v.dtype == np.int32:
+            xf[k] = v
+        else:
+            xf[k] = v.astype(np.float64)
+    orc = oracle.default()
+    t0 = time.perf_counter()
+    orc.layer(xf["cu_seqlens"], w.n_qk_heads, w.n_v_heads, w.head_dim, xf["qkv"], xf["z"], xf["b"], xf["a"],
+              xf["conv_w"], xf["dt_bias"], xf["A_log"], xf["norm_w"], xf["conv0"], xf["S0"])
+    dt = time.perf_counter() - t0
+    T = int(x["cu_seqlens"][-1])
+    return {"value": round(T / dt, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"the whole prefill workload once ({T} tokens x 48 V-heads), fp64, one thread, "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the oracle")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only: the mixer's path here runs on a single MI355X; "
+              f"--gpus {a.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    B.load()
+    log("prefill workload: T=4096 Hqk=16 Hv=48 bf16")
+    pre = bench_prefill(a.steps, a.warmup)
+    log(f"prefill: {pre['ms_per_step']:.3f} ms/step, core {pre['core_ms'] * 1e3:.1f} us")
+    decode = None
+    if not a.no_decode:
+        decode = []
+        for wid in (2, 4):
+            log(f"decode workload {wid}")
+            decode.append(bench_decode(wid))
+            log(json.dumps(decode[-1]))
+    cpu = None
+    if not a.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline()
+    line = {
+        "metric": "GDN layer tokens/s: prefill T=4096 & decode step; % HBM/MFMA roofline",
+        "value": round(pre["tokens"] * a.steps / (pre["total_ms"] * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(pre["ms_per_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 in/out, fp32 state and arithmetic", "data": "synthetic (seeded)",
+        "config": {"workload": "prefill T=4096, 1 sequence, Hqk=16, Hv=48, d=128, chunk 64, bf16, zero states",
+                   "global_batch": 1, "seq_len": pre["tokens"], "parallelism": "single GPU"},
+        "roofline": pre["roofline"],
+        "decode": decode,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

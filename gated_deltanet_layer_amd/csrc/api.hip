@@ -1,0 +1,252 @@
+// api.hip -- the C ABI declared in include/gdn.h: host-side argument checks,
+// then asynchronous launches on the caller's stream. Nothing here allocates,
+// synchronises, prints or aborts.
+#include <math.h>
+#include <stdint.h>
+
+#include "gdn.h"
+#include "gdn_internal.h"
+
+namespace {
+
+using gdn::kHeadDim;
+
+constexpr int64_t kMaxGrid = 0x7fffffff;
+
+bool finite_nonneg(float x) { return isfinite(x) && x >= 0.0f; }
+
+gdn_status check_config(const gdn_config *cfg) {
+  if (!cfg) return GDN_E_INVALID_ARG;
+  if (cfg->n_qk_heads < 1 || cfg->n_v_heads < 1) return GDN_E_INVALID_ARG;
+  if (cfg->n_v_heads % cfg->n_qk_heads != 0) return GDN_E_INVALID_ARG;
+  if (cfg->act_dtype != GDN_F32 && cfg->act_dtype != GDN_BF16) return GDN_E_INVALID_ARG;
+  if (!finite_nonneg(cfg->l2_eps) || !finite_nonneg(cfg->norm_eps)) return GDN_E_INVALID_ARG;
+  if (cfg->head_dim != kHeadDim) return GDN_E_UNSUPPORTED;
+  if (cfg->conv_kernel != gdn::kConvK) return GDN_E_UNSUPPORTED;
+  // Grid y of the prep kernel is the number of 128-channel head blocks.
+  if (2LL * cfg->n_qk_heads + cfg->n_v_heads > 65535) return GDN_E_UNSUPPORTED;
+  return GDN_OK;
+}
+
+size_t act_size(const gdn_config *cfg) { return cfg->act_dtype == GDN_BF16 ? 2 : 4; }
+
+// [a, a + na) and [b, b + nb) overlap (byte ranges; null or empty never does).
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+struct Range {
+  const void *p;
+  size_t n;
+};
+
+// Any overlap among the outputs, or between an output and an input.
+template <size_t NO, size_t NI>
+bool any_overlap(const Range (&outs)[NO], const Range (&ins)[NI]) {
+  for (size_t i = 0; i < NO; ++i) {
+    for (size_t j = i + 1; j < NO; ++j)
+      if (overlap(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return true;
+    for (size_t j = 0; j < NI; ++j)
+      if (overlap(outs[i].p, outs[i].n, ins[j].p, ins[j].n)) return true;
+  }
+  return false;
+}
+
+gdn_status launched(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_E_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+gdn_config gdn_default_config(int32_t n_qk_heads, int32_t n_v_heads, gdn_dtype act) {
+  gdn_config c;
+  c.n_qk_heads = n_qk_heads;
+  c.n_v_heads = n_v_heads;
+  c.head_dim = kHeadDim;
+  c.conv_kernel = gdn::kConvK;
+  c.l2_eps = 1e-6f;
+  c.norm_eps = 1e-6f;
+  c.act_dtype = act;
+  return c;
+}
+
+const char *gdn_status_string(gdn_status s) {
+  switch (s) {
+    case GDN_OK: return "ok";
+    case GDN_E_INVALID_ARG: return "invalid argument";
+    case GDN_E_UNSUPPORTED: return "unsupported configuration";
+    case GDN_E_HIP: return "HIP launch or runtime error";
+    case GDN_E_WORKSPACE: return "workspace missing or too small";
+  }
+  return "unknown status";
+}
+
+const char *gdn_version(void) { return "gdn-mi355x 0.1 (gfx950)"; }
+
+gdn_status gdn_conv_gate_prep(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens,
+                              const int32_t *cu_seqlens, const void *qkv, const void *beta_logit,
+                              const void *alpha_logit, const float *conv_w, const float *dt_bias,
+                              const float *A_log, const void *conv_state_in, void *conv_state_out,
+                              float *q, float *k, float *v, float *beta, float *g,
+                              gdn_stream_t stream) {
+  const gdn_status cs = check_config(cfg);
+  if (cs != GDN_OK) return cs;
+  if (n_seqs < 0 || n_tokens < 0) return GDN_E_INVALID_ARG;
+  if (n_seqs == 0) return n_tokens == 0 ? GDN_OK : GDN_E_INVALID_ARG;
+  if (!cu_seqlens || !conv_w || !dt_bias || !A_log || !conv_state_in || !conv_state_out)
+    return GDN_E_INVALID_ARG;
+  if (n_tokens > 0 && (!qkv || !beta_logit || !alpha_logit || !q || !k || !v || !beta || !g))
+    return GDN_E_INVALID_ARG;
+  const int Hqk = cfg->n_qk_heads, Hv = cfg->n_v_heads;
+  const size_t C = static_cast<size_t>(kHeadDim) * (2 * Hqk + Hv);
+  const size_t T = static_cast<size_t>(n_tokens), as = act_size(cfg);
+  const int64_t tiles = (static_cast<int64_t>(n_tokens) + gdn::kPrepTile - 1) / gdn::kPrepTile + n_seqs;
+  if (tiles > kMaxGrid) return GDN_E_UNSUPPORTED;
+  const size_t st = static_cast<size_t>(n_seqs) * (gdn::kConvK - 1) * C * as;
+  const Range outs[] = {{q, T * Hqk * kHeadDim * 4}, {k, T * Hqk * kHeadDim * 4}, {v, T * Hv * kHeadDim * 4},
+                        {beta, T * Hv * 4}, {g, T * Hv * 4}};
+  const Range ins[] = {{qkv, T * C * as}, {beta_logit, T * Hv * as}, {alpha_logit, T * Hv * as},
+                       {conv_w, C * 4 * 4}, {dt_bias, Hv * 4u}, {A_log, Hv * 4u},
+                       {cu_seqlens, (n_seqs + 1u) * 4u}, {conv_state_in, st}, {conv_state_out, st}};
+  if (any_overlap(outs, ins)) return GDN_E_INVALID_ARG;
+  // The conv state may be updated in place, but must not partly overlap.
+  if (conv_state_in != conv_state_out && overlap(conv_state_in, st, conv_state_out, st)) return GDN_E_INVALID_ARG;
+  for (const Range &r : ins)
+    if (r.p != conv_state_out && r.p != conv_state_in && overlap(r.p, r.n, conv_state_out, st)) return GDN_E_INVALID_ARG;
+
+  gdn::PrepParams p;
+  p.cu = cu_seqlens;
+  p.n_seqs = n_seqs;
+  p.n_tokens = n_tokens;
+  p.n_qk = Hqk;
+  p.n_v = Hv;
+  p.qkv = qkv;
+  p.b = beta_logit;
+  p.a = alpha_logit;
+  p.conv_w = conv_w;
+  p.dt_bias = dt_bias;
+  p.A_log = A_log;
+  p.st_in = conv_state_in;
+  p.st_out = conv_state_out;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.beta = beta;
+  p.g = g;
+  p.l2_eps = cfg->l2_eps;
+  return launched(gdn::launch_prep(p, cfg->act_dtype, static_cast<hipStream_t>(stream)));
+}
+
+size_t gdn_prefill_workspace_bytes(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens) {
+  if (check_config(cfg) != GDN_OK || n_seqs < 0 || n_tokens < 0) return 0;
+  if (n_tokens == 0) return 0;
+  return gdn::prefill_workspace_bytes(n_seqs, n_tokens, cfg->n_v_heads);
+}
+
+gdn_status gdn_prefill_chunked(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens,
+                               const int32_t *cu_seqlens, const float *q, const float *k, const float *v,
+                               const float *beta, const float *g, const float *S_in, float *S_out, void *o,
+                               void *workspace, size_t workspace_bytes, gdn_stream_t stream) {
+  const gdn_status cs = check_config(cfg);
+  if (cs != GDN_OK) return cs;
+  if (n_seqs < 0 || n_tokens < 0) return GDN_E_INVALID_ARG;
+  if (n_seqs == 0) return n_tokens == 0 ? GDN_OK : GDN_E_INVALID_ARG;
+  if (!cu_seqlens || !S_in || !S_out) return GDN_E_INVALID_ARG;
+  if (n_tokens > 0 && (!q || !k || !v || !beta || !g || !o)) return GDN_E_INVALID_ARG;
+  const int Hqk = cfg->n_qk_heads, Hv = cfg->n_v_heads;
+  const size_t need = gdn_prefill_workspace_bytes(cfg, n_seqs, n_tokens);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_E_WORKSPACE;
+  const int64_t chunks = gdn::max_chunks(n_seqs, n_tokens);
+  if (chunks > kMaxGrid || Hqk > 65535 ||
+      static_cast<int64_t>(n_seqs) * Hv * (kHeadDim / 32) > kMaxGrid)
+    return GDN_E_UNSUPPORTED;
+  const size_t T = static_cast<size_t>(n_tokens);
+  const size_t sb = static_cast<size_t>(n_seqs) * Hv * kHeadDim * kHeadDim * 4;
+  const Range outs[] = {{o, T * Hv * kHeadDim * act_size(cfg)}, {workspace, need}};
+  const Range ins[] = {{q, T * Hqk * kHeadDim * 4}, {k, T * Hqk * kHeadDim * 4}, {v, T * Hv * kHeadDim * 4},
+                       {beta, T * Hv * 4}, {g, T * Hv * 4}, {cu_seqlens, (n_seqs + 1u) * 4u},
+                       {S_in, sb}, {S_out, sb}};
+  if (any_overlap(outs, ins)) return GDN_E_INVALID_ARG;
+  if (S_in != S_out && overlap(S_in, sb, S_out, sb)) return GDN_E_INVALID_ARG;
+  for (size_t i = 0; i < 6; ++i)
+    if (overlap(ins[i].p, ins[i].n, S_out, sb)) return GDN_E_INVALID_ARG;
+
+  gdn::PrefillParams p;
+  p.cu = cu_seqlens;
+  p.n_seqs = n_seqs;
+  p.n_tokens = n_tokens;
+  p.n_qk = Hqk;
+  p.n_v = Hv;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.beta = beta;
+  p.g = g;
+  p.S_in = S_in;
+  p.S_out = S_out;
+  p.o = o;
+  p.ws = workspace;
+  p.ws_bytes = workspace_bytes;
+  return launched(gdn::launch_prefill(p, cfg->act_dtype, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_decode_step(const gdn_config *cfg, int32_t n_seqs, const float *q, const float *k,
+                           const float *v, const float *beta, const float *g, const float *S_in,
+                           float *S_out, void *o, gdn_stream_t stream) {
+  const gdn_status cs = check_config(cfg);
+  if (cs != GDN_OK) return cs;
+  if (n_seqs < 0) return GDN_E_INVALID_ARG;
+  if (n_seqs == 0) return GDN_OK;
+  if (!q || !k || !v || !beta || !g || !S_in || !S_out || !o) return GDN_E_INVALID_ARG;
+  const int Hqk = cfg->n_qk_heads, Hv = cfg->n_v_heads;
+  if (static_cast<int64_t>(n_seqs) * Hv * (kHeadDim / 32) > kMaxGrid) return GDN_E_UNSUPPORTED;
+  const size_t N = static_cast<size_t>(n_seqs);
+  const size_t sb = N * Hv * kHeadDim * kHeadDim * 4;
+  const Range outs[] = {{o, N * Hv * kHeadDim * act_size(cfg)}};
+  const Range ins[] = {{q, N * Hqk * kHeadDim * 4}, {k, N * Hqk * kHeadDim * 4}, {v, N * Hv * kHeadDim * 4},
+                       {beta, N * Hv * 4}, {g, N * Hv * 4}, {S_in, sb}, {S_out, sb}};
+  if (any_overlap(outs, ins)) return GDN_E_INVALID_ARG;
+  if (S_in != S_out && overlap(S_in, sb, S_out, sb)) return GDN_E_INVALID_ARG;
+  for (size_t i = 0; i < 5; ++i)
+    if (overlap(ins[i].p, ins[i].n, S_out, sb)) return GDN_E_INVALID_ARG;
+
+  gdn::DecodeParams p;
+  p.n_seqs = n_seqs;
+  p.n_qk = Hqk;
+  p.n_v = Hv;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.beta = beta;
+  p.g = g;
+  p.S_in = S_in;
+  p.S_out = S_out;
+  p.o = o;
+  return launched(gdn::launch_decode(p, cfg->act_dtype, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_gated_rmsnorm(const gdn_config *cfg, int64_t n_rows, const void *o, const void *z,
+                             const float *norm_w, void *y, gdn_stream_t stream) {
+  const gdn_status cs = check_config(cfg);
+  if (cs != GDN_OK) return cs;
+  if (n_rows < 0) return GDN_E_INVALID_ARG;
+  if (n_rows == 0) return GDN_OK;
+  if (!o || !z || !norm_w || !y) return GDN_E_INVALID_ARG;
+  if ((n_rows + 3) / 4 > kMaxGrid) return GDN_E_UNSUPPORTED;
+  const size_t bytes = static_cast<size_t>(n_rows) * kHeadDim * act_size(cfg);
+  // y may be o (in place); nothing else may overlap y.
+  if (y != o && overlap(y, bytes, o, bytes)) return GDN_E_INVALID_ARG;
+  if (overlap(y, bytes, z, bytes) || overlap(y, bytes, norm_w, kHeadDim * 4)) return GDN_E_INVALID_ARG;
+  gdn::NormParams p;
+  p.n_rows = n_rows;
+  p.o = o;
+  p.z = z;
+  p.w = norm_w;
+  p.y = y;
+  p.eps = cfg->norm_eps;
+  return launched(gdn::launch_norm(p, cfg->act_dtype, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,69 @@
+// gdn_internal.h -- host-side launch interface between the C ABI (api.hip)
+// and the kernel files. Every launcher enqueues on `stream` and returns the
+// launch status; argument checking has already been done by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gdn.h"
+
+namespace gdn {
+
+constexpr int kWave = 64;      // wavefront width on CDNA
+constexpr int kHeadDim = 128;  // the only head dim the page's models use
+constexpr int kConvK = 4;      // conv kernel size
+
+// Token tile of the prep kernel and chunk length of the chunked delta rule.
+constexpr int kPrepTile = 16;
+constexpr int kChunk = 64;
+
+struct PrepParams {
+  const int32_t *cu;
+  int n_seqs, n_tokens, n_qk, n_v;
+  const void *qkv, *b, *a;
+  const float *conv_w, *dt_bias, *A_log;
+  const void *st_in;
+  void *st_out;
+  float *q, *k, *v, *beta, *g;
+  float l2_eps;
+};
+hipError_t launch_prep(const PrepParams &p, gdn_dtype act, hipStream_t s);
+
+struct DecodeParams {
+  int n_seqs, n_qk, n_v;
+  const float *q, *k, *v, *beta, *g;
+  const float *S_in;
+  float *S_out;
+  void *o;
+};
+hipError_t launch_decode(const DecodeParams &p, gdn_dtype act, hipStream_t s);
+
+struct NormParams {
+  int64_t n_rows;
+  const void *o, *z;
+  const float *w;
+  void *y;
+  float eps;
+};
+hipError_t launch_norm(const NormParams &p, gdn_dtype act, hipStream_t s);
+
+struct PrefillParams {
+  const int32_t *cu;
+  int n_seqs, n_tokens, n_qk, n_v;
+  const float *q, *k, *v, *beta, *g;
+  const float *S_in;
+  float *S_out;
+  void *o;
+  void *ws;
+  size_t ws_bytes;
+};
+// Upper bound on the number of chunks over all sequences.
+inline int64_t max_chunks(int n_seqs, int n_tokens) {
+  return (static_cast<int64_t>(n_tokens) + kChunk - 1) / kChunk + n_seqs;
+}
+size_t prefill_workspace_bytes(int n_seqs, int n_tokens, int n_v);
+hipError_t launch_prefill(const PrefillParams &p, gdn_dtype act, hipStream_t s);
+
+}  // namespace gdn

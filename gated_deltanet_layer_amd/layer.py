@@ -1,0 +1,75 @@
+"""Chained calls of the C ABI over preallocated device buffers.
+
+``Prefill`` runs gdn_conv_gate_prep -> gdn_prefill_chunked -> gdn_gated_rmsnorm
+over packed sequences; ``Decode`` runs gdn_conv_gate_prep -> gdn_decode_step ->
+gdn_gated_rmsnorm for one token per sequence. Both allocate their
+intermediates (q, k, v, beta, g, o, y, workspace) once with torch and then only
+call the library, so a timed loop allocates nothing.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import binding as B
+
+
+def _act(cfg):
+    return torch.bfloat16 if cfg.act_dtype == B.GDN_BF16 else torch.float32
+
+
+class Prefill:
+    def __init__(self, cfg: B.gdn_config, n_seqs: int, n_tokens: int, device="cuda"):
+        self.cfg, self.N, self.T = cfg, n_seqs, n_tokens
+        Hqk, Hv, d = cfg.n_qk_heads, cfg.n_v_heads, cfg.head_dim
+        f32 = dict(dtype=torch.float32, device=device)
+        self.q = torch.empty(n_tokens, Hqk, d, **f32)
+        self.k = torch.empty(n_tokens, Hqk, d, **f32)
+        self.v = torch.empty(n_tokens, Hv, d, **f32)
+        self.beta = torch.empty(n_tokens, Hv, **f32)
+        self.g = torch.empty(n_tokens, Hv, **f32)
+        self.o = torch.empty(n_tokens, Hv, d, dtype=_act(cfg), device=device)
+        self.y = torch.empty(n_tokens, Hv, d, dtype=_act(cfg), device=device)
+        wsb = B.gdn_prefill_workspace_bytes(cfg, n_seqs, n_tokens)
+        self.ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=device) if wsb else None
+
+    def prep(self, cu, qkv, b, a, conv_w, dt_bias, A_log, conv_in, conv_out, stream=None):
+        B.gdn_conv_gate_prep(self.cfg, self.N, self.T, cu, qkv, b, a, conv_w, dt_bias, A_log,
+                             conv_in, conv_out, self.q, self.k, self.v, self.beta, self.g, stream)
+
+    def core(self, cu, S_in, S_out, stream=None):
+        B.gdn_prefill_chunked(self.cfg, self.N, self.T, cu, self.q, self.k, self.v, self.beta, self.g,
+                              S_in, S_out, self.o, self.ws, stream)
+
+    def norm(self, z, norm_w, stream=None):
+        B.gdn_gated_rmsnorm(self.cfg, self.T * self.cfg.n_v_heads, self.o, z, norm_w, self.y, stream)
+
+    def __call__(self, cu, qkv, z, b, a, conv_w, dt_bias, A_log, norm_w, conv_in, conv_out, S_in, S_out,
+                 stream=None):
+        self.prep(cu, qkv, b, a, conv_w, dt_bias, A_log, conv_in, conv_out, stream)
+        self.core(cu, S_in, S_out, stream)
+        self.norm(z, norm_w, stream)
+        return self.y
+
+
+class Decode:
+    """One token for each of n_seqs sequences per call; states updated in place."""
+
+    def __init__(self, cfg: B.gdn_config, n_seqs: int, device="cuda"):
+        self.cfg, self.N = cfg, n_seqs
+        Hqk, Hv, d = cfg.n_qk_heads, cfg.n_v_heads, cfg.head_dim
+        f32 = dict(dtype=torch.float32, device=device)
+        self.cu = torch.arange(n_seqs + 1, dtype=torch.int32, device=device)
+        self.q = torch.empty(n_seqs, Hqk, d, **f32)
+        self.k = torch.empty(n_seqs, Hqk, d, **f32)
+        self.v = torch.empty(n_seqs, Hv, d, **f32)
+        self.beta = torch.empty(n_seqs, Hv, **f32)
+        self.g = torch.empty(n_seqs, Hv, **f32)
+        self.o = torch.empty(n_seqs, Hv, d, dtype=_act(cfg), device=device)
+
+    def __call__(self, qkv, z, b, a, conv_w, dt_bias, A_log, norm_w, conv_state, S, y, stream=None):
+        cfg, N = self.cfg, self.N
+        B.gdn_conv_gate_prep(cfg, N, N, self.cu, qkv, b, a, conv_w, dt_bias, A_log, conv_state, conv_state,
+                             self.q, self.k, self.v, self.beta, self.g, stream)
+        B.gdn_decode_step(cfg, N, self.q, self.k, self.v, self.beta, self.g, S, S, self.o, stream)
+        B.gdn_gated_rmsnorm(cfg, N * cfg.n_v_heads, self.o, z, norm_w, y, stream)
+        return y

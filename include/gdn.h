@@ -1,0 +1,173 @@
+/*
+ * gdn.h -- C ABI of the gated DeltaNet token mixer for AMD Instinct MI355X
+ * (gfx950), implemented in libgdn.so.
+ *
+ * The mixer is the one the xwen CLAUDE.md page specifies for the Qwen 3.6
+ * hybrid layers (section "Architecture cheat sheet", gated DeltaNet
+ * paragraph). It starts from the already projected fused qkv stream and ends
+ * after the gated RMSNorm; the projections around it are not part of it.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers. Every buffer pointer is a DEVICE pointer (memory the caller
+ * allocated on the current HIP device), except `cfg`, which is a host pointer.
+ * The caller owns every buffer; the library allocates nothing and keeps no
+ * state between calls. All recurrent state travels in the explicit
+ * conv-state and delta-state buffers.
+ *
+ * Streams. `stream` is a hipStream_t passed as void* (NULL = the null
+ * stream). Every call validates its arguments on the host, then enqueues its
+ * kernels on `stream` and returns without synchronising. Nothing prints,
+ * aborts or exits.
+ *
+ * Errors. A failed argument check returns GDN_E_INVALID_ARG or
+ * GDN_E_UNSUPPORTED and launches nothing. A launch failure returns GDN_E_HIP.
+ * Faults during kernel execution surface at the caller's next
+ * synchronisation, as for any HIP kernel.
+ *
+ * Shapes and layouts (row-major, last index fastest). T = tokens in the call,
+ * N = sequences, Hqk = K/Q heads, Hv = V heads, d = head_dim = 128,
+ * C = d * (2*Hqk + Hv) = fused width.
+ *   qkv            [T][C]        act dtype; q block | k block | v block, each
+ *                                head-major, d contiguous channels per head
+ *   beta_logit,
+ *   alpha_logit    [T][Hv]       act dtype
+ *   conv_w         [C][4]        fp32; conv_w[c][3] multiplies the current
+ *                                token, conv_w[c][0] the token three back
+ *   dt_bias, A_log [Hv]          fp32
+ *   conv_state     [N][3][C]     act dtype; the 3 raw qkv rows preceding the
+ *                                next token, oldest first
+ *   q, k           [T][Hqk][d]   fp32; L2-normalised
+ *   v              [T][Hv][d]    fp32
+ *   beta, g        [T][Hv]       fp32
+ *   S              [N][Hv][d][d] fp32; S[n][j][i][c], i = key index,
+ *                                c = value index
+ *   o              [T][Hv][d]    act dtype; delta-rule readout
+ *   z, y           [T][Hv][d]    act dtype
+ * V-head j uses K/Q-head j mod Hqk (tiled repeat).
+ * Packed sequences: sequence n owns tokens cu_seqlens[n] .. cu_seqlens[n+1]-1;
+ * cu_seqlens is a DEVICE int32 array of n_seqs+1 non-decreasing entries with
+ * cu_seqlens[0] = 0 and cu_seqlens[n_seqs] = n_tokens. The library cannot
+ * check its contents on the host; entries outside that contract are the
+ * caller's error (kernels clamp every index they derive from it to the
+ * buffers' bounds).
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define GDN_API __attribute__((visibility("default")))
+#else
+#define GDN_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_E_INVALID_ARG = 1,   /* null pointer, bad size or count, aliasing not allowed */
+    GDN_E_UNSUPPORTED = 2,   /* a configuration this build does not implement */
+    GDN_E_HIP = 3,           /* a HIP runtime call or kernel launch failed */
+    GDN_E_WORKSPACE = 4      /* workspace missing or smaller than required */
+} gdn_status;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+typedef void *gdn_stream_t;  /* a hipStream_t */
+
+typedef struct {
+    int32_t n_qk_heads;      /* Hqk >= 1 */
+    int32_t n_v_heads;       /* Hv >= 1, a multiple of Hqk */
+    int32_t head_dim;        /* d; only 128 is implemented */
+    int32_t conv_kernel;     /* only 4 is implemented */
+    float l2_eps;            /* q/k clamp-form L2 norm epsilon (the page: 1e-6) */
+    float norm_eps;          /* gated RMSNorm epsilon (the page: 1e-6) */
+    gdn_dtype act_dtype;     /* qkv, logits, conv state, o, z, y */
+} gdn_config;
+
+/* A config with the page's values: Hqk, Hv as given, d = 128, kernel 4,
+ * both epsilons 1e-6, activations of type `act`. */
+GDN_API gdn_config gdn_default_config(int32_t n_qk_heads, int32_t n_v_heads, gdn_dtype act);
+
+/*
+ * gdn_conv_gate_prep -- the steps before the delta rule (the page's gated
+ * DeltaNet paragraph, up to the gates):
+ *   causal depthwise conv over all C fused channels, kernel 4, no bias, with
+ *   the 3 rows of conv_state_in as left context of each sequence;
+ *   SiLU over all C channels; split into q | k | v;
+ *   q and k divided by max(||x||_2, l2_eps) per head;
+ *   beta = sigmoid(beta_logit); g = -exp(A_log) * softplus(alpha_logit + dt_bias).
+ * conv_state_out[n] receives the last 3 rows of [conv_state_in[n]; qkv rows
+ * of sequence n] (raw inputs, copied bit for bit); a sequence with 0 tokens
+ * passes its state through.
+ * conv_state_out may equal conv_state_in (in-place update). No other
+ * buffers may overlap. n_tokens may be 0 (only the state copy runs).
+ * Decode is the case n_tokens == n_seqs with cu_seqlens = {0, 1, ..., N}.
+ */
+GDN_API gdn_status gdn_conv_gate_prep(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens,
+                              const int32_t *cu_seqlens,
+                              const void *qkv, const void *beta_logit, const void *alpha_logit,
+                              const float *conv_w, const float *dt_bias, const float *A_log,
+                              const void *conv_state_in, void *conv_state_out,
+                              float *q, float *k, float *v, float *beta, float *g,
+                              gdn_stream_t stream);
+
+/*
+ * gdn_prefill_chunked -- the delta rule over packed sequences in its chunked
+ * form (chunks of 64 tokens counted from each sequence's first token; the
+ * page names chunk 64 in its section "Ground truth, in order of authority").
+ * Per sequence n and V-head j it produces the same result as the recurrent
+ * step of gdn_decode_step applied token by token from S_in[n][j]:
+ *   o[t][j] = readout after each token, S_out[n][j] = state after the last.
+ * S_out may equal S_in. `workspace` is device scratch of at least
+ * gdn_prefill_workspace_bytes(cfg, n_seqs, n_tokens) bytes (may be NULL
+ * when that size is 0); it holds no result between calls.
+ */
+GDN_API gdn_status gdn_prefill_chunked(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens,
+                               const int32_t *cu_seqlens,
+                               const float *q, const float *k, const float *v,
+                               const float *beta, const float *g,
+                               const float *S_in, float *S_out, void *o,
+                               void *workspace, size_t workspace_bytes, gdn_stream_t stream);
+
+/* Workspace size gdn_prefill_chunked needs for these sizes (0 for a bad cfg). */
+GDN_API size_t gdn_prefill_workspace_bytes(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens);
+
+/*
+ * gdn_decode_step -- one recurrent step of the delta rule for n_seqs
+ * sequences of one token each (inputs laid out with T = n_seqs). Per sequence
+ * n and V-head j (the page's recurrent step, in its order):
+ *   S <- exp(g) * S;  delta = beta * (v - S.k);  S <- S + k (x) delta;
+ *   o = (S . q) / sqrt(head_dim)   (read from the updated state)
+ * S_out may equal S_in (in-place update).
+ */
+GDN_API gdn_status gdn_decode_step(const gdn_config *cfg, int32_t n_seqs,
+                           const float *q, const float *k, const float *v,
+                           const float *beta, const float *g,
+                           const float *S_in, float *S_out, void *o, gdn_stream_t stream);
+
+/*
+ * gdn_gated_rmsnorm -- per row of d values (n_rows = T * Hv):
+ *   y = o / sqrt(mean(o^2) + norm_eps) * norm_w * silu(z)
+ * with norm_w [d] fp32 shared by all heads and used as stored (no +1).
+ * y may equal o (in place). n_rows may be 0.
+ */
+GDN_API gdn_status gdn_gated_rmsnorm(const gdn_config *cfg, int64_t n_rows, const void *o, const void *z,
+                             const float *norm_w, void *y, gdn_stream_t stream);
+
+/* A static, NUL-terminated description of a status code. */
+GDN_API const char *gdn_status_string(gdn_status status);
+
+/* The library's version string (static). */
+GDN_API const char *gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

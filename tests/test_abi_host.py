@@ -1,0 +1,131 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+include/gdn.h declares, and its host-side validation rejects bad arguments
+before anything is launched (every call here fails validation or returns
+early, so no HIP work is issued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_deltanet_layer_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from gated_deltanet_layer_amd import build
+        build.build()
+    return B.load()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"GDN_API\s+[\w\s\*]+?\b(gdn_\w+)\s*\(", text)))
+
+
+def test_header_declarations_match_binding():
+    assert declared_symbols() == sorted(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+
+
+def test_only_abi_symbols_are_exported(lib):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
+    mine = sorted({ln.split()[-1] for ln in out.splitlines() if " T " in ln and ln.split()[-1].startswith("gdn_")})
+    assert mine == declared_symbols()
+
+
+def test_status_strings_and_version(lib):
+    assert B.status_string(0) == "ok"
+    assert "workspace" in B.status_string(B.GDN_E_WORKSPACE)
+    assert lib.gdn_version().decode().startswith("gdn-mi355x")
+
+
+def test_default_config(lib):
+    c = lib.gdn_default_config(16, 48, B.GDN_BF16)
+    assert (c.n_qk_heads, c.n_v_heads, c.head_dim, c.conv_kernel, c.act_dtype) == (16, 48, 128, 4, B.GDN_BF16)
+    assert c.l2_eps == pytest.approx(1e-6) and c.norm_eps == pytest.approx(1e-6)
+
+
+def test_workspace_size(lib):
+    cfg = B.make_config(16, 48)
+    # (ceil(T/64) + N) chunks x Hv x (two 64x64 fp32 matrices + 64 fp64)
+    assert B.gdn_prefill_workspace_bytes(cfg, 1, 4096) == (64 + 1) * 48 * (2 * 4096 * 4 + 64 * 8)
+    assert B.gdn_prefill_workspace_bytes(cfg, 1, 0) == 0
+    bad = B.make_config(16, 40)
+    assert B.gdn_prefill_workspace_bytes(bad, 1, 64) == 0
+
+
+FAKE = [0x100000 * (i + 1) for i in range(20)]   # distinct, never dereferenced
+
+
+def _decode(lib, cfg, n, ptrs):
+    return lib.gdn_decode_step(ctypes.byref(cfg), n, *ptrs, None)
+
+
+def test_decode_validation(lib):
+    cfg = B.make_config(2, 4)
+    p = FAKE[:8]
+    assert _decode(lib, cfg, 0, p) == B.GDN_OK                       # nothing to do
+    assert _decode(lib, cfg, -1, p) == B.GDN_E_INVALID_ARG
+    assert _decode(lib, cfg, 1, [None] + p[1:]) == B.GDN_E_INVALID_ARG
+    assert _decode(lib, B.make_config(2, 3), 1, p) == B.GDN_E_INVALID_ARG   # Hv % Hqk
+    assert _decode(lib, B.make_config(2, 4, head_dim=64), 1, p) == B.GDN_E_UNSUPPORTED
+    assert _decode(lib, B.make_config(2, 4, conv_kernel=3), 1, p) == B.GDN_E_UNSUPPORTED
+    neg = B.make_config(2, 4)
+    neg.norm_eps = -1.0
+    assert _decode(lib, neg, 1, p) == B.GDN_E_INVALID_ARG
+    bad_dtype = B.make_config(2, 4)
+    bad_dtype.act_dtype = 7
+    assert _decode(lib, bad_dtype, 1, p) == B.GDN_E_INVALID_ARG
+    # o overlapping v: rejected.
+    q = p[:]
+    q[7] = q[2] + 64
+    assert _decode(lib, cfg, 1, q) == B.GDN_E_INVALID_ARG
+    # S_out overlapping S_in partially: rejected.
+    q = p[:]
+    q[6] = q[5] + 4096
+    assert _decode(lib, cfg, 1, q) == B.GDN_E_INVALID_ARG
+    assert lib.gdn_decode_step(None, 1, *p, None) == B.GDN_E_INVALID_ARG
+
+
+def test_prefill_validation(lib):
+    cfg = B.make_config(2, 4)
+    need = B.gdn_prefill_workspace_bytes(cfg, 1, 100)
+    args = lambda ws, wsb, n=1, t=100: (ctypes.byref(cfg), n, t, *FAKE[:9], ws, wsb, None)
+    base = list(args(FAKE[10], need))
+    assert lib.gdn_prefill_chunked(*args(None, 0)) == B.GDN_E_WORKSPACE
+    assert lib.gdn_prefill_chunked(*args(FAKE[10], need - 1)) == B.GDN_E_WORKSPACE
+    assert lib.gdn_prefill_chunked(*args(FAKE[10], need, n=0, t=5)) == B.GDN_E_INVALID_ARG
+    assert lib.gdn_prefill_chunked(*args(FAKE[10], need, n=0, t=0)) == B.GDN_OK
+    bad = base[:]
+    bad[3] = None    # cu_seqlens
+    assert lib.gdn_prefill_chunked(*bad) == B.GDN_E_INVALID_ARG
+
+
+def test_prep_and_norm_validation(lib):
+    cfg = B.make_config(2, 4)
+    p = FAKE[:14]
+    assert lib.gdn_conv_gate_prep(ctypes.byref(cfg), 0, 0, *p, None) == B.GDN_OK
+    assert lib.gdn_conv_gate_prep(ctypes.byref(cfg), 1, -3, *p, None) == B.GDN_E_INVALID_ARG
+    nulls = p[:]
+    nulls[0] = None  # cu_seqlens
+    assert lib.gdn_conv_gate_prep(ctypes.byref(cfg), 1, 4, *nulls, None) == B.GDN_E_INVALID_ARG
+    # q overlapping the qkv input: rejected.
+    ov = p[:]
+    ov[10] = ov[1] + 16
+    assert lib.gdn_conv_gate_prep(ctypes.byref(cfg), 1, 4, *ov, None) == B.GDN_E_INVALID_ARG
+    assert lib.gdn_gated_rmsnorm(ctypes.byref(cfg), 0, *FAKE[:4], None) == B.GDN_OK
+    assert lib.gdn_gated_rmsnorm(ctypes.byref(cfg), -1, *FAKE[:4], None) == B.GDN_E_INVALID_ARG
+    assert lib.gdn_gated_rmsnorm(ctypes.byref(cfg), 4, None, *FAKE[1:4], None) == B.GDN_E_INVALID_ARG
+    yz = FAKE[:4]
+    yz = [yz[0], yz[1], yz[2], yz[1] + 8]   # y overlapping z
+    assert lib.gdn_gated_rmsnorm(ctypes.byref(cfg), 4, *yz, None) == B.GDN_E_INVALID_ARG
