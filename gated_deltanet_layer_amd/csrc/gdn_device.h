@@ -163,82 +163,152 @@ __device__ __forceinline__ int first_unit(const int *cu, int seq, int unit_len, 
 //   A fragment, lane l: A[row = l % 16][k = 8 * (l / 16) + e], e = 0..7
 //   B fragment, lane l: B[k = 8 * (l / 16) + e][col = l % 16], e = 0..7
 //   accumulator, lane l: C[row = 4 * (l / 16) + r][col = l % 16], r = 0..3
-// F32 precision issues eight 16x16x4 fp32 MFMAs, the e-th taking element e
-// of each lane's fragment (so every k of the step is covered once).
-// BF16X3 splits each fp32 operand into hi = bf16(x) and lo = bf16(x - hi)
-// and sums hi*hi + hi*lo + lo*hi with three 16x16x32 bf16 MFMAs; the
-// dropped lo*lo term is below 2^-16 relative.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 enum class Prec { F32, BF16X3 };
 
-struct Frag { float e[8]; };
+// Operands live in LDS (and in the prefill workspace) as 32-byte blocks of
+// 8 consecutive contraction indices k, so that a fragment is two 16-byte
+// reads with no conversion:
+//   F32:    8 x fp32; the MMA issues eight 16x16x4 fp32 MFMAs, the e-th one
+//           taking element e of each lane's fragment (every k once).
+//   BF16X3: 8 x bf16 hi followed by 8 x bf16 lo, hi = bf16(x) and
+//           lo = bf16(x - hi); the MMA sums hi*hi + hi*lo + lo*hi with three
+//           16x16x32 bf16 MFMAs (the dropped lo*lo term is below 2^-16
+//           relative), an fp32-grade product.
+// An operand row of K contraction indices takes K/8 blocks; rows are padded
+// by the caller to spread LDS banks.
+constexpr int kBlk = 32;   // bytes per 8-index block
 
-template <Prec P> struct Mma;
+template <Prec P> struct Op;
 
-template <> struct Mma<Prec::F32> {
-  static __device__ __forceinline__ void run(f32x4 &acc, const Frag &a, const Frag &b) {
+template <> struct Op<Prec::F32> {
+  struct Frag { f32x4 a, b; };
+  static __device__ __forceinline__ Frag load(const uint8_t *blk) {
+    Frag f;
+    f.a = *reinterpret_cast<const f32x4 *>(blk);
+    f.b = *reinterpret_cast<const f32x4 *>(blk + 16);
+    return f;
+  }
+  // Four consecutive indices k .. k+3 (k % 4 == 0) of one row.
+  static __device__ __forceinline__ void put4(uint8_t *row, int k, f32x4 x) {
+    *reinterpret_cast<f32x4 *>(row + (k >> 3) * kBlk + (k & 7) * 4) = x;
+  }
+  // Element (k, idx) of a matrix stored k-major with `pitch` bytes per k row
+  // and idx as the blocked index: the fragment whose tile index runs along
+  // the blocked axis (a transposed read).
+  static __device__ __forceinline__ Frag gather(const uint8_t *base, int pitch, int idx, int k0) {
+    Frag f;
+    const uint8_t *p = base + k0 * pitch + (idx >> 3) * kBlk + (idx & 7) * 4;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.e[e], b.e[e], acc, 0, 0, 0);
+    for (int e = 0; e < 4; ++e) f.a[e] = *reinterpret_cast<const float *>(p + e * pitch);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f.b[e] = *reinterpret_cast<const float *>(p + (e + 4) * pitch);
+    return f;
+  }
+  static __device__ __forceinline__ void mma(f32x4 &c, const Frag &a, const Frag &b) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a[e], b.a[e], c, 0, 0, 0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b[e], b.b[e], c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ void mma2(f32x4 &c0, f32x4 &c1, const Frag &a, const Frag &b0, const Frag &b1) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      c0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a[e], b0.a[e], c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a[e], b1.a[e], c1, 0, 0, 0);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      c0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b[e], b0.b[e], c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b[e], b1.b[e], c1, 0, 0, 0);
+    }
   }
 };
 
-__device__ __forceinline__ void split_bf16(const Frag &x, bf16x8 &hi, bf16x8 &lo) {
+__device__ __forceinline__ void split4(f32x4 x, bf16x4 &hi, bf16x4 &lo) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const __bf16 h = static_cast<__bf16>(x.e[e]);
+  for (int e = 0; e < 4; ++e) {
+    const __bf16 h = static_cast<__bf16>(x[e]);
     hi[e] = h;
-    lo[e] = static_cast<__bf16>(x.e[e] - static_cast<float>(h));
+    lo[e] = static_cast<__bf16>(x[e] - static_cast<float>(h));
   }
 }
 
-template <> struct Mma<Prec::BF16X3> {
-  static __device__ __forceinline__ void run(f32x4 &acc, const Frag &a, const Frag &b) {
-    bf16x8 ah, al, bh, bl;
-    split_bf16(a, ah, al);
-    split_bf16(b, bh, bl);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+template <> struct Op<Prec::BF16X3> {
+  struct Frag { bf16x8 hi, lo; };
+  static __device__ __forceinline__ Frag load(const uint8_t *blk) {
+    Frag f;
+    f.hi = *reinterpret_cast<const bf16x8 *>(blk);
+    f.lo = *reinterpret_cast<const bf16x8 *>(blk + 16);
+    return f;
+  }
+  static __device__ __forceinline__ void put4(uint8_t *row, int k, f32x4 x) {
+    bf16x4 hi, lo;
+    split4(x, hi, lo);
+    uint8_t *b = row + (k >> 3) * kBlk + (k & 7) * 2;
+    *reinterpret_cast<bf16x4 *>(b) = hi;
+    *reinterpret_cast<bf16x4 *>(b + 16) = lo;
+  }
+  static __device__ __forceinline__ Frag gather(const uint8_t *base, int pitch, int idx, int k0) {
+    Frag f;
+    const uint8_t *p = base + k0 * pitch + (idx >> 3) * kBlk + (idx & 7) * 2;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      f.hi[e] = *reinterpret_cast<const __bf16 *>(p + e * pitch);
+      f.lo[e] = *reinterpret_cast<const __bf16 *>(p + e * pitch + 16);
+    }
+    return f;
+  }
+  static __device__ __forceinline__ void mma(f32x4 &c, const Frag &a, const Frag &b) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ void mma2(f32x4 &c0, f32x4 &c1, const Frag &a, const Frag &b0, const Frag &b1) {
+    c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b0.hi, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b1.hi, c1, 0, 0, 0);
+    c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b0.lo, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b1.lo, c1, 0, 0, 0);
+    c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b0.hi, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b1.hi, c1, 0, 0, 0);
   }
 };
 
-// Fragment loads from LDS (fp32).
-// Row-major source with k contiguous: A[row][k] at base[row * ld + k].
-__device__ __forceinline__ Frag frag_rows(const float *base, int ld, int row0, int k0) {
+// Fragment of rows row0.. (lane row = row0 + l % 16), contraction step k0
+// (a multiple of 32), from a blocked matrix with `pitch` bytes per row.
+template <Prec P>
+__device__ __forceinline__ typename Op<P>::Frag frag(const uint8_t *base, int pitch, int row0, int k0) {
   const int l = lane_id();
-  const float *p = base + (row0 + (l & 15)) * ld + k0 + 8 * (l >> 4);
-  const float4 x = *reinterpret_cast<const float4 *>(p);
-  const float4 y = *reinterpret_cast<const float4 *>(p + 4);
-  Frag f;
-  f.e[0] = x.x; f.e[1] = x.y; f.e[2] = x.z; f.e[3] = x.w;
-  f.e[4] = y.x; f.e[5] = y.y; f.e[6] = y.z; f.e[7] = y.w;
-  return f;
+  return Op<P>::load(base + (row0 + (l & 15)) * pitch + ((k0 >> 3) + (l >> 4)) * kBlk);
 }
-// Source with the tile's index (row of A, or column of B) contiguous and k
-// strided: X[k][idx] at base[k * ld + idx]. Optional per-k scale.
-__device__ __forceinline__ Frag frag_cols(const float *base, int ld, int idx0, int k0) {
+// Transposed fragment: tile index idx0 + l % 16 along the blocked axis,
+// contraction index along the rows.
+template <Prec P>
+__device__ __forceinline__ typename Op<P>::Frag frag_t(const uint8_t *base, int pitch, int idx0, int k0) {
   const int l = lane_id();
-  const float *p = base + (k0 + 8 * (l >> 4)) * ld + idx0 + (l & 15);
-  Frag f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) f.e[e] = p[e * ld];
-  return f;
+  return Op<P>::gather(base, pitch, idx0 + (l & 15), k0 + 8 * (l >> 4));
 }
-__device__ __forceinline__ Frag frag_cols_scaled(const float *base, int ld, int idx0, int k0,
-                                                 const float *kscale) {
+// Store an accumulator tile transposed: element (row0 + 4(l/16) + r, col0 + l%16)
+// goes to row col0 + l%16, index row0 + 4(l/16) + r of the blocked matrix.
+template <Prec P>
+__device__ __forceinline__ void put_acc_t(uint8_t *base, int pitch, int row0, int col0, f32x4 acc) {
   const int l = lane_id();
-  const int kb = k0 + 8 * (l >> 4);
-  const float *p = base + kb * ld + idx0 + (l & 15);
-  Frag f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) f.e[e] = p[e * ld] * kscale[kb + e];
-  return f;
+  Op<P>::put4(base + (col0 + (l & 15)) * pitch, row0 + 4 * (l >> 4), acc);
 }
 
 // Accumulator element r of lane l sits at (row0 + 4*(l/16) + r, col0 + l%16).
 __device__ __forceinline__ int acc_row(int r) { return 4 * (lane_id() >> 4) + r; }
 __device__ __forceinline__ int acc_col() { return lane_id() & 15; }
 
+// Workgroup barrier for LDS only: waits for this wave's LDS operations, not
+// for its global loads and stores, so prefetches stay in flight across it.
+__device__ __forceinline__ void block_sync_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Legacy fp32 fragments from row-major fp32 LDS (used by the small fp32 MFMA
+// steps of the triangular solve).
 }  // namespace gdn
