@@ -40,6 +40,8 @@ from gated_deltanet_layer_amd import binding as B  # noqa: E402
 from gated_deltanet_layer_amd import layer as Lyr  # noqa: E402
 from gated_deltanet_layer_amd import workloads as wl  # noqa: E402
 
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "gated_deltanet_layer_amd", "csrc")
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 CHUNK = 64
@@ -54,6 +56,67 @@ def dev(x: np.ndarray) -> torch.Tensor:
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the HIP sources (the traffic counters are only valid for this build)."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(key: str):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated) recorded in
+    profiles/traffic.json for the current kernel sources, else None."""
+    path = os.path.join(PROFILES, "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_hash() or key not in rec.get("kernels", {}):
+        return None
+    k = rec["kernels"][key]
+    return int(k["fetch_bytes"] + k["write_bytes"])
+
+
+def summarize_rocprof(db_path: str) -> str:
+    """Per-kernel summary of a rocprofv3 database: durations from a kernel
+    trace, or per-dispatch counter values from a --pmc run."""
+    import collections
+    import sqlite3
+    db = sqlite3.connect(db_path)
+    tables = {r[0] for r in db.execute("select name from sqlite_master")}
+    lines = []
+
+    def short(name):
+        name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+        name = name.replace("(gdn::Prec)1", "BF16X3").replace("(gdn::Prec)0", "F32")
+        return name.split("(")[0][:70]
+    if "counters_collection" in tables and db.execute("select count(*) from counters_collection").fetchone()[0]:
+        per = collections.defaultdict(float)
+        for k, d, n, v in db.execute("select kernel_name, dispatch_id, counter_name, value from counters_collection"):
+            per[(k, d, n)] += v
+        agg = collections.defaultdict(list)
+        for (k, d, n), v in per.items():
+            agg[(short(k), n)].append(v)
+        lines.append(f"{'kernel':70s} {'counter':12s} {'dispatches':>10s} {'mean':>14s}")
+        for (k, n), v in sorted(agg.items()):
+            lines.append(f"{k:70s} {n:12s} {len(v):10d} {sum(v) / len(v):14.1f}")
+    else:
+        agg = collections.defaultdict(list)
+        for n, gx, gy, wx, dur in db.execute("select name, grid_x, grid_y, workgroup_x, duration from kernels"):
+            agg[(short(n), gx, gy, wx)].append(dur)
+        lines.append(f"{'kernel':70s} {'grid(threads)':>16s} {'wg':>5s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s}")
+        for (k, gx, gy, wx), d in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+            lines.append(f"{k:70s} {f'{gx}x{gy}':>16s} {wx:5d} {len(d):6d} {sum(d) / len(d) / 1e3:9.2f} "
+                         f"{min(d) / 1e3:9.2f}")
+    return "\n".join(lines)
 
 
 def bench_prefill(steps: int, warmup: int):
@@ -93,7 +156,8 @@ def bench_prefill(steps: int, warmup: int):
     achieved = flops / (core_ms * 1e-3) / 1e12
     return dict(total_ms=total_ms, ms_per_step=total_ms / steps, tokens=T, core_ms=core_ms,
                 roofline={"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
-                          "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                          "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                          "traffic": measured_traffic("prefill_core"),
                           "kernel": "gdn_prefill_chunked (chunk_local + chunk_state)",
                           "flop_per_launch": flops, "avg_launch_us": round(core_ms * 1e3, 2)})
 
@@ -144,7 +208,9 @@ def bench_decode(wid: int, warmup_steps: int = 32):
     return {"workload": w.name, "tokens_per_s": round(w.n_seqs * steps / (total_ms * 1e-3), 1),
             "us_per_step": round(total_ms * 1e3 / steps, 2),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "gdn_decode_step",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic("decode_b64" if w.n_seqs > 1 else "decode_b1"),
+                         "kernel": "gdn_decode_step",
                          "bytes_per_launch": nbytes, "avg_launch_us": round(k_ms * 1e3, 2)}}
 
 
@@ -178,7 +244,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-decode", action="store_true", help="skip the decode workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the oracle")
+    ap.add_argument("--only", choices=["prefill", "decode-b1", "decode-b64"], default=None,
+                    help="run one workload only (for counter collection)")
+    ap.add_argument("--summarize-rocprof", metavar="DB", default=None,
+                    help="print a per-kernel summary of a rocprofv3 results database and exit")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy 4 times (reference for HBM byte counters)")
     a = ap.parse_args()
+    if a.summarize_rocprof:
+        print(summarize_rocprof(a.summarize_rocprof))
+        return
     if a.gpus != 1:
         print(f"bench.py measures one GPU only: the mixer's path here runs on a single MI355X; "
               f"--gpus {a.gpus} is not supported", file=sys.stderr)
@@ -188,18 +263,30 @@ def main():
         sys.exit(2)
     torch.cuda.set_device(0)
     B.load()
+    if a.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 4 x 268435456 bytes")
+    if a.only in ("decode-b1", "decode-b64"):
+        d = bench_decode(2 if a.only == "decode-b1" else 4)
+        print(json.dumps(d), flush=True)
+        return
     log("prefill workload: T=4096 Hqk=16 Hv=48 bf16")
     pre = bench_prefill(a.steps, a.warmup)
     log(f"prefill: {pre['ms_per_step']:.3f} ms/step, core {pre['core_ms'] * 1e3:.1f} us")
     decode = None
-    if not a.no_decode:
+    if not a.no_decode and a.only is None:
         decode = []
         for wid in (2, 4):
             log(f"decode workload {wid}")
             decode.append(bench_decode(wid))
             log(json.dumps(decode[-1]))
     cpu = None
-    if not a.no_cpu_baseline:
+    if not a.no_cpu_baseline and a.only is None:
         log("cpu baseline (oracle)")
         cpu = cpu_baseline()
     line = {

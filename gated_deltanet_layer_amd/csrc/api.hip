@@ -142,7 +142,7 @@ gdn_status gdn_conv_gate_prep(const gdn_config *cfg, int32_t n_seqs, int32_t n_t
 size_t gdn_prefill_workspace_bytes(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens) {
   if (check_config(cfg) != GDN_OK || n_seqs < 0 || n_tokens < 0) return 0;
   if (n_tokens == 0) return 0;
-  return gdn::prefill_workspace_bytes(n_seqs, n_tokens, cfg->n_v_heads);
+  return gdn::prefill_workspace_bytes(n_seqs, n_tokens, cfg->n_qk_heads, cfg->n_v_heads);
 }
 
 gdn_status gdn_prefill_chunked(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens,

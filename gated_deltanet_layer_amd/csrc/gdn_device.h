@@ -277,6 +277,52 @@ template <> struct Op<Prec::BF16X3> {
   }
 };
 
+// Fragment-major operand layout (global memory): the 16-row x 32-index block
+// (rt, ks) of a matrix with KS contraction steps sits at byte
+// (rt * KS + ks) * kFragBlk; inside it, lane l = 16 * ((k % 32) / 8) + r % 16
+// owns the 8 indices k of its fragment, so that a wave loads a whole
+// fragment with one coalesced 1 KB access per 16-byte plane.
+//   BF16X3: hi plane at l * 16, lo plane at 1024 + l * 16
+//   F32:    8 floats at l * 32
+constexpr int kFragBlk = 2048;
+
+__device__ __forceinline__ size_t frag_lane_off(int KS, int r, int k) {
+  const int l = 16 * ((k & 31) >> 3) + (r & 15);
+  return static_cast<size_t>((r >> 4) * KS + (k >> 5)) * kFragBlk + l * 32;   // F32 lane slot
+}
+
+template <Prec P> struct FragIO;
+template <> struct FragIO<Prec::F32> {
+  // Four consecutive indices k .. k+3 (k % 4 == 0) of row r.
+  static __device__ __forceinline__ void put4(uint8_t *m, int KS, int r, int k, f32x4 x) {
+    *reinterpret_cast<f32x4 *>(m + frag_lane_off(KS, r, k) + (k & 7) * 4) = x;
+  }
+  static __device__ __forceinline__ Op<Prec::F32>::Frag load(const uint8_t *m, int KS, int rt, int ks) {
+    const uint8_t *b = m + static_cast<size_t>(rt * KS + ks) * kFragBlk + lane_id() * 32;
+    Op<Prec::F32>::Frag f;
+    f.a = *reinterpret_cast<const f32x4 *>(b);
+    f.b = *reinterpret_cast<const f32x4 *>(b + 16);
+    return f;
+  }
+};
+template <> struct FragIO<Prec::BF16X3> {
+  static __device__ __forceinline__ void put4(uint8_t *m, int KS, int r, int k, f32x4 x) {
+    bf16x4 hi, lo;
+    split4(x, hi, lo);
+    const int l = 16 * ((k & 31) >> 3) + (r & 15);
+    uint8_t *b = m + static_cast<size_t>((r >> 4) * KS + (k >> 5)) * kFragBlk + l * 16 + (k & 7) * 2;
+    *reinterpret_cast<bf16x4 *>(b) = hi;
+    *reinterpret_cast<bf16x4 *>(b + 1024) = lo;
+  }
+  static __device__ __forceinline__ Op<Prec::BF16X3>::Frag load(const uint8_t *m, int KS, int rt, int ks) {
+    const uint8_t *b = m + static_cast<size_t>(rt * KS + ks) * kFragBlk + lane_id() * 16;
+    Op<Prec::BF16X3>::Frag f;
+    f.hi = *reinterpret_cast<const bf16x8 *>(b);
+    f.lo = *reinterpret_cast<const bf16x8 *>(b + 1024);
+    return f;
+  }
+};
+
 // Fragment of rows row0.. (lane row = row0 + l % 16), contraction step k0
 // (a multiple of 32), from a blocked matrix with `pitch` bytes per row.
 template <Prec P>

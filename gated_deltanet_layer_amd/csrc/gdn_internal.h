@@ -63,7 +63,7 @@ struct PrefillParams {
 inline int64_t max_chunks(int n_seqs, int n_tokens) {
   return (static_cast<int64_t>(n_tokens) + kChunk - 1) / kChunk + n_seqs;
 }
-size_t prefill_workspace_bytes(int n_seqs, int n_tokens, int n_v);
+size_t prefill_workspace_bytes(int n_seqs, int n_tokens, int n_qk, int n_v);
 hipError_t launch_prefill(const PrefillParams &p, gdn_dtype act, hipStream_t s);
 
 }  // namespace gdn

@@ -15,17 +15,21 @@
 // last three lines depend on S0.
 //
 // Two kernels:
-//  * chunk_local: one block per (chunk, K-head). Builds K K^T and Q K^T once
-//    for the K-head, then for each V-head that uses it (tiled repeat: V-heads
-//    h, h + Hqk, ...) applies that head's decays and beta, writes P, and
-//    inverts the unit lower-triangular I + A by blocked forward substitution
-//    on 16x16 blocks (diagonal blocks by substitution, off-diagonal blocks by
-//    fp32 MFMA products), writing Tm and gam to the workspace.
+//  * chunk_local: one block per (chunk, K-head), fully parallel. Writes the
+//    chunk's K, Q and K^T as ready-to-load MFMA operands, builds K K^T and
+//    Q K^T once for the K-head, then for each V-head that uses it (tiled
+//    repeat: V-heads h, h + Hqk, ...) applies that head's decays and beta,
+//    writes P, and inverts the unit lower-triangular I + A by blocked forward
+//    substitution on 16x16 blocks (diagonal blocks by substitution,
+//    off-diagonal blocks by fp32 MFMA products), writing Tm and gam.
 //  * chunk_state: one block per (sequence, V-head, 32-column slab of S). The
 //    value columns of S are independent, so four blocks share a head. It
 //    walks the sequence's chunks in order with the fp32 state slab held in
 //    MFMA accumulators: [K; Q] S, D = Tm (V - Gam K S), O = s(Gam Q S + P D),
-//    S <- Gam_n S + K~^T D.
+//    S <- Gam_n S + K^T diag(exp(gam_n - gam)) D. The left operands of these
+//    products (K, Q, Tm, P, K^T) stream from the workspace straight into
+//    registers, each reloaded for the next chunk right after its last use;
+//    only the right operands (S^T, R^T, D^T) and V pass through LDS.
 // Every product runs at fp32-grade precision: fp32 MFMA for fp32
 // activations, three-pass split bf16 MFMA (hi*hi + hi*lo + lo*hi) for bf16
 // activations. Operands are split once, when they are written to LDS (or to
@@ -49,24 +53,32 @@ constexpr int kChunkMat = kChunk * kChunk;
 // indices (16 or 8 blocks of 32 bytes) plus 16 bytes to spread LDS banks.
 constexpr int kPitch128 = (kHeadDim / 8) * kBlk + 16;   // 528
 constexpr int kPitch64 = (kChunk / 8) * kBlk + 16;      // 272
-constexpr int kWsPitch = (kChunk / 8) * kBlk;           // 256: workspace rows, unpadded
 constexpr int kLdS = kChunk + 1;          // fp32 pitch of the solve's scalar matrices
 constexpr int kLdV = kSlab + 4;           // fp32 pitch of the V slab in LDS
 constexpr int kLdO = kSlab;               // fp32 pitch of the O staging rows (4 waves x 16 rows fit the R^T buffer)
 
+// Workspace, all operands in the fragment-major layout:
+//   per (chunk, K-head): K rows (64 x 128, 4 x 4 blocks), Q rows (same) and
+//                        K^T rows (128 x 64, 8 x 2 blocks): 96 KB
+//   per (chunk, V-head): Tm (64 x 64, 4 x 2 blocks) and P (same): 32 KB
+//   per (chunk, V-head): gam, 64 fp64
+constexpr size_t kKBytes = 16 * kFragBlk;
+constexpr size_t kQkBytes = 3 * kKBytes;
+constexpr size_t kMatBytes = 8 * kFragBlk;
+constexpr size_t kVBytes = 2 * kMatBytes;
+
 struct Workspace {
-  uint8_t *T;  // [max_chunks][Hv][64 rows][256 B]  Tm, blocked operand rows
-  uint8_t *P;  // [max_chunks][Hv][64 rows][256 B]  P, blocked operand rows
-  double *gam; // [max_chunks][Hv][64] cumulative log-decay inside the chunk
+  uint8_t *qk;
+  uint8_t *v;
+  double *gam;
 };
 
-__host__ __device__ inline Workspace carve(void *ws, int64_t max_chunks, int n_v) {
+__host__ __device__ inline Workspace carve(void *ws, int64_t max_chunks, int n_qk, int n_v) {
   Workspace w;
   uint8_t *base = static_cast<uint8_t *>(ws);
-  const int64_t mat_bytes = max_chunks * n_v * kChunk * kWsPitch;
-  w.T = base;
-  w.P = base + mat_bytes;
-  w.gam = reinterpret_cast<double *>(base + 2 * mat_bytes);
+  w.qk = base;
+  w.v = base + static_cast<size_t>(max_chunks) * n_qk * kQkBytes;
+  w.gam = reinterpret_cast<double *>(w.v + static_cast<size_t>(max_chunks) * n_v * kVBytes);
   return w;
 }
 
@@ -92,20 +104,36 @@ template <> __device__ __forceinline__ Op<Prec::BF16X3>::Frag make_frag<Prec::BF
 }
 
 // ---------------------------------------------------------------------------
-// chunk_local: per (chunk, K-head). ~72 KB of LDS, two blocks per CU.
+// chunk_local: per (chunk, K-head), 4 waves, ~72 KB of LDS (two blocks per CU).
+//  1. K and Q rows of the chunk -> operand blocks in the workspace (K also
+//     into LDS), K^T rows -> operand blocks.
+//  2. Wave w computes row tile w of the lower triangles of K K^T and Q K^T.
+//  3. The V-heads that use this K-head are solved in parallel, one per wave
+//     (up to kSolveWaves at a time): decays, P, L = I + A, and L^-1 by
+//     blocked forward substitution done in place in the wave's own LDS
+//     region, then Tm = L^-1 diag(beta). Only wave-level ordering is needed
+//     inside a solve.
+constexpr int kSolveWaves = 3;
+constexpr int kTri = kChunk * (kChunk + 1) / 2;   // packed lower triangle incl. diagonal
+
+__device__ __forceinline__ int tri(int r, int m) { return r * (r + 1) / 2 + m; }
+
+// Orders this wave's earlier LDS accesses before its later ones.
+__device__ __forceinline__ void wave_sync_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 template <Prec P>
 __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(PrefillParams p, int64_t max_chunks) {
   // Phase 1 holds K as blocked operand rows; phase 2 reuses the bytes for
-  // the fp32 matrices L = I + A and X = L^-1 of the solve.
-  __shared__ __attribute__((aligned(16))) uint8_t kbuf[kChunk * kPitch128];
-  __shared__ float Gkk[kChunk * kLdS];
-  __shared__ float Gqk[kChunk * kLdS];
-  __shared__ float Tsc[4][16 * 17];
-  __shared__ double gam_s[kChunk];
-  __shared__ float bet_s[kChunk];
-  uint8_t *Kb = kbuf;
-  float *Lm = reinterpret_cast<float *>(kbuf);
-  float *Xm = Lm + kChunk * kLdS;
+  // the solving waves' fp32 matrices (L, overwritten in place by L^-1).
+  constexpr int kKbBytes = kChunk * kPitch128;
+  constexpr int kLxBytes = kSolveWaves * kChunk * kLdS * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t buf[kKbBytes > kLxBytes ? kKbBytes : kLxBytes];
+  __shared__ float Gk[kTri];                  // K K^T, lower triangle
+  __shared__ float Gq[kTri];                  // Q K^T, lower triangle
+  __shared__ float Tsc[kSolveWaves][16 * 17];
+  __shared__ double gam_s[kSolveWaves][kChunk];
+  __shared__ float bet_s[kSolveWaves][kChunk];
+  uint8_t *Kb = buf;
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
@@ -119,179 +147,215 @@ __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(PrefillParam
   const int t0 = seq0 + ci * kChunk;
   const int len = min(kChunk, L - ci * kChunk);
   const int cid = blockIdx.x;
-  const Workspace ws = carve(p.ws, max_chunks, p.n_v);
+  const Workspace ws = carve(p.ws, max_chunks, p.n_qk, p.n_v);
   const size_t qk_stride = static_cast<size_t>(p.n_qk) * kHeadDim;
   const float *kg = p.k + t0 * qk_stride + h * kHeadDim;
   const float *qg = p.q + t0 * qk_stride + h * kHeadDim;
+  uint8_t *wk = ws.qk + (static_cast<size_t>(cid) * p.n_qk + h) * kQkBytes;   // K rows, Q rows, K^T rows
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
-  {  // K rows -> blocked operand rows in LDS (rows >= len are zero).
+  // Q rows of this wave's Gram row tile, as A fragments (loaded up front).
+  const int rt = wave;
+  const int qrow = 16 * rt + (lane & 15);
+  f32x4 qa[kHeadDim / 32], qb[kHeadDim / 32];
+  {
+    const float *qp = qg + min(qrow, len - 1) * qk_stride + 8 * (lane >> 4);
+#pragma unroll
+    for (int ks = 0; ks < kHeadDim / 32; ++ks) {
+      qa[ks] = *reinterpret_cast<const f32x4 *>(qp + 32 * ks);
+      qb[ks] = *reinterpret_cast<const f32x4 *>(qp + 32 * ks + 4);
+    }
+  }
+  {  // K and Q rows -> operand blocks (K also into LDS); rows >= len are zero.
     constexpr int kPer = kChunk * (kHeadDim / 4) / kLocalThreads;
-    f32x4 buf[kPer];
+    f32x4 kb4[kPer], qb4[kPer];
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int idx = tid + u * kLocalThreads, r = idx / (kHeadDim / 4), c4 = idx % (kHeadDim / 4);
-      const f32x4 x = *reinterpret_cast<const f32x4 *>(kg + min(r, len - 1) * qk_stride + 4 * c4);
-      buf[u] = r < len ? x : f32x4{0.f, 0.f, 0.f, 0.f};
+      const size_t off = min(r, len - 1) * qk_stride + 4 * c4;
+      kb4[u] = *reinterpret_cast<const f32x4 *>(kg + off);
+      qb4[u] = *reinterpret_cast<const f32x4 *>(qg + off);
     }
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int idx = tid + u * kLocalThreads, r = idx / (kHeadDim / 4), c4 = idx % (kHeadDim / 4);
-      Op<P>::put4(Kb + r * kPitch128, 4 * c4, buf[u]);
+      const f32x4 kx = r < len ? kb4[u] : zero4, qx = r < len ? qb4[u] : zero4;
+      Op<P>::put4(Kb + r * kPitch128, 4 * c4, kx);
+      FragIO<P>::put4(wk, kHeadDim / 32, r, 4 * c4, kx);
+      FragIO<P>::put4(wk + kKBytes, kHeadDim / 32, r, 4 * c4, qx);
+    }
+  }
+  {  // K^T rows: element (i, r) of K^T is K[r][i]; 4 consecutive r per item.
+    constexpr int kTItems = kHeadDim * (kChunk / 4) / kLocalThreads;
+    f32x4 kt[kTItems];
+#pragma unroll
+    for (int u = 0; u < kTItems; ++u) {
+      const int item = tid + u * kLocalThreads, i = item % kHeadDim, r0 = 4 * (item / kHeadDim);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kt[u][e] = kg[min(r0 + e, len - 1) * qk_stride + i];
+    }
+#pragma unroll
+    for (int u = 0; u < kTItems; ++u) {
+      const int item = tid + u * kLocalThreads, i = item % kHeadDim, r0 = 4 * (item / kHeadDim);
+      f32x4 x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = r0 + e < len ? kt[u][e] : 0.f;
+      FragIO<P>::put4(wk + 2 * kKBytes, kChunk / 32, i, r0, x);
     }
   }
   block_sync_lds();
 
-  // The 10 lower-triangular 16x16 tiles of K K^T and of Q K^T (Q straight from global).
-  for (int tile = wave; tile < 20; tile += 4) {
-    const int which = tile / 10, tt = tile % 10;
-    int rt = 0;
-    while ((rt + 1) * (rt + 2) / 2 <= tt) ++rt;
-    const int ct = tt - rt * (rt + 1) / 2;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    const int qrow = rt * 16 + (lane & 15);
-    const float *qp = qg + min(qrow, len - 1) * qk_stride + 8 * (lane >> 4);
+  // Row tile rt of the lower triangles of K K^T and Q K^T.
+  {
+    const bool qvalid = qrow < len;
+    for (int ct = 0; ct <= rt; ++ct) {
+      f32x4 ak = zero4, aq = zero4;
 #pragma unroll
-    for (int ks = 0; ks < kHeadDim / 32; ++ks) {
-      typename Op<P>::Frag a;
-      if (which) {
-        f32x4 x0 = *reinterpret_cast<const f32x4 *>(qp + ks * 32);
-        f32x4 x1 = *reinterpret_cast<const f32x4 *>(qp + ks * 32 + 4);
-        if (qrow >= len) x0 = x1 = f32x4{0.f, 0.f, 0.f, 0.f};
-        a = make_frag<P>(x0, x1);
-      } else {
-        a = frag<P>(Kb, kPitch128, rt * 16, ks * 32);
+      for (int ks = 0; ks < kHeadDim / 32; ++ks) {
+        const typename Op<P>::Frag b = frag<P>(Kb, kPitch128, ct * 16, ks * 32);
+        Op<P>::mma(ak, frag<P>(Kb, kPitch128, rt * 16, ks * 32), b);
+        Op<P>::mma(aq, make_frag<P>(qvalid ? qa[ks] : zero4, qvalid ? qb[ks] : zero4), b);
       }
-      Op<P>::mma(acc, a, frag<P>(Kb, kPitch128, ct * 16, ks * 32));
-    }
-    float *G = which ? Gqk : Gkk;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) G[(rt * 16 + acc_row(r)) * kLdS + ct * 16 + acc_col()] = acc[r];
-  }
-  block_sync_lds();   // K is dead from here: kbuf becomes L and X
-
-  for (int j = h; j < p.n_v; j += p.n_qk) {
-    // Cumulative log-decay (0 past len, so gam stays at its last value) and
-    // beta. gam reaches a few hundred inside a chunk and only its differences
-    // gam_r - gam_m are used: in fp32 they would lose ~|gam| * 6e-8 to
-    // cancellation, so the scan and the differences are fp64.
-    if (wave == 0) {
-      const size_t e = static_cast<size_t>(t0 + min(lane, len - 1)) * p.n_v + j;
-      const double gr = lane < len ? static_cast<double>(p.g[e]) : 0.0;
-      const float br = lane < len ? p.beta[e] : 0.f;
-      const double gm = wave_inclusive_scan_d(gr);
-      gam_s[lane] = gm;
-      bet_s[lane] = br;
-      ws.gam[(static_cast<size_t>(cid) * p.n_v + j) * kChunk + lane] = gm;
-    }
-    block_sync_lds();
-
-    const size_t wsm = (static_cast<size_t>(cid) * p.n_v + j) * kChunk * kWsPitch;
-    // L = I + A into LDS and P to the workspace, 4 consecutive m per item.
-    for (int it = tid; it < kChunkMat / 4; it += kLocalThreads) {
-      const int r = it / (kChunk / 4), m0 = 4 * (it % (kChunk / 4));
-      f32x4 pv = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = m0 + e;
-        float lv = r == m ? 1.f : 0.f;
-        if (m <= r) {
-          const float dec = expf(static_cast<float>(gam_s[r] - gam_s[m]));
-          pv[e] = dec * Gqk[r * kLdS + m];
-          if (m < r) lv = bet_s[r] * dec * Gkk[r * kLdS + m];
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * rt + acc_row(r), col = 16 * ct + acc_col();
+        if (col <= row) {
+          Gk[tri(row, col)] = ak[r];
+          Gq[tri(row, col)] = aq[r];
         }
-        Lm[r * kLdS + m] = lv;
-        Xm[r * kLdS + m] = 0.f;
       }
-      Op<P>::put4(ws.P + wsm + r * kWsPitch, m0, pv);
     }
-    block_sync_lds();
+  }
+  block_sync_lds();   // K is dead from here: buf becomes the solving waves' matrices
 
-    // Diagonal blocks: X_bb = L_bb^-1 by forward substitution, one column per lane.
-    if (lane < 16) {
-      const int b = wave, c = lane;
-      const float *Lb = Lm + (b * 16) * kLdS + b * 16;
-      float x[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float acc = r == c ? 1.f : 0.f;
-#pragma unroll
-        for (int m = 0; m < r; ++m) acc -= Lb[r * kLdS + m] * x[m];
-        x[r] = acc;
+  const int nvh = p.n_v / p.n_qk;
+  for (int u0 = 0; u0 < nvh; u0 += kSolveWaves) {
+    const int u = u0 + wave;
+    if (wave < kSolveWaves && u < nvh) {
+      const int j = h + u * p.n_qk;
+      float *Lx = reinterpret_cast<float *>(buf) + wave * kChunk * kLdS;
+      double *gam = gam_s[wave];
+      float *bet = bet_s[wave];
+      // Cumulative log-decay (0 past len, so gam stays at its last value) and
+      // beta. gam reaches a few hundred inside a chunk and only its
+      // differences gam_r - gam_m are used: in fp32 they would lose
+      // ~|gam| * 6e-8 to cancellation, so the scan and the differences are fp64.
+      {
+        const size_t e = static_cast<size_t>(t0 + min(lane, len - 1)) * p.n_v + j;
+        const double gr = lane < len ? static_cast<double>(p.g[e]) : 0.0;
+        const float br = lane < len ? p.beta[e] : 0.f;
+        const double gm = wave_inclusive_scan_d(gr);
+        gam[lane] = gm;
+        bet[lane] = br;
+        ws.gam[(static_cast<size_t>(cid) * p.n_v + j) * kChunk + lane] = gm;
       }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) Xm[(b * 16 + r) * kLdS + b * 16 + c] = x[r];
-    }
-    block_sync_lds();
+      wave_sync_lds();
 
-    // Off-diagonal blocks, block row by block row:
-    //   X_ij = -X_ii * sum_{k=j}^{i-1} L_ik X_kj   (wave j computes X_ij)
-    for (int bi = 1; bi < 4; ++bi) {
-      const int bj = wave;
-      if (bj < bi) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int bk = bj; bk < bi; ++bk) {
+      uint8_t *wv = ws.v + (static_cast<size_t>(cid) * p.n_v + j) * kVBytes;   // Tm, then P
+      // L = I + A into LDS and P to the workspace, 4 consecutive m per item.
+      for (int it = lane; it < kChunkMat / 4; it += kWave) {
+        const int r = it / (kChunk / 4), m0 = 4 * (it % (kChunk / 4));
+        f32x4 pv = zero4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = m0 + e;
+          float lv = r == m ? 1.f : 0.f;
+          if (m <= r) {
+            const float dec = expf(static_cast<float>(gam[r] - gam[m]));
+            pv[e] = dec * Gq[tri(r, m)];
+            if (m < r) lv = bet[r] * dec * Gk[tri(r, m)];
+          }
+          Lx[r * kLdS + m] = lv;
+        }
+        FragIO<P>::put4(wv + kMatBytes, kChunk / 32, r, m0, pv);
+      }
+      wave_sync_lds();
+
+      // Diagonal blocks X_bb = L_bb^-1 by forward substitution: lane 16 b + c
+      // owns column c of block b and writes it over L_bb.
+      {
+        const int b = lane >> 4, c = lane & 15;
+        const float *Lb = Lx + (b * 16) * kLdS + b * 16;
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float acc = r == c ? 1.f : 0.f;
+#pragma unroll
+          for (int m = 0; m < r; ++m) acc -= Lb[r * kLdS + m] * x[m];
+          x[r] = acc;
+        }
+        wave_sync_lds();
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Lx[(b * 16 + r) * kLdS + b * 16 + c] = x[r];
+      }
+      wave_sync_lds();
+
+      // Off-diagonal blocks, in place: for block row i and j = 0 .. i-1 in
+      // order, X_ij = -X_ii * sum_{k=j}^{i-1} L_ik X_kj. Block (i, k) still
+      // holds L_ik for k >= j (only blocks left of j were overwritten), and
+      // blocks of rows above i already hold X.
+      float *ts = Tsc[wave];
+      for (int bi = 1; bi < 4; ++bi) {
+        for (int bj = 0; bj < bi; ++bj) {
+          f32x4 acc = zero4;
+          for (int bk = bj; bk < bi; ++bk) {
+#pragma unroll
+            for (int k4 = 0; k4 < 4; ++k4) {
+              const float a = Lx[(bi * 16 + (lane & 15)) * kLdS + bk * 16 + 4 * k4 + (lane >> 4)];
+              const float b = Lx[(bk * 16 + 4 * k4 + (lane >> 4)) * kLdS + bj * 16 + (lane & 15)];
+              acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ts[acc_row(r) * 17 + acc_col()] = acc[r];
+          wave_sync_lds();
+          f32x4 x = zero4;
 #pragma unroll
           for (int k4 = 0; k4 < 4; ++k4) {
-            const float a = Lm[(bi * 16 + (lane & 15)) * kLdS + bk * 16 + 4 * k4 + (lane >> 4)];
-            const float b = Xm[(bk * 16 + 4 * k4 + (lane >> 4)) * kLdS + bj * 16 + (lane & 15)];
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+            const float a = Lx[(bi * 16 + (lane & 15)) * kLdS + bi * 16 + 4 * k4 + (lane >> 4)];
+            const float b = ts[(4 * k4 + (lane >> 4)) * 17 + (lane & 15)];
+            x = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, x, 0, 0, 0);
           }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Lx[(bi * 16 + acc_row(r)) * kLdS + bj * 16 + acc_col()] = -x[r];
+          wave_sync_lds();
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Tsc[wave][acc_row(r) * 17 + acc_col()] = acc[r];
       }
-      block_sync_lds();
-      if (bj < bi) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) {
-          const float a = Xm[(bi * 16 + (lane & 15)) * kLdS + bi * 16 + 4 * k4 + (lane >> 4)];
-          const float b = Tsc[wave][(4 * k4 + (lane >> 4)) * 17 + (lane & 15)];
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Xm[(bi * 16 + acc_row(r)) * kLdS + bj * 16 + acc_col()] = -acc[r];
-      }
-      block_sync_lds();
-    }
 
-    // Tm = X diag(beta) to the workspace.
-    for (int it = tid; it < kChunkMat / 4; it += kLocalThreads) {
-      const int r = it / (kChunk / 4), m0 = 4 * (it % (kChunk / 4));
-      f32x4 tv;
+      // Tm = X diag(beta) (lower triangle) to the workspace.
+      for (int it = lane; it < kChunkMat / 4; it += kWave) {
+        const int r = it / (kChunk / 4), m0 = 4 * (it % (kChunk / 4));
+        f32x4 tv;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) tv[e] = m0 + e <= r ? Xm[r * kLdS + m0 + e] * bet_s[m0 + e] : 0.f;
-      Op<P>::put4(ws.T + wsm + r * kWsPitch, m0, tv);
+        for (int e = 0; e < 4; ++e) tv[e] = m0 + e <= r ? Lx[r * kLdS + m0 + e] * bet[m0 + e] : 0.f;
+        FragIO<P>::put4(wv, kChunk / 32, r, m0, tv);
+      }
     }
-    block_sync_lds();
   }
 }
 
 // ---------------------------------------------------------------------------
-// chunk_state: per (sequence, V-head, 32-column slab). 8 waves. While chunk
-// c is computed, chunk c+1's K, Q, Tm, P, V and gam are loaded into
-// registers; they are written to LDS after chunk c's last LDS read.
-//
-// Work per chunk (wave w, rt = w % 4):
-//   X/Y : waves 0-3 X = K S, waves 4-7 Y = Q S, rows 16 rt, both column tiles
-//   R   : waves 0-3 R = V - diag(Gam) X  -> R^T in LDS
-//   D   : wave w tile (rt, w / 4) of Tm R  -> D^T and (diag(k~) D)^T in LDS,
-//         k~_r = exp(gam_n - gam_r)
-//   O   : waves 4-7 O = s (diag(Gam) Y + P D), rows 16 rt
-//   S   : wave w state rows 16 w: S <- Gam_n S + K^T diag(k~) D
+// chunk_state: per (sequence, V-head, 32-column slab). 8 waves; wave w has
+// rt = w % 4. Per chunk:
+//   X/Y : waves 0-3 X = K S, waves 4-7 Y = Q S (rows 16 rt, both column tiles)
+//   R   : waves 0-3 R = V - diag(Gam) X            -> R^T in LDS
+//   D   : waves 0-3 D = Tm R (rows 16 rt)          -> D^T and (diag(k~) D)^T
+//         in LDS, k~_r = exp(gam_n - gam_r)
+//   O   : waves 4-7 O = s (diag(Gam) Y + P D)      (rows 16 rt)
+//   S   : all waves S <- Gam_n S + K^T diag(k~) D  (state rows 16 w)
+// Left operands stay in registers: K or Q rows (4 fragments), Tm or P rows
+// (2), K^T rows (2); each set is reloaded for the next chunk right after its
+// last use in this one, so its loads overlap the rest of the chunk.
 template <Prec P, typename TA>
 __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParams p, int64_t max_chunks) {
-  __shared__ __attribute__((aligned(16))) uint8_t Kb[kChunk * kPitch128];    // K rows, blocked over i
-  __shared__ __attribute__((aligned(16))) uint8_t Qb[kChunk * kPitch128];    // Q rows
+  using Frag = typename Op<P>::Frag;
   __shared__ __attribute__((aligned(16))) uint8_t Stb[kSlab * kPitch128];    // S^T rows c, blocked over i
-  __shared__ __attribute__((aligned(16))) uint8_t Tb[kChunk * kPitch64];     // Tm rows r, blocked over m
-  __shared__ __attribute__((aligned(16))) uint8_t Pb[kChunk * kPitch64];     // P rows r
   __shared__ __attribute__((aligned(16))) uint8_t Rtb[kSlab * kPitch64];     // R^T rows c, blocked over r
   __shared__ __attribute__((aligned(16))) uint8_t Dtb[kSlab * kPitch64];     // D^T
   __shared__ __attribute__((aligned(16))) uint8_t Dsb[kSlab * kPitch64];     // (diag(k~) D)^T
+  __shared__ __attribute__((aligned(16))) float Vs[kChunk * kLdV];           // V rows of the slab (fp32)
   __shared__ float G_s[kChunk];            // exp(gam_r)
   __shared__ float ksc_s[kChunk];          // exp(gam_n - gam_r)
-  __shared__ __attribute__((aligned(16))) float Vs[kChunk * kLdV];   // V rows of the slab (fp32)
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
@@ -311,10 +375,9 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
   // Chunk ids past the workspace only arise from cu_seqlens outside the
   // contract; never index past the workspace.
   if (cid0 + nchunks > max_chunks) return;
-  const Workspace ws = carve(p.ws, max_chunks, p.n_v);
+  const Workspace ws = carve(p.ws, max_chunks, p.n_qk, p.n_v);
   const float scale = 0.08838834764831845f;  // 1/sqrt(128)
   const int col_base = slab * kSlab;
-  const size_t qk_stride = static_cast<size_t>(p.n_qk) * kHeadDim;
   const size_t v_stride = static_cast<size_t>(p.n_v) * kHeadDim;
   TA *o = static_cast<TA *>(p.o);
 
@@ -330,98 +393,78 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) put_acc_t<P>(Stb, kPitch128, 16 * wave, 16 * ct, S[ct]);
 
-  // Prefetch registers for one chunk.
-  constexpr int kRowsPer = kChunk * (kHeadDim / 4) / kStateThreads;    // f32x4 of K (and of Q) per thread
-  constexpr int kMatPer = kChunk * kWsPitch / 16 / kStateThreads;      // 16-byte pieces of Tm (and of P)
-  f32x4 pk[kRowsPer], pq[kRowsPer];
-  static_assert(kMatPer == 2, "two 16-byte pieces of Tm and of P per thread");
-  uint4 pt0, pt1, pp0, pp1;
-  f32x4 pvv = {0.f, 0.f, 0.f, 0.f};   // one 16-byte piece of the V slab
-  // Per-thread pieces: K/Q rows r_u = (tid + u * 512) / 32, 4 floats at 4 * (tid % 32);
-  // V row tid / 8, 4 floats at 4 * (tid % 8).
-  const int kq_c4 = tid % (kHeadDim / 4);
+  // Operand sources of chunk c (fragment-major blocks).
+  const size_t qk_step = static_cast<size_t>(p.n_qk) * kQkBytes;
+  const size_t v_step = static_cast<size_t>(p.n_v) * kVBytes;
+  const uint8_t *qk0 = ws.qk + (static_cast<size_t>(cid0) * p.n_qk + hk) * kQkBytes;
+  const uint8_t *v0 = ws.v + (static_cast<size_t>(cid0) * p.n_v + j) * kVBytes;
+  const uint8_t *xy_src0 = qk0 + (x_wave ? 0 : kKBytes);             // K rows or Q rows
+  const uint8_t *d_src0 = v0 + (x_wave ? 0 : kMatBytes);             // Tm rows or P rows
+  const uint8_t *kt_src0 = qk0 + 2 * kKBytes;                        // K^T rows
   const int v_row = tid / (kSlab / 4), v_c4 = tid % (kSlab / 4);
+
+  Frag fxy[kHeadDim / 32], fd[kChunk / 32], fk[kChunk / 32];
+  f32x4 pvv;
   double pg = 0.0, pg_end = 0.0;
 
-#define GDN_PREFETCH(c)                                                                              \
+#define GDN_LOAD_XY(c)                                                                               \
+  _Pragma("unroll") for (int ks = 0; ks < kHeadDim / 32; ++ks)                                       \
+    fxy[ks] = FragIO<P>::load(xy_src0 + (c) * qk_step, kHeadDim / 32, rt, ks)
+#define GDN_LOAD_D(c)                                                                                \
+  _Pragma("unroll") for (int ks = 0; ks < kChunk / 32; ++ks)                                         \
+    fd[ks] = FragIO<P>::load(d_src0 + (c) * v_step, kChunk / 32, rt, ks)
+#define GDN_LOAD_KT(c)                                                                               \
+  _Pragma("unroll") for (int ks = 0; ks < kChunk / 32; ++ks)                                         \
+    fk[ks] = FragIO<P>::load(kt_src0 + (c) * qk_step, kChunk / 32, wave, ks)
+  // V slab piece and gam of chunk c (committed to LDS after the chunk before it).
+#define GDN_LOAD_VG(c)                                                                               \
   do {                                                                                               \
-    const int t0_ = seq0 + (c) * kChunk;                                                             \
-    const int len_ = min(kChunk, L - (c) * kChunk);                                                  \
-    const float *kg = p.k + t0_ * qk_stride + hk * kHeadDim + 4 * kq_c4;                             \
-    const float *qg = p.q + t0_ * qk_stride + hk * kHeadDim + 4 * kq_c4;                             \
-    _Pragma("unroll") for (int u = 0; u < kRowsPer; ++u) {                                           \
-      const int r = (tid + u * kStateThreads) / (kHeadDim / 4);                                      \
-      const int off = min(r, len_ - 1) * static_cast<int>(qk_stride);                                \
-      pk[u] = *reinterpret_cast<const f32x4 *>(kg + off);                                            \
-      pq[u] = *reinterpret_cast<const f32x4 *>(qg + off);                                            \
-    }                                                                                                \
-    const size_t wsi = static_cast<size_t>(cid0 + (c)) * p.n_v + j;                                  \
-    {                                                                                                \
-      const uint4 *tg = reinterpret_cast<const uint4 *>(ws.T + wsi * kChunk * kWsPitch);             \
-      const uint4 *pg4 = reinterpret_cast<const uint4 *>(ws.P + wsi * kChunk * kWsPitch);            \
-      pt0 = tg[tid];                                                                                 \
-      pt1 = tg[tid + kStateThreads];                                                                 \
-      pp0 = pg4[tid];                                                                                \
-      pp1 = pg4[tid + kStateThreads];                                                                \
-    }                                                                                                \
+    const int t0_ = seq0 + (c) * kChunk, len_ = min(kChunk, L - (c) * kChunk);                       \
+    pvv = *reinterpret_cast<const f32x4 *>(p.v + (t0_ + min(v_row, len_ - 1)) * v_stride +          \
+                                           j * kHeadDim + col_base + 4 * v_c4);                      \
     if (tid < kChunk) {                                                                              \
-      pg = ws.gam[wsi * kChunk + tid];                                                               \
-      pg_end = ws.gam[wsi * kChunk + kChunk - 1];                                                    \
+      const double *gm = ws.gam + (static_cast<size_t>(cid0 + (c)) * p.n_v + j) * kChunk;            \
+      pg = gm[tid];                                                                                  \
+      pg_end = gm[kChunk - 1];                                                                       \
     }                                                                                                \
-    pvv = *reinterpret_cast<const f32x4 *>(p.v + (t0_ + min(v_row, len_ - 1)) * v_stride + j * kHeadDim + \
-                                           col_base + 4 * v_c4);                                     \
   } while (0)
-
-// Rows past the chunk's length were loaded from its last row; they are
-// zeroed here, where the loaded values are first used, so that the loads
-// stay in flight until then.
-#define GDN_COMMIT(c)                                                                                \
+  // Rows past the chunk's length were loaded from its last row and are zeroed
+  // here, at first use, so that the loads stay in flight until then.
+#define GDN_COMMIT_VG(c)                                                                             \
   do {                                                                                               \
     const int len_ = min(kChunk, L - (c) * kChunk);                                                  \
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};                                                        \
-    _Pragma("unroll") for (int u = 0; u < kRowsPer; ++u) {                                           \
-      const int idx = tid + u * kStateThreads, r = idx / (kHeadDim / 4), c4 = idx % (kHeadDim / 4);  \
-      Op<P>::put4(Kb + r * kPitch128, 4 * c4, r < len_ ? pk[u] : zero4);                             \
-      Op<P>::put4(Qb + r * kPitch128, 4 * c4, r < len_ ? pq[u] : zero4);                             \
-    }                                                                                                \
-    {                                                                                                \
-      const int r0 = tid / (kWsPitch / 16), w0 = (tid % (kWsPitch / 16)) * 16;                       \
-      const int r1 = r0 + kStateThreads / (kWsPitch / 16);                                           \
-      *reinterpret_cast<uint4 *>(Tb + r0 * kPitch64 + w0) = pt0;                                     \
-      *reinterpret_cast<uint4 *>(Tb + r1 * kPitch64 + w0) = pt1;                                     \
-      *reinterpret_cast<uint4 *>(Pb + r0 * kPitch64 + w0) = pp0;                                     \
-      *reinterpret_cast<uint4 *>(Pb + r1 * kPitch64 + w0) = pp1;                                     \
-    }                                                                                                \
+    *reinterpret_cast<f32x4 *>(Vs + v_row * kLdV + 4 * v_c4) = v_row < len_ ? pvv : zero4;          \
     if (tid < kChunk) {                                                                              \
       G_s[tid] = expf(static_cast<float>(pg));                                                       \
       ksc_s[tid] = expf(static_cast<float>(pg_end - pg));                                            \
     }                                                                                                \
-    *reinterpret_cast<f32x4 *>(Vs + v_row * kLdV + 4 * v_c4) = v_row < len_ ? pvv : zero4;          \
   } while (0)
 
   if (nchunks > 0) {
-    GDN_PREFETCH(0);
-    GDN_COMMIT(0);
+    GDN_LOAD_XY(0);
+    GDN_LOAD_D(0);
+    GDN_LOAD_KT(0);
+    GDN_LOAD_VG(0);
+    GDN_COMMIT_VG(0);
   }
 
   for (int ci = 0; ci < nchunks; ++ci) {
     const int t0 = seq0 + ci * kChunk;
     const int len = min(kChunk, L - ci * kChunk);
-    block_sync_lds();                        // chunk ci in LDS, St = S at chunk start
+    // Operands of the next chunk (the last chunk reloads itself, so every
+    // iteration issues the same loads).
+    const int cn = min(ci + 1, nchunks - 1);
+    block_sync_lds();                        // St, V, gam of chunk ci visible
     const float g_end = G_s[kChunk - 1];
-    // The next chunk's operands are loaded while this one is computed. The
-    // last chunk reloads itself, so that every iteration issues and commits
-    // the same loads (no loads left in flight across the loop edge).
-    const int cnext = min(ci + 1, nchunks - 1);
-    GDN_PREFETCH(cnext);
+    GDN_LOAD_VG(cn);
 
     // X = K S (waves 0-3) or Y = Q S (waves 4-7), rows 16 rt, both column tiles.
     f32x4 XY[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    const uint8_t *Asrc = x_wave ? Kb : Qb;
 #pragma unroll
     for (int ks = 0; ks < kHeadDim / 32; ++ks)
-      Op<P>::mma2(XY[0], XY[1], frag<P>(Asrc, kPitch128, 16 * rt, 32 * ks), frag<P>(Stb, kPitch128, 0, 32 * ks),
-                  frag<P>(Stb, kPitch128, 16, 32 * ks));
+      Op<P>::mma2(XY[0], XY[1], fxy[ks], frag<P>(Stb, kPitch128, 0, 32 * ks), frag<P>(Stb, kPitch128, 16, 32 * ks));
+    GDN_LOAD_XY(cn);
     if (x_wave) {
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
@@ -436,17 +479,20 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
     }
     block_sync_lds();
 
-    {  // D = Tm R: tile (rt, wave / 4); D^T and (diag(k~) D)^T to LDS.
-      const int ct = wave >> 2;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (x_wave) {  // D = Tm R, rows 16 rt; D^T and (diag(k~) D)^T to LDS.
+      f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int ks = 0; ks < kChunk / 32; ++ks)
-        Op<P>::mma(acc, frag<P>(Tb, kPitch64, 16 * rt, 32 * ks), frag<P>(Rtb, kPitch64, 16 * ct, 32 * ks));
-      put_acc_t<P>(Dtb, kPitch64, 16 * rt, 16 * ct, acc);
-      f32x4 ds;
+        Op<P>::mma2(acc[0], acc[1], fd[ks], frag<P>(Rtb, kPitch64, 0, 32 * ks), frag<P>(Rtb, kPitch64, 16, 32 * ks));
+      GDN_LOAD_D(cn);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ds[r] = acc[r] * ksc_s[16 * rt + acc_row(r)];
-      put_acc_t<P>(Dsb, kPitch64, 16 * rt, 16 * ct, ds);
+      for (int ct = 0; ct < 2; ++ct) {
+        put_acc_t<P>(Dtb, kPitch64, 16 * rt, 16 * ct, acc[ct]);
+        f32x4 ds;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ds[r] = acc[ct][r] * ksc_s[16 * rt + acc_row(r)];
+        put_acc_t<P>(Dsb, kPitch64, 16 * rt, 16 * ct, ds);
+      }
     }
     block_sync_lds();
 
@@ -454,8 +500,8 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
       f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int ks = 0; ks < kChunk / 32; ++ks)
-        Op<P>::mma2(acc[0], acc[1], frag<P>(Pb, kPitch64, 16 * rt, 32 * ks), frag<P>(Dtb, kPitch64, 0, 32 * ks),
-                    frag<P>(Dtb, kPitch64, 16, 32 * ks));
+        Op<P>::mma2(acc[0], acc[1], fd[ks], frag<P>(Dtb, kPitch64, 0, 32 * ks), frag<P>(Dtb, kPitch64, 16, 32 * ks));
+      GDN_LOAD_D(cn);
       // Stage this wave's 16 x 32 rows of O in the (now dead) R^T buffer,
       // then write them out with one 16-byte store per lane (bf16) or two (fp32).
       static_assert(4 * 16 * kLdO * sizeof(float) <= sizeof(Rtb), "O staging must fit the R^T buffer");
@@ -478,21 +524,23 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
         Act<TA>::store4(o, dst + 4, make_float4(b[0], b[1], b[2], b[3]));
       }
     }
-    // S <- Gam_n S + K^T (diag(k~) D); rows 16 wave. K^T is read transposed
-    // from the K rows.
+    // S <- Gam_n S + K^T (diag(k~) D); state rows 16 wave.
     S[0] = S[0] * g_end;
     S[1] = S[1] * g_end;
 #pragma unroll
     for (int ks = 0; ks < kChunk / 32; ++ks)
-      Op<P>::mma2(S[0], S[1], frag_t<P>(Kb, kPitch128, 16 * wave, 32 * ks), frag<P>(Dsb, kPitch64, 0, 32 * ks),
-                  frag<P>(Dsb, kPitch64, 16, 32 * ks));
-    block_sync_lds();                        // every read of chunk ci's LDS data is done
+      Op<P>::mma2(S[0], S[1], fk[ks], frag<P>(Dsb, kPitch64, 0, 32 * ks), frag<P>(Dsb, kPitch64, 16, 32 * ks));
+    GDN_LOAD_KT(cn);
+    block_sync_lds();                        // every LDS read of chunk ci is done
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) put_acc_t<P>(Stb, kPitch128, 16 * wave, 16 * ct, S[ct]);
-    GDN_COMMIT(cnext);
+    GDN_COMMIT_VG(cn);
   }
-#undef GDN_PREFETCH
-#undef GDN_COMMIT
+#undef GDN_LOAD_XY
+#undef GDN_LOAD_D
+#undef GDN_LOAD_KT
+#undef GDN_LOAD_VG
+#undef GDN_COMMIT_VG
 
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct)
@@ -503,9 +551,9 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
 
 }  // namespace
 
-size_t prefill_workspace_bytes(int n_seqs, int n_tokens, int n_v) {
+size_t prefill_workspace_bytes(int n_seqs, int n_tokens, int n_qk, int n_v) {
   const int64_t chunks = max_chunks(n_seqs, n_tokens);
-  return static_cast<size_t>(chunks) * n_v * (2 * kChunk * kWsPitch + kChunk * sizeof(double));
+  return static_cast<size_t>(chunks) * (n_qk * kQkBytes + n_v * (kVBytes + kChunk * sizeof(double)));
 }
 
 hipError_t launch_prefill(const PrefillParams &p, gdn_dtype act, hipStream_t s) {
