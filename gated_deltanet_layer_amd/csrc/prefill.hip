@@ -49,6 +49,7 @@ constexpr int kLocalThreads = 256;        // chunk_local: 4 waves
 constexpr int kStateThreads = 512;        // chunk_state: 8 waves
 constexpr int kSlab = 32;                 // state columns per chunk_state block
 constexpr int kChunkMat = kChunk * kChunk;
+constexpr int kXcds = 8;                  // accelerator complex dies on MI355X
 // Row pitches (bytes) of blocked operands in LDS: 128 or 64 contraction
 // indices (16 or 8 blocks of 32 bytes) plus 16 bytes to spread LDS banks.
 constexpr int kPitch128 = (kHeadDim / 8) * kBlk + 16;   // 528
@@ -362,10 +363,17 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
   const int lane = lane_id();
   const int rt = wave & 3;
   const bool x_wave = wave < 4;
+  // Block order: workgroups are dealt to the 8 XCDs round-robin (block b on
+  // XCD b % 8), each with its own L2. Blocks b = 32 g + 8 s + x hold slab s
+  // of (sequence, V-head) pair 8 g + x, so the 4 slabs of a pair, and the
+  // V-heads j, j + 8, ... that share K-head operands, run on one XCD and
+  // share its L2.
   const int nslab = kHeadDim / kSlab;
-  const int slab = blockIdx.x % nslab;
-  const int j = (blockIdx.x / nslab) % p.n_v;
-  const int n = blockIdx.x / (nslab * p.n_v);
+  const int pair = kXcds * (blockIdx.x / (kXcds * nslab)) + blockIdx.x % kXcds;
+  const int slab = (blockIdx.x / kXcds) % nslab;
+  if (pair >= p.n_seqs * p.n_v) return;
+  const int j = pair % p.n_v;
+  const int n = pair / p.n_v;
   const int hk = j % p.n_qk;
   const int seq0 = p.cu[n];
   const int L = p.cu[n + 1] - seq0;
@@ -559,7 +567,8 @@ size_t prefill_workspace_bytes(int n_seqs, int n_tokens, int n_qk, int n_v) {
 hipError_t launch_prefill(const PrefillParams &p, gdn_dtype act, hipStream_t s) {
   const int64_t chunks = max_chunks(p.n_seqs, p.n_tokens);
   const dim3 grid_local(static_cast<unsigned>(chunks), static_cast<unsigned>(p.n_qk));
-  const dim3 grid_state(static_cast<unsigned>(static_cast<int64_t>(p.n_seqs) * p.n_v * (kHeadDim / kSlab)));
+  const int64_t pairs = static_cast<int64_t>(p.n_seqs) * p.n_v;
+  const dim3 grid_state(static_cast<unsigned>((pairs + kXcds - 1) / kXcds * kXcds * (kHeadDim / kSlab)));
   if (act == GDN_BF16) {
     if (p.n_tokens > 0)
       hipLaunchKernelGGL(chunk_local_kernel<Prec::BF16X3>, grid_local, dim3(kLocalThreads), 0, s, p, chunks);
