@@ -234,7 +234,7 @@ gdn_status gdn_gated_rmsnorm(const gdn_config *cfg, int64_t n_rows, const void *
   if (n_rows < 0) return GDN_E_INVALID_ARG;
   if (n_rows == 0) return GDN_OK;
   if (!o || !z || !norm_w || !y) return GDN_E_INVALID_ARG;
-  if ((n_rows + 3) / 4 > kMaxGrid) return GDN_E_UNSUPPORTED;
+  if ((n_rows + 15) / 16 > kMaxGrid) return GDN_E_UNSUPPORTED;
   const size_t bytes = static_cast<size_t>(n_rows) * kHeadDim * act_size(cfg);
   // y may be o (in place); nothing else may overlap y.
   if (y != o && overlap(y, bytes, o, bytes)) return GDN_E_INVALID_ARG;

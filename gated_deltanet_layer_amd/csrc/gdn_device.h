@@ -67,10 +67,33 @@ __device__ __forceinline__ float siluf_(float x) { return x / (1.0f + expf(-x));
 // ------------------------------------------------------ wave primitives
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
+// x + x from another lane of the same 16-lane row, by a DPP lane pattern.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_add(float x) {
+  const int y = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xf, 0xf, true);
+  return x + __builtin_bit_cast(float, y);
+}
+
+// Sum over each 16-lane row, left in every lane of the row: quad_perm
+// [1,0,3,2] and [2,3,0,1] give quad sums, row_half_mirror adds the other
+// quad of each 8-lane half, row_mirror adds the other half.
+__device__ __forceinline__ float row16_sum(float x) {
+  x = dpp_add<0xb1>(x);
+  x = dpp_add<0x4e>(x);
+  x = dpp_add<0x141>(x);
+  x = dpp_add<0x140>(x);
   return x;
+}
+
+// Sum over the 64 lanes of the wave (every lane gets it): row sums by DPP,
+// then the four rows' sums read from lanes 0, 16, 32, 48.
+__device__ __forceinline__ float wave_sum(float x) {
+  x = row16_sum(x);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
+  return (r0 + r1) + (r2 + r3);
 }
 
 __device__ __forceinline__ int wave_sum_i(int x) {

@@ -8,10 +8,11 @@
 // HF checkpoint").
 //
 // Grid: x = token tiles (kPrepTile tokens of one sequence; an empty sequence
-// owns one tile that only moves its conv state), y = head block (128 fused
-// channels: Hqk q heads, Hqk k heads, Hv v heads). One wave per block; each
-// lane owns 2 adjacent channels and keeps the 3 previous raw rows in
-// registers, so each qkv row is read once per tile (plus a 3-row halo).
+// owns one tile that only moves its conv state), y = groups of 4 head blocks
+// (a head block is 128 fused channels: Hqk q heads, Hqk k heads, Hv v
+// heads). One wave per head block, so a block reads 4 adjacent 256-byte
+// pieces of every bf16 row; each lane owns 2 adjacent channels and loads the tile's rows plus a 3-row halo
+// into registers before computing, so all its loads are in flight together.
 // HBM-bound: per token it reads C act values and writes C fp32 values.
 #include "gdn_device.h"
 #include "gdn_internal.h"
@@ -19,10 +20,13 @@
 namespace gdn {
 namespace {
 
+constexpr int kPrepWaves = 4;   // consecutive head blocks per block (1 KB of each bf16 row)
+
 template <typename TA>
-__global__ __launch_bounds__(kWave) void prep_kernel(PrepParams p) {
+__global__ __launch_bounds__(kPrepWaves * kWave) void prep_kernel(PrepParams p) {
   const int lane = lane_id();
-  const int hb = blockIdx.y;
+  const int hb = blockIdx.y * kPrepWaves + threadIdx.x / kWave;
+  if (hb >= 2 * p.n_qk + p.n_v) return;
   int n, tile;
   if (!find_unit(p.cu, p.n_seqs, blockIdx.x, kPrepTile, 1, &n, &tile)) return;
   const int seq0 = p.cu[n];
@@ -43,15 +47,20 @@ __global__ __launch_bounds__(kWave) void prep_kernel(PrepParams p) {
   const int tau0 = tile * kPrepTile;
   const int ntok = min(kPrepTile, L - tau0);
 
-  // Raw rows tau0-3 .. tau0-1 of [state; x]: the window before the tile.
-  float2 xm[kConvK - 1];
+  // Raw rows tau0-3 .. tau0+15 of [state; x], all loaded before any is used.
+  // Rows before the sequence come from the conv state; rows past its end are
+  // clamped to its last row and never used.
+  constexpr int kRows = kPrepTile + kConvK - 1;
+  float2 xr[kRows];
 #pragma unroll
-  for (int r = 0; r < kConvK - 1; ++r) {
+  for (int r = 0; r < kRows; ++r) {
     const int pos = tau0 - (kConvK - 1) + r;
-    xm[r] = pos < 0 ? Act<TA>::load2(st_in, st_base + static_cast<size_t>(pos + kConvK - 1) * C + c)
-                    : Act<TA>::load2(qkv, static_cast<size_t>(seq0 + pos) * C + c);
+    // An empty sequence reads its state row 0 instead (never used).
+    const bool from_state = pos < 0 || L == 0;
+    const TA *src = from_state ? st_in + st_base + static_cast<size_t>(max(pos + kConvK - 1, 0)) * C
+                               : qkv + static_cast<size_t>(seq0 + min(pos, L - 1)) * C;
+    xr[r] = Act<TA>::load2(src, c);
   }
-  const float2 old0 = xm[0], old1 = xm[1], old2 = xm[2];
 
   const bool is_qk = hb < 2 * p.n_qk;
   float *dst;
@@ -67,23 +76,22 @@ __global__ __launch_bounds__(kWave) void prep_kernel(PrepParams p) {
     dst_stride = p.n_v * kHeadDim;
   }
 
-  for (int i = 0; i < ntok; ++i) {
-    const size_t t = static_cast<size_t>(seq0 + tau0 + i);
-    const float2 x = Act<TA>::load2(qkv, t * C + c);
-    float y0 = w0.x * xm[0].x + w0.y * xm[1].x + w0.z * xm[2].x + w0.w * x.x;
-    float y1 = w1.x * xm[0].y + w1.y * xm[1].y + w1.z * xm[2].y + w1.w * x.y;
-    y0 = siluf_(y0);
-    y1 = siluf_(y1);
-    if (is_qk) {
-      const float ss = wave_sum(y0 * y0 + y1 * y1);
-      const float inv = 1.0f / fmaxf(sqrtf(ss), p.l2_eps);
-      y0 *= inv;
-      y1 *= inv;
+#pragma unroll
+  for (int i = 0; i < kPrepTile; ++i) {
+    if (i < ntok) {
+      const size_t t = static_cast<size_t>(seq0 + tau0 + i);
+      float y0 = w0.x * xr[i].x + w0.y * xr[i + 1].x + w0.z * xr[i + 2].x + w0.w * xr[i + 3].x;
+      float y1 = w1.x * xr[i].y + w1.y * xr[i + 1].y + w1.z * xr[i + 2].y + w1.w * xr[i + 3].y;
+      y0 = siluf_(y0);
+      y1 = siluf_(y1);
+      if (is_qk) {
+        const float ss = wave_sum(y0 * y0 + y1 * y1);
+        const float inv = 1.0f / fmaxf(sqrtf(ss), p.l2_eps);
+        y0 *= inv;
+        y1 *= inv;
+      }
+      *reinterpret_cast<float2 *>(dst + t * dst_stride + 2 * lane) = make_float2(y0, y1);
     }
-    *reinterpret_cast<float2 *>(dst + t * dst_stride + 2 * lane) = make_float2(y0, y1);
-    xm[0] = xm[1];
-    xm[1] = xm[2];
-    xm[2] = x;
   }
 
   if (!is_qk && lane < ntok) {
@@ -98,18 +106,25 @@ __global__ __launch_bounds__(kWave) void prep_kernel(PrepParams p) {
   // The first tile of a sequence writes its new conv state: rows L, L+1, L+2
   // of [state; x]. This lane read the old state of exactly these channels
   // above, so an in-place update is safe; no other tile reads the state.
+  // Written with constant register indices for each short length (rows
+  // 0..2 of [state; x] are xr[0..2], token 0 and 1 are xr[3] and xr[4]).
   if (tile == 0) {
-#pragma unroll
-    for (int r = 0; r < kConvK - 1; ++r) {
-      const int src = L + r;
-      float2 val;
-      if (src >= kConvK - 1) {
-        val = Act<TA>::load2(qkv, static_cast<size_t>(seq0 + src - (kConvK - 1)) * C + c);
-      } else {
-        val = src == 0 ? old0 : (src == 1 ? old1 : old2);
-      }
-      Act<TA>::store2(st_out, st_base + static_cast<size_t>(r) * C + c, val);
+    float2 s0, s1, s2;
+    if (L == 0) {
+      s0 = xr[0]; s1 = xr[1]; s2 = xr[2];
+    } else if (L == 1) {
+      s0 = xr[1]; s1 = xr[2]; s2 = xr[3];
+    } else if (L == 2) {
+      s0 = xr[2]; s1 = xr[3]; s2 = xr[4];
+    } else {
+      const size_t r0 = static_cast<size_t>(seq0 + L - (kConvK - 1)) * C + c;
+      s0 = Act<TA>::load2(qkv, r0);
+      s1 = Act<TA>::load2(qkv, r0 + C);
+      s2 = Act<TA>::load2(qkv, r0 + 2 * static_cast<size_t>(C));
     }
+    Act<TA>::store2(st_out, st_base + c, s0);
+    Act<TA>::store2(st_out, st_base + C + c, s1);
+    Act<TA>::store2(st_out, st_base + 2 * static_cast<size_t>(C) + c, s2);
   }
 }
 
@@ -117,11 +132,12 @@ __global__ __launch_bounds__(kWave) void prep_kernel(PrepParams p) {
 
 hipError_t launch_prep(const PrepParams &p, gdn_dtype act, hipStream_t s) {
   const int64_t tiles = (static_cast<int64_t>(p.n_tokens) + kPrepTile - 1) / kPrepTile + p.n_seqs;
-  const dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(2 * p.n_qk + p.n_v));
+  const int head_blocks = 2 * p.n_qk + p.n_v;
+  const dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>((head_blocks + kPrepWaves - 1) / kPrepWaves));
   if (act == GDN_BF16)
-    hipLaunchKernelGGL(prep_kernel<bf16_t>, grid, dim3(kWave), 0, s, p);
+    hipLaunchKernelGGL(prep_kernel<bf16_t>, grid, dim3(kPrepWaves * kWave), 0, s, p);
   else
-    hipLaunchKernelGGL(prep_kernel<float>, grid, dim3(kWave), 0, s, p);
+    hipLaunchKernelGGL(prep_kernel<float>, grid, dim3(kPrepWaves * kWave), 0, s, p);
   return hipGetLastError();
 }
 
