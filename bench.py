@@ -6,18 +6,22 @@ gdn_conv_gate_prep -> gdn_prefill_chunked -> gdn_gated_rmsnorm, inputs
 already resident in HBM. ``value`` is tokens per second over exactly
 ``--steps`` timed steps after ``--warmup`` untimed ones.
 
-The same run also times the decode path (gdn_conv_gate_prep ->
-gdn_decode_step -> gdn_gated_rmsnorm per token) on the batch-1 workload
-(32 V-heads, 1024 consecutive steps) and the batch-64 workload (256 steps),
-and reports them under "decode".
+The same run also times the decode path on the batch-1 workload (32 V-heads,
+1024 consecutive steps) and the batch-64 workload (256 steps), and reports
+them under "decode": the three calls per token (gdn_conv_gate_prep ->
+gdn_decode_step -> gdn_gated_rmsnorm) and the single gdn_decode_fused call,
+each with plain launches and as the whole loop captured in one HIP graph.
 
 Rooflines use the kernels' algorithmic work, timed with HIP events recorded
 on the stream the kernels run on:
   * chunked delta rule (gdn_prefill_chunked): 9,000,277 flop per
     (chunk of 64, V-head) -- 5 CH^2 d + 6 CH d^2 + CH^3/3 with CH = 64,
     d = 128, triangles counted once -- against the bf16 dense MFMA peak;
-  * decode step (gdn_decode_step): bytes of S read + written, q, k, v, beta,
-    g read and o written, against 8 TB/s HBM.
+  * decode step (gdn_decode_fused, graph replay): bytes of S read + written,
+    the token's qkv row, conv state read + written, z read, y written, the
+    logits and the parameters, against 8 TB/s HBM; and the delta-rule
+    kernel alone (gdn_decode_step): S read + written, q, k, v, beta, g read,
+    o written.
 The CPU baseline is the fp64 oracle, single-threaded, over the whole prefill
 workload once.
 """
@@ -163,55 +167,114 @@ def bench_prefill(steps: int, warmup: int):
 
 
 def decode_kernel_bytes(w: wl.Workload) -> int:
+    """Algorithmic bytes of one gdn_decode_step launch: S read + written, q, k,
+    v, beta, g read, o written."""
     N, Hqk, Hv, d = w.n_seqs, w.n_qk_heads, w.n_v_heads, w.head_dim
     act = 2 if w.act == "bf16" else 4
     return (2 * N * Hv * d * d * 4 + 2 * N * Hqk * d * 4 + N * Hv * d * 4 + 2 * N * Hv * 4
             + N * Hv * d * act)
 
 
+def decode_step_bytes(w: wl.Workload) -> int:
+    """Algorithmic bytes of one whole decode step (one gdn_decode_fused launch):
+    S read + written, the token's qkv row, conv state read + written, z read,
+    y written, the two logits, and the parameters (conv_w, dt_bias, A_log,
+    norm_w)."""
+    N, Hqk, Hv, d = w.n_seqs, w.n_qk_heads, w.n_v_heads, w.head_dim
+    act = 2 if w.act == "bf16" else 4
+    C = d * (2 * Hqk + Hv)
+    return (2 * N * Hv * d * d * 4 + N * C * act + 2 * N * 3 * C * act + 2 * N * Hv * d * act
+            + 2 * N * Hv * act + C * 4 * 4 + 2 * Hv * 4 + d * 4)
+
+
 def bench_decode(wid: int, warmup_steps: int = 32):
+    """Time the workload's whole decode loop four ways: the three calls per
+    step (prep, step, norm) and the single fused call, each with plain
+    launches and as one captured HIP graph replayed once."""
     w = wl.WORKLOADS[wid]
     x = wl.generate(w)
     t = {k: dev(v) for k, v in x.items()}
     cfg = B.make_config(w.n_qk_heads, w.n_v_heads, w.act)
-    run = Lyr.Decode(cfg, w.n_seqs)
-    conv, S = t["conv0"].clone(), t["S0"].clone()
+    N, steps = w.n_seqs, w.steps
+    three = Lyr.Decode(cfg, N)
+    conv = t["conv0"].clone()
+    fused = Lyr.DecodeFused(cfg, N, t["conv0"].clone())
+    S = t["S0"].clone()
     ys = torch.empty_like(t["z"])
-    steps = w.steps
 
-    def one(s, evs=None):
-        B.gdn_conv_gate_prep(cfg, w.n_seqs, w.n_seqs, run.cu, t["qkv"][s], t["b"][s], t["a"][s], t["conv_w"],
-                             t["dt_bias"], t["A_log"], conv, conv, run.q, run.k, run.v, run.beta, run.g)
+    def three_step(s, evs=None):
+        B.gdn_conv_gate_prep(cfg, N, N, three.cu, t["qkv"][s], t["b"][s], t["a"][s], t["conv_w"],
+                             t["dt_bias"], t["A_log"], conv, conv, three.q, three.k, three.v, three.beta, three.g)
         if evs is not None:
             evs[0].record()
-        B.gdn_decode_step(cfg, w.n_seqs, run.q, run.k, run.v, run.beta, run.g, S, S, run.o)
+        B.gdn_decode_step(cfg, N, three.q, three.k, three.v, three.beta, three.g, S, S, three.o)
         if evs is not None:
             evs[1].record()
-        B.gdn_gated_rmsnorm(cfg, w.n_seqs * w.n_v_heads, run.o, t["z"][s], t["norm_w"], ys[s])
+        B.gdn_gated_rmsnorm(cfg, N * w.n_v_heads, three.o, t["z"][s], t["norm_w"], ys[s])
+
+    def fused_step(s, evs=None):
+        fused(t["qkv"][s], t["z"][s], t["b"][s], t["a"][s], t["conv_w"], t["dt_bias"], t["A_log"], t["norm_w"],
+              S, ys[s])
+
+    def reset():
+        S.copy_(t["S0"])
+        conv.copy_(t["conv0"])
+        fused.bufs[0].copy_(t["conv0"])
+        fused.cur = 0
+        torch.cuda.synchronize()
+
+    def timed(fn):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        fn()
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end)
 
     for s in range(min(warmup_steps, steps)):
-        one(s)
-    conv.copy_(t["conv0"])
-    S.copy_(t["S0"])
+        three_step(s)
+        fused_step(s)
+    modes = {}
+    # Plain launches; the three-call loop also times each gdn_decode_step launch.
+    reset()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for s in range(steps):
-        one(s, evs[s])
-    end.record()
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
+    ms = timed(lambda: [three_step(s, evs[s]) for s in range(steps)])
     k_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-    nbytes = decode_kernel_bytes(w)
-    gbs = nbytes / (k_ms * 1e-3) / 1e9
-    return {"workload": w.name, "tokens_per_s": round(w.n_seqs * steps / (total_ms * 1e-3), 1),
-            "us_per_step": round(total_ms * 1e3 / steps, 2),
+    modes["three_call"] = ms
+    reset()
+    modes["fused"] = timed(lambda: [fused_step(s) for s in range(steps)])
+    # The whole loop captured as one graph, replayed once untimed, then timed.
+    for name, fn in (("three_call_graph", three_step), ("fused_graph", fused_step)):
+        reset()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for s in range(steps):
+                fn(s)
+        reset()
+        g.replay()
+        reset()
+        modes[name] = timed(g.replay)
+        del g
+    best = min(modes, key=modes.get)
+    per = {k: {"us_per_step": round(v * 1e3 / steps, 2), "tokens_per_s": round(N * steps / (v * 1e-3), 1)}
+           for k, v in modes.items()}
+    step_bytes = decode_step_bytes(w)
+    f_us = modes["fused_graph"] * 1e3 / steps
+    gbs = step_bytes / (f_us * 1e-6) / 1e9
+    kb = decode_kernel_bytes(w)
+    kgbs = kb / (k_ms * 1e-3) / 1e9
+    return {"workload": w.name, "best": best, "tokens_per_s": per[best]["tokens_per_s"],
+            "us_per_step": per[best]["us_per_step"], "modes": per,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4),
-                         "traffic": measured_traffic("decode_b64" if w.n_seqs > 1 else "decode_b1"),
-                         "kernel": "gdn_decode_step",
-                         "bytes_per_launch": nbytes, "avg_launch_us": round(k_ms * 1e3, 2)}}
+                         "traffic": measured_traffic("decode_fused_b64" if N > 1 else "decode_fused_b1"),
+                         "kernel": "gdn_decode_fused (graph replay; launch duration = loop time / steps)",
+                         "bytes_per_launch": step_bytes, "avg_launch_us": round(f_us, 2)},
+            "roofline_decode_step": {"bound": "hbm", "achieved": round(kgbs, 1), "peak": HBM_PEAK_GBS,
+                                     "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4),
+                                     "traffic": measured_traffic("decode_b64" if N > 1 else "decode_b1"),
+                                     "kernel": "gdn_decode_step (plain launches, HIP events around each)",
+                                     "bytes_per_launch": kb, "avg_launch_us": round(k_ms * 1e3, 2)}}
 
 
 def cpu_baseline():

@@ -28,8 +28,8 @@ CONV_K = 4
 
 # Every entry point include/gdn.h declares.
 EXPORTS = ("gdn_default_config", "gdn_conv_gate_prep", "gdn_prefill_chunked",
-           "gdn_prefill_workspace_bytes", "gdn_decode_step", "gdn_gated_rmsnorm",
-           "gdn_status_string", "gdn_version")
+           "gdn_prefill_workspace_bytes", "gdn_decode_step", "gdn_decode_fused",
+           "gdn_gated_rmsnorm", "gdn_status_string", "gdn_version")
 
 
 class GdnError(RuntimeError):
@@ -73,6 +73,8 @@ def load(path: Optional[str] = None):
     lib.gdn_prefill_workspace_bytes.restype = ctypes.c_size_t
     lib.gdn_decode_step.argtypes = [cfgp, ctypes.c_int32] + [_P] * 8 + [_P]
     lib.gdn_decode_step.restype = ctypes.c_int
+    lib.gdn_decode_fused.argtypes = [cfgp, ctypes.c_int32] + [_P] * 13 + [_P]
+    lib.gdn_decode_fused.restype = ctypes.c_int
     lib.gdn_gated_rmsnorm.argtypes = [cfgp, ctypes.c_int64, _P, _P, _P, _P, _P]
     lib.gdn_gated_rmsnorm.restype = ctypes.c_int
     if path is None:
@@ -173,6 +175,22 @@ def gdn_decode_step(cfg: gdn_config, n_seqs: int, q, k, v, beta, g, S_in, S_out,
     _check("gdn_decode_step", s)
 
 
+def gdn_decode_fused(cfg: gdn_config, n_seqs: int, qkv, beta_logit, alpha_logit, z, conv_w, dt_bias,
+                     A_log, norm_w, conv_state_in, conv_state_out, S_in, S_out, y, stream=None):
+    Hqk, Hv, d, N = cfg.n_qk_heads, cfg.n_v_heads, cfg.head_dim, n_seqs
+    C, ad = d * (2 * Hqk + Hv), _act_dtype(cfg)
+    s = load().gdn_decode_fused(
+        ctypes.byref(cfg), N, _ptr(qkv, "qkv", ad, N * C), _ptr(beta_logit, "beta_logit", ad, N * Hv),
+        _ptr(alpha_logit, "alpha_logit", ad, N * Hv), _ptr(z, "z", ad, N * Hv * d),
+        _ptr(conv_w, "conv_w", torch.float32, C * CONV_K), _ptr(dt_bias, "dt_bias", torch.float32, Hv),
+        _ptr(A_log, "A_log", torch.float32, Hv), _ptr(norm_w, "norm_w", torch.float32, d),
+        _ptr(conv_state_in, "conv_state_in", ad, N * (CONV_K - 1) * C),
+        _ptr(conv_state_out, "conv_state_out", ad, N * (CONV_K - 1) * C),
+        _ptr(S_in, "S_in", torch.float32, N * Hv * d * d), _ptr(S_out, "S_out", torch.float32, N * Hv * d * d),
+        _ptr(y, "y", ad, N * Hv * d), _stream(stream))
+    _check("gdn_decode_fused", s)
+
+
 def gdn_gated_rmsnorm(cfg: gdn_config, n_rows: int, o, z, norm_w, y, stream=None):
     d, ad = cfg.head_dim, _act_dtype(cfg)
     s = load().gdn_gated_rmsnorm(
@@ -183,4 +201,4 @@ def gdn_gated_rmsnorm(cfg: gdn_config, n_rows: int, o, z, norm_w, y, stream=None
 
 __all__ = ["load", "make_config", "gdn_config", "GdnError", "status_string", "EXPORTS",
            "gdn_conv_gate_prep", "gdn_prefill_chunked", "gdn_prefill_workspace_bytes",
-           "gdn_decode_step", "gdn_gated_rmsnorm", "GDN_F32", "GDN_BF16"]
+           "gdn_decode_step", "gdn_decode_fused", "gdn_gated_rmsnorm", "GDN_F32", "GDN_BF16"]

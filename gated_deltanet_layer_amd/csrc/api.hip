@@ -227,6 +227,55 @@ gdn_status gdn_decode_step(const gdn_config *cfg, int32_t n_seqs, const float *q
   return launched(gdn::launch_decode(p, cfg->act_dtype, static_cast<hipStream_t>(stream)));
 }
 
+gdn_status gdn_decode_fused(const gdn_config *cfg, int32_t n_seqs, const void *qkv, const void *beta_logit,
+                            const void *alpha_logit, const void *z, const float *conv_w, const float *dt_bias,
+                            const float *A_log, const float *norm_w, const void *conv_state_in,
+                            void *conv_state_out, const float *S_in, float *S_out, void *y,
+                            gdn_stream_t stream) {
+  const gdn_status cs = check_config(cfg);
+  if (cs != GDN_OK) return cs;
+  if (n_seqs < 0) return GDN_E_INVALID_ARG;
+  if (n_seqs == 0) return GDN_OK;
+  if (!qkv || !beta_logit || !alpha_logit || !z || !conv_w || !dt_bias || !A_log || !norm_w ||
+      !conv_state_in || !conv_state_out || !S_in || !S_out || !y)
+    return GDN_E_INVALID_ARG;
+  const int Hqk = cfg->n_qk_heads, Hv = cfg->n_v_heads;
+  if (static_cast<int64_t>(n_seqs) * Hv > kMaxGrid) return GDN_E_UNSUPPORTED;
+  const size_t N = static_cast<size_t>(n_seqs), as = act_size(cfg);
+  const size_t C = static_cast<size_t>(kHeadDim) * (2 * Hqk + Hv);
+  const size_t sb = N * Hv * kHeadDim * kHeadDim * 4;
+  const size_t st = N * (gdn::kConvK - 1) * C * as;
+  const Range outs[] = {{y, N * Hv * kHeadDim * as}, {conv_state_out, st}};
+  const Range ins[] = {{qkv, N * C * as}, {beta_logit, N * Hv * as}, {alpha_logit, N * Hv * as},
+                       {z, N * Hv * kHeadDim * as}, {conv_w, C * 4 * 4}, {dt_bias, Hv * 4u},
+                       {A_log, Hv * 4u}, {norm_w, kHeadDim * 4u}, {conv_state_in, st}, {S_in, sb}, {S_out, sb}};
+  if (any_overlap(outs, ins)) return GDN_E_INVALID_ARG;
+  if (S_in != S_out && overlap(S_in, sb, S_out, sb)) return GDN_E_INVALID_ARG;
+  for (size_t i = 0; i < 9; ++i)
+    if (overlap(ins[i].p, ins[i].n, S_out, sb)) return GDN_E_INVALID_ARG;
+
+  gdn::FusedDecodeParams p;
+  p.n_seqs = n_seqs;
+  p.n_qk = Hqk;
+  p.n_v = Hv;
+  p.qkv = qkv;
+  p.b = beta_logit;
+  p.a = alpha_logit;
+  p.z = z;
+  p.conv_w = conv_w;
+  p.dt_bias = dt_bias;
+  p.A_log = A_log;
+  p.norm_w = norm_w;
+  p.st_in = conv_state_in;
+  p.st_out = conv_state_out;
+  p.S_in = S_in;
+  p.S_out = S_out;
+  p.y = y;
+  p.l2_eps = cfg->l2_eps;
+  p.norm_eps = cfg->norm_eps;
+  return launched(gdn::launch_decode_fused(p, cfg->act_dtype, static_cast<hipStream_t>(stream)));
+}
+
 gdn_status gdn_gated_rmsnorm(const gdn_config *cfg, int64_t n_rows, const void *o, const void *z,
                              const float *norm_w, void *y, gdn_stream_t stream) {
   const gdn_status cs = check_config(cfg);

@@ -1,0 +1,204 @@
+// decode_fused.hip -- one decode step of the whole token mixer in one launch:
+// conv + SiLU + split + L2 norm + gates for the step's token, the recurrent
+// delta-rule update of the 128x128 state, and the gated RMSNorm of the
+// readout.
+//
+// Method: the xwen CLAUDE.md page, section "Architecture cheat sheet", gated
+// DeltaNet paragraph: causal depthwise conv (kernel 4, no bias) over the
+// fused stream, SiLU over all of it, q | k | v split, x / max(||x||, eps),
+// K-head j mod Hqk for V-head j (tiled repeat), beta = sigmoid(b),
+// g = -exp(A_log) softplus(a + dt_bias) (section "GGUF facts that differ
+// from the HF checkpoint" for -exp(A_log) and the multiply-ready norm
+// weight), then the recurrent step (decay, read S.k, delta, rank-1 update,
+// readout of the updated state over sqrt(128)) and the gated RMSNorm
+// (norm, times the weight, times silu(z)).
+//
+// A block owns one (sequence, V-head): it streams the head's 64 KiB state in
+// and out once, so the normalisation of the 128 readout values needs no
+// other block. The state loads are issued first; while they are in flight,
+// waves 0..2 compute q, k (of K-head j mod Hqk) and v of the token, each
+// lane two adjacent channels, and one lane the two gates. The state step
+// uses
+//   u = e^g (S^T k),  d = beta (v - u),  o = (e^g (S^T q) + (k.q) d) / sqrt(128),
+//   S' = e^g S + k d^T.
+// Thread t holds rows 8 (t / 32) .. +7 and columns 4 (t % 32) .. +3 (32
+// floats): each row is read and written as 512 contiguous bytes by 32 lanes.
+//
+// The new conv state of the V-head's channels is written by its block, that
+// of the q and k channels of K-head h by the block of V-head h; other blocks
+// read those channels of the old state during the step, so the old and new
+// conv states must be different buffers.
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kFusedThreads = 512;
+constexpr int kFusedWaves = kFusedThreads / kWave;
+constexpr int kRowsPerThread = 8;
+constexpr int kColQuads = kHeadDim / 4;   // 32 lanes span a row
+
+template <typename TA>
+__global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedDecodeParams p) {
+  __shared__ __attribute__((aligned(16))) float qs[kHeadDim];
+  __shared__ __attribute__((aligned(16))) float ks[kHeadDim];
+  __shared__ __attribute__((aligned(16))) float vs[kHeadDim];
+  __shared__ float gate[2];
+  __shared__ float red[kFusedWaves][9][kColQuads];
+  __shared__ float tot[9][kColQuads];
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = lane_id();
+  const int j = blockIdx.x % p.n_v;
+  const int n = blockIdx.x / p.n_v;
+  const int hk = j % p.n_qk;
+  const int cq = tid % kColQuads;
+  const int row0 = kRowsPerThread * (tid / kColQuads);
+  const int col0 = 4 * cq;
+
+  // 1. The state rows of this thread (in flight during the token's prep).
+  const size_t sbase = (static_cast<size_t>(n) * p.n_v + j) * kHeadDim * kHeadDim;
+  float4 S[kRowsPerThread];
+#pragma unroll
+  for (int r = 0; r < kRowsPerThread; ++r)
+    S[r] = *reinterpret_cast<const float4 *>(p.S_in + sbase + (row0 + r) * kHeadDim + col0);
+
+  const size_t e = static_cast<size_t>(n) * p.n_v + j;
+  float4 zv = make_float4(0.f, 0.f, 0.f, 0.f), wv = zv;
+  if (wave == 0) {
+    zv = Act<TA>::load4(static_cast<const TA *>(p.z), e * kHeadDim + col0);
+    wv = *reinterpret_cast<const float4 *>(p.norm_w + col0);
+  }
+
+  // 2. The token's q (wave 0), k (wave 1), v (wave 2); gates (wave 3).
+  const int C = kHeadDim * (2 * p.n_qk + p.n_v);
+  if (wave < 3) {
+    const int hb = wave == 0 ? hk : (wave == 1 ? p.n_qk + hk : 2 * p.n_qk + j);
+    const int c = hb * kHeadDim + 2 * lane;
+    const TA *st = static_cast<const TA *>(p.st_in) + static_cast<size_t>(n) * (kConvK - 1) * C;
+    const TA *x = static_cast<const TA *>(p.qkv) + static_cast<size_t>(n) * C;
+    const float2 x0 = Act<TA>::load2(st, c);
+    const float2 x1 = Act<TA>::load2(st, c + C);
+    const float2 x2 = Act<TA>::load2(st, c + 2 * C);
+    const float2 x3 = Act<TA>::load2(x, c);
+    const float4 w0 = reinterpret_cast<const float4 *>(p.conv_w)[c];
+    const float4 w1 = reinterpret_cast<const float4 *>(p.conv_w)[c + 1];
+    float y0 = w0.x * x0.x + w0.y * x1.x + w0.z * x2.x + w0.w * x3.x;
+    float y1 = w1.x * x0.y + w1.y * x1.y + w1.z * x2.y + w1.w * x3.y;
+    y0 = siluf_(y0);
+    y1 = siluf_(y1);
+    if (wave < 2) {
+      const float ss = wave_sum(y0 * y0 + y1 * y1);
+      const float inv = 1.0f / fmaxf(sqrtf(ss), p.l2_eps);
+      y0 *= inv;
+      y1 *= inv;
+    }
+    float *dst = wave == 0 ? qs : (wave == 1 ? ks : vs);
+    *reinterpret_cast<float2 *>(dst + 2 * lane) = make_float2(y0, y1);
+    // New conv state: old rows 1, 2 and the token.
+    if (wave == 2 || j == hk) {
+      TA *so = static_cast<TA *>(p.st_out) + static_cast<size_t>(n) * (kConvK - 1) * C;
+      Act<TA>::store2(so, c, x1);
+      Act<TA>::store2(so, c + C, x2);
+      Act<TA>::store2(so, c + 2 * C, x3);
+    }
+  } else if (tid == 3 * kWave) {
+    gate[0] = sigmoidf_(Act<TA>::load(static_cast<const TA *>(p.b), e));
+    gate[1] = -expf(p.A_log[j]) * softplusf_(Act<TA>::load(static_cast<const TA *>(p.a), e) + p.dt_bias[j]);
+  }
+  __syncthreads();
+
+  // 3. Column sums S^T k, S^T q over this thread's rows, and k.q.
+  float kr[kRowsPerThread], qr[kRowsPerThread];
+#pragma unroll
+  for (int h = 0; h < kRowsPerThread / 4; ++h) {
+    const float4 k4 = *reinterpret_cast<const float4 *>(ks + row0 + 4 * h);
+    const float4 q4 = *reinterpret_cast<const float4 *>(qs + row0 + 4 * h);
+    kr[4 * h] = k4.x; kr[4 * h + 1] = k4.y; kr[4 * h + 2] = k4.z; kr[4 * h + 3] = k4.w;
+    qr[4 * h] = q4.x; qr[4 * h + 1] = q4.y; qr[4 * h + 2] = q4.z; qr[4 * h + 3] = q4.w;
+  }
+  float part[9];
+#pragma unroll
+  for (int i = 0; i < 9; ++i) part[i] = 0.0f;
+#pragma unroll
+  for (int r = 0; r < kRowsPerThread; ++r) {
+    part[0] += S[r].x * kr[r]; part[1] += S[r].y * kr[r];
+    part[2] += S[r].z * kr[r]; part[3] += S[r].w * kr[r];
+    part[4] += S[r].x * qr[r]; part[5] += S[r].y * qr[r];
+    part[6] += S[r].z * qr[r]; part[7] += S[r].w * qr[r];
+    part[8] += kr[r] * qr[r];
+  }
+  // The two row groups of a wave (lanes l and l + 32 share columns), then
+  // the waves through LDS.
+#pragma unroll
+  for (int i = 0; i < 9; ++i) part[i] += __shfl_xor(part[i], 32, kWave);
+  if (lane < kColQuads) {
+#pragma unroll
+    for (int i = 0; i < 9; ++i) red[wave][i][cq] = part[i];
+  }
+  __syncthreads();
+  if (tid < 9 * kColQuads) {
+    const int i = tid / kColQuads, c = tid % kColQuads;
+    float s = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kFusedWaves; ++w) s += red[w][i][c];
+    tot[i][c] = s;
+  }
+  __syncthreads();
+
+  // 4. Delta, readout, state update.
+  const float bt = gate[0];
+  const float eg = expf(gate[1]);
+  const float kq = tot[8][cq];
+  const float4 v4 = *reinterpret_cast<const float4 *>(vs + col0);
+  const float vc[4] = {v4.x, v4.y, v4.z, v4.w};
+  const float scale = 0.08838834764831845f;  // 1/sqrt(128)
+  float d[4], o[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    d[c] = bt * (vc[c] - eg * tot[c][cq]);
+    o[c] = scale * (eg * tot[4 + c][cq] + kq * d[c]);
+  }
+  float *Sout = p.S_out + sbase;
+#pragma unroll
+  for (int r = 0; r < kRowsPerThread; ++r) {
+    float4 w;
+    w.x = eg * S[r].x + kr[r] * d[0];
+    w.y = eg * S[r].y + kr[r] * d[1];
+    w.z = eg * S[r].z + kr[r] * d[2];
+    w.w = eg * S[r].w + kr[r] * d[3];
+    *reinterpret_cast<float4 *>(Sout + (row0 + r) * kHeadDim + col0) = w;
+  }
+
+  // 5. Gated RMSNorm of the 128 readout values: each 32-lane half of wave 0
+  // holds all of them (4 per lane).
+  if (wave == 0) {
+    float ss = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
+    ss = row16_sum(ss);
+    ss += __shfl_xor(ss, 16, kWave);
+    const float inv = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + p.norm_eps);
+    if (lane < kColQuads) {
+      float4 y;
+      y.x = o[0] * inv * wv.x * siluf_(zv.x);
+      y.y = o[1] * inv * wv.y * siluf_(zv.y);
+      y.z = o[2] * inv * wv.z * siluf_(zv.z);
+      y.w = o[3] * inv * wv.w * siluf_(zv.w);
+      Act<TA>::store4(static_cast<TA *>(p.y), e * kHeadDim + col0, y);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_fused(const FusedDecodeParams &p, gdn_dtype act, hipStream_t s) {
+  const int64_t blocks = static_cast<int64_t>(p.n_seqs) * p.n_v;
+  if (act == GDN_BF16)
+    hipLaunchKernelGGL(decode_fused_kernel<bf16_t>, dim3(static_cast<unsigned>(blocks)), dim3(kFusedThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL(decode_fused_kernel<float>, dim3(static_cast<unsigned>(blocks)), dim3(kFusedThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -38,6 +38,9 @@ template <> struct Act<float> {
   static __device__ __forceinline__ void store4(float *p, size_t i, float4 x) {
     *reinterpret_cast<float4 *>(p + i) = x;
   }
+  static __device__ __forceinline__ float4 load4(const float *p, size_t i) {
+    return *reinterpret_cast<const float4 *>(p + i);
+  }
 };
 template <> struct Act<bf16_t> {
   static __device__ __forceinline__ float load(const bf16_t *p, size_t i) { return bf16_to_f32(p[i].bits); }
@@ -55,6 +58,11 @@ template <> struct Act<bf16_t> {
     w.x = static_cast<uint32_t>(f32_to_bf16(x.x)) | (static_cast<uint32_t>(f32_to_bf16(x.y)) << 16);
     w.y = static_cast<uint32_t>(f32_to_bf16(x.z)) | (static_cast<uint32_t>(f32_to_bf16(x.w)) << 16);
     *reinterpret_cast<uint2 *>(p + i) = w;
+  }
+  static __device__ __forceinline__ float4 load4(const bf16_t *p, size_t i) {
+    const uint2 w = *reinterpret_cast<const uint2 *>(p + i);
+    return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                       __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
   }
 };
 

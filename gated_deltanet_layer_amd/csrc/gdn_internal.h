@@ -40,6 +40,19 @@ struct DecodeParams {
 };
 hipError_t launch_decode(const DecodeParams &p, gdn_dtype act, hipStream_t s);
 
+struct FusedDecodeParams {
+  int n_seqs, n_qk, n_v;
+  const void *qkv, *b, *a, *z;
+  const float *conv_w, *dt_bias, *A_log, *norm_w;
+  const void *st_in;
+  void *st_out;
+  const float *S_in;
+  float *S_out;
+  void *y;
+  float l2_eps, norm_eps;
+};
+hipError_t launch_decode_fused(const FusedDecodeParams &p, gdn_dtype act, hipStream_t s);
+
 struct NormParams {
   int64_t n_rows;
   const void *o, *z;

@@ -2,9 +2,10 @@
 
 ``Prefill`` runs gdn_conv_gate_prep -> gdn_prefill_chunked -> gdn_gated_rmsnorm
 over packed sequences; ``Decode`` runs gdn_conv_gate_prep -> gdn_decode_step ->
-gdn_gated_rmsnorm for one token per sequence. Both allocate their
-intermediates (q, k, v, beta, g, o, y, workspace) once with torch and then only
-call the library, so a timed loop allocates nothing.
+gdn_gated_rmsnorm for one token per sequence; ``DecodeFused`` runs the same
+step as the single launch gdn_decode_fused. Each allocates its intermediates
+(q, k, v, beta, g, o, y, workspace, the second conv-state buffer) once with
+torch and then only calls the library, so a timed loop allocates nothing.
 """
 from __future__ import annotations
 
@@ -72,4 +73,29 @@ class Decode:
                              self.q, self.k, self.v, self.beta, self.g, stream)
         B.gdn_decode_step(cfg, N, self.q, self.k, self.v, self.beta, self.g, S, S, self.o, stream)
         B.gdn_gated_rmsnorm(cfg, N * cfg.n_v_heads, self.o, z, norm_w, y, stream)
+        return y
+
+
+class DecodeFused:
+    """One token for each of n_seqs sequences per call, in one launch.
+
+    gdn_decode_fused needs distinct old and new conv-state buffers, so the
+    runner alternates between ``conv_state`` (given, used as the first
+    buffer and overwritten) and a second buffer of its own;
+    ``self.conv_state`` is the current one. S is updated in place."""
+
+    def __init__(self, cfg: B.gdn_config, n_seqs: int, conv_state: torch.Tensor):
+        self.cfg, self.N = cfg, n_seqs
+        self.bufs = [conv_state, torch.empty_like(conv_state)]
+        self.cur = 0
+
+    @property
+    def conv_state(self) -> torch.Tensor:
+        return self.bufs[self.cur]
+
+    def __call__(self, qkv, z, b, a, conv_w, dt_bias, A_log, norm_w, S, y, stream=None):
+        src, dst = self.bufs[self.cur], self.bufs[1 - self.cur]
+        B.gdn_decode_fused(self.cfg, self.N, qkv, b, a, z, conv_w, dt_bias, A_log, norm_w, src, dst, S, S, y,
+                           stream)
+        self.cur = 1 - self.cur
         return y

@@ -152,6 +152,28 @@ GDN_API gdn_status gdn_decode_step(const gdn_config *cfg, int32_t n_seqs,
                            const float *S_in, float *S_out, void *o, gdn_stream_t stream);
 
 /*
+ * gdn_decode_fused -- one decode step of the whole mixer in a single launch,
+ * for n_seqs sequences of one token each: the work of gdn_conv_gate_prep
+ * (with cu_seqlens = 0, 1, .., n_seqs), gdn_decode_step and
+ * gdn_gated_rmsnorm, without storing q, k, v, beta, g or o. Same arithmetic
+ * as those three calls (the page's section "Architecture cheat sheet", gated
+ * DeltaNet paragraph), except that the readout o reaches the norm in fp32
+ * rather than rounded to the act dtype.
+ *   qkv [N][C], beta_logit, alpha_logit [N][Hv], z, y [N][Hv][d]: act dtype
+ *   conv_w [C][4], dt_bias [Hv], A_log [Hv], norm_w [d]: fp32
+ *   conv_state_in, conv_state_out [N][3][C]: act dtype; they must NOT overlap
+ *     (blocks of the step read channels of the old state that other blocks
+ *     write), so a caller alternates two buffers.
+ *   S_in, S_out [N][Hv][d][d]: fp32; S_out may equal S_in.
+ * n_seqs may be 0.
+ */
+GDN_API gdn_status gdn_decode_fused(const gdn_config *cfg, int32_t n_seqs, const void *qkv,
+                            const void *beta_logit, const void *alpha_logit, const void *z,
+                            const float *conv_w, const float *dt_bias, const float *A_log,
+                            const float *norm_w, const void *conv_state_in, void *conv_state_out,
+                            const float *S_in, float *S_out, void *y, gdn_stream_t stream);
+
+/*
  * gdn_gated_rmsnorm -- per row of d values (n_rows = T * Hv):
  *   y = o / sqrt(mean(o^2) + norm_eps) * norm_w * silu(z)
  * with norm_w [d] fp32 shared by all heads and used as stored (no +1).

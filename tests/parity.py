@@ -123,6 +123,23 @@ def gpu_decode(w: wl.Workload, x: dict):
     return dict(y=host(ys), o=host(os_), S_out=host(S), conv_out_bits=bits(conv), conv_out=conv)
 
 
+def gpu_decode_fused(w: wl.Workload, x: dict):
+    """Run the decode loop as one gdn_decode_fused launch per step on the GPU.
+    Returns y [steps, N, Hv, d], final S and conv state."""
+    cfg = B.make_config(w.n_qk_heads, w.n_v_heads, w.act)
+    steps, N = x["qkv"].shape[:2]
+    t = {k: dev(v) for k, v in x.items()}
+    run = Lyr.DecodeFused(cfg, N, t["conv0"].clone())
+    S = t["S0"].clone()
+    ys = torch.empty_like(t["z"])
+    for s in range(steps):
+        run(t["qkv"][s], t["z"][s], t["b"][s], t["a"][s], t["conv_w"], t["dt_bias"], t["A_log"], t["norm_w"],
+            S, ys[s])
+    torch.cuda.synchronize()
+    conv = run.conv_state
+    return dict(y=host(ys), S_out=host(S), conv_out_bits=bits(conv), conv_out=conv)
+
+
 def decode_as_packed(x: dict, seqs=None) -> dict:
     """Decode streams [steps, N, ...] -> packed prefill layout (sequence-major)."""
     steps, N = x["qkv"].shape[:2]

@@ -130,3 +130,28 @@ def test_prep_and_norm_validation(lib):
     yz = FAKE[:4]
     yz = [yz[0], yz[1], yz[2], yz[1] + 8]   # y overlapping z
     assert lib.gdn_gated_rmsnorm(ctypes.byref(cfg), 4, *yz, None) == B.GDN_E_INVALID_ARG
+
+
+def test_decode_fused_validation(lib):
+    cfg = B.make_config(2, 4)
+    p = FAKE[:13]   # qkv, b, a, z, conv_w, dt_bias, A_log, norm_w, conv_in, conv_out, S_in, S_out, y
+    call = lambda n, ptrs, c=cfg: lib.gdn_decode_fused(ctypes.byref(c), n, *ptrs, None)
+    assert call(0, p) == B.GDN_OK
+    assert call(-1, p) == B.GDN_E_INVALID_ARG
+    for i in range(13):
+        q = p[:]
+        q[i] = None
+        assert call(1, q) == B.GDN_E_INVALID_ARG, i
+    # The new conv state may not be the old one (other blocks still read it).
+    q = p[:]
+    q[9] = q[8]
+    assert call(1, q) == B.GDN_E_INVALID_ARG
+    # y overlapping z, S_out partly overlapping S_in: rejected.
+    q = p[:]
+    q[12] = q[3] + 8
+    assert call(1, q) == B.GDN_E_INVALID_ARG
+    q = p[:]
+    q[11] = q[10] + 4096
+    assert call(1, q) == B.GDN_E_INVALID_ARG
+    assert call(1, p, B.make_config(2, 4, head_dim=64)) == B.GDN_E_UNSUPPORTED
+    assert lib.gdn_decode_fused(None, 1, *p, None) == B.GDN_E_INVALID_ARG
