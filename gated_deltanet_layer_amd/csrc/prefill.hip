@@ -53,10 +53,8 @@ constexpr int kXcds = 8;                  // accelerator complex dies on MI355X
 // Row pitches (bytes) of blocked operands in LDS: 128 or 64 contraction
 // indices (16 or 8 blocks of 32 bytes) plus 16 bytes to spread LDS banks.
 constexpr int kPitch128 = (kHeadDim / 8) * kBlk + 16;   // 528
-constexpr int kPitch64 = (kChunk / 8) * kBlk + 16;      // 272
 constexpr int kLdS = kChunk + 1;          // fp32 pitch of the solve's scalar matrices
 constexpr int kLdV = kSlab + 4;           // fp32 pitch of the V slab in LDS
-constexpr int kLdO = kSlab;               // fp32 pitch of the O staging rows (4 waves x 16 rows fit the R^T buffer)
 
 // Workspace, all operands in the fragment-major layout:
 //   per (chunk, K-head): K rows (64 x 128, 4 x 4 blocks), Q rows (same) and
@@ -336,6 +334,50 @@ __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(PrefillParam
 }
 
 // ---------------------------------------------------------------------------
+// Right operands of chunk_state live in LDS in the fragment-major layout of
+// the MFMA B operand: one 2 KB block per 32 x 16 (k x column) tile, lane l's
+// 16 bytes at l * 16 of each 1 KB plane (BF16X3: plane 0 = hi, plane 1 =
+// lo; F32: plane 0 = indices 0..3 of the lane's 8, plane 1 = indices 4..7).
+// A wave reads a fragment as two linear 1 KB reads, free of LDS bank
+// conflicts (gfx950 LDS: 64 banks of 4 bytes).
+constexpr int kLdsBlk = 2048;
+constexpr int kLdOs = kSlab + 4;         // fp32 pitch of the O staging rows
+
+template <Prec P> __device__ __forceinline__ typename Op<P>::Frag lds_frag(const uint8_t *buf, int blk);
+template <> __device__ __forceinline__ Op<Prec::F32>::Frag lds_frag<Prec::F32>(const uint8_t *buf, int blk) {
+  const uint8_t *b = buf + blk * kLdsBlk + lane_id() * 16;
+  Op<Prec::F32>::Frag f;
+  f.a = *reinterpret_cast<const f32x4 *>(b);
+  f.b = *reinterpret_cast<const f32x4 *>(b + kLdsBlk / 2);
+  return f;
+}
+template <> __device__ __forceinline__ Op<Prec::BF16X3>::Frag lds_frag<Prec::BF16X3>(const uint8_t *buf, int blk) {
+  const uint8_t *b = buf + blk * kLdsBlk + lane_id() * 16;
+  Op<Prec::BF16X3>::Frag f;
+  f.hi = *reinterpret_cast<const bf16x8 *>(b);
+  f.lo = *reinterpret_cast<const bf16x8 *>(b + kLdsBlk / 2);
+  return f;
+}
+
+// Store contraction indices k0 .. k0+3 (k0 % 4 == 0) of column c of a right
+// operand with KS contraction steps of 32 (one accumulator's four values).
+template <Prec P> __device__ __forceinline__ void lds_put4(uint8_t *buf, int KS, int k0, int c, f32x4 x);
+template <> __device__ __forceinline__ void lds_put4<Prec::F32>(uint8_t *buf, int KS, int k0, int c, f32x4 x) {
+  const int blk = (c >> 4) * KS + (k0 >> 5);
+  const int ln = 16 * ((k0 & 31) >> 3) + (c & 15);
+  *reinterpret_cast<f32x4 *>(buf + blk * kLdsBlk + ((k0 & 4) ? kLdsBlk / 2 : 0) + ln * 16) = x;
+}
+template <> __device__ __forceinline__ void lds_put4<Prec::BF16X3>(uint8_t *buf, int KS, int k0, int c, f32x4 x) {
+  const int blk = (c >> 4) * KS + (k0 >> 5);
+  const int ln = 16 * ((k0 & 31) >> 3) + (c & 15);
+  bf16x4 hi, lo;
+  split4(x, hi, lo);
+  uint8_t *b = buf + blk * kLdsBlk + ln * 16 + (k0 & 7) * 2;
+  *reinterpret_cast<bf16x4 *>(b) = hi;
+  *reinterpret_cast<bf16x4 *>(b + kLdsBlk / 2) = lo;
+}
+
+// ---------------------------------------------------------------------------
 // chunk_state: per (sequence, V-head, 32-column slab). 8 waves; wave w has
 // rt = w % 4. Per chunk:
 //   X/Y : waves 0-3 X = K S, waves 4-7 Y = Q S (rows 16 rt, both column tiles)
@@ -350,11 +392,12 @@ __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(PrefillParam
 template <Prec P, typename TA>
 __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParams p, int64_t max_chunks) {
   using Frag = typename Op<P>::Frag;
-  __shared__ __attribute__((aligned(16))) uint8_t Stb[kSlab * kPitch128];    // S^T rows c, blocked over i
-  __shared__ __attribute__((aligned(16))) uint8_t Rtb[kSlab * kPitch64];     // R^T rows c, blocked over r
-  __shared__ __attribute__((aligned(16))) uint8_t Dtb[kSlab * kPitch64];     // D^T
-  __shared__ __attribute__((aligned(16))) uint8_t Dsb[kSlab * kPitch64];     // (diag(k~) D)^T
-  __shared__ __attribute__((aligned(16))) float Vs[kChunk * kLdV];           // V rows of the slab (fp32)
+  __shared__ __attribute__((aligned(16))) uint8_t Stb[8 * kLdsBlk];    // S: B of K S, Q S (2 col x 4 k tiles)
+  __shared__ __attribute__((aligned(16))) uint8_t Rtb[4 * kLdsBlk];    // R: B of Tm R (2 x 2)
+  __shared__ __attribute__((aligned(16))) uint8_t Dtb[4 * kLdsBlk];    // D: B of P D
+  __shared__ __attribute__((aligned(16))) uint8_t Dsb[4 * kLdsBlk];    // diag(k~) D: B of K^T (.)
+  __shared__ __attribute__((aligned(16))) float Vs[kChunk * kLdV];    // V rows of the slab (fp32)
+  __shared__ __attribute__((aligned(16))) float Os[4 * 16 * kLdOs];   // O staging, 16 rows per y-wave
   __shared__ float G_s[kChunk];            // exp(gam_r)
   __shared__ float ksc_s[kChunk];          // exp(gam_n - gam_r)
 
@@ -363,6 +406,8 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
   const int lane = lane_id();
   const int rt = wave & 3;
   const bool x_wave = wave < 4;
+  const int lr = 4 * (lane >> 4);    // accumulator row offset of this lane
+  const int lc = lane & 15;          // accumulator column of this lane
   // Block order: workgroups are dealt to the 8 XCDs round-robin (block b on
   // XCD b % 8), each with its own L2. Blocks b = 32 g + 8 s + x hold slab s
   // of (sequence, V-head) pair 8 g + x, so the 4 slabs of a pair, and the
@@ -399,7 +444,7 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
     for (int r = 0; r < 4; ++r)
       S[ct][r] = p.S_in[sbase + static_cast<size_t>(16 * wave + acc_row(r)) * kHeadDim + col_base + 16 * ct + acc_col()];
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) put_acc_t<P>(Stb, kPitch128, 16 * wave, 16 * ct, S[ct]);
+  for (int ct = 0; ct < 2; ++ct) lds_put4<P>(Stb, 4, 16 * wave + lr, 16 * ct + lc, S[ct]);
 
   // Operand sources of chunk c (fragment-major blocks).
   const size_t qk_step = static_cast<size_t>(p.n_qk) * kQkBytes;
@@ -418,9 +463,11 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
 #define GDN_LOAD_XY(c)                                                                               \
   _Pragma("unroll") for (int ks = 0; ks < kHeadDim / 32; ++ks)                                       \
     fxy[ks] = FragIO<P>::load(xy_src0 + (c) * qk_step, kHeadDim / 32, rt, ks)
+  // Row tiles 0 and 1 of Tm and P end before column 32: their second k
+  // step is zero and skipped.
 #define GDN_LOAD_D(c)                                                                                \
   _Pragma("unroll") for (int ks = 0; ks < kChunk / 32; ++ks)                                         \
-    fd[ks] = FragIO<P>::load(d_src0 + (c) * v_step, kChunk / 32, rt, ks)
+    if (ks == 0 || rt >= 2) fd[ks] = FragIO<P>::load(d_src0 + (c) * v_step, kChunk / 32, rt, ks)
 #define GDN_LOAD_KT(c)                                                                               \
   _Pragma("unroll") for (int ks = 0; ks < kChunk / 32; ++ks)                                         \
     fk[ks] = FragIO<P>::load(kt_src0 + (c) * qk_step, kChunk / 32, wave, ks)
@@ -471,7 +518,7 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
     f32x4 XY[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int ks = 0; ks < kHeadDim / 32; ++ks)
-      Op<P>::mma2(XY[0], XY[1], fxy[ks], frag<P>(Stb, kPitch128, 0, 32 * ks), frag<P>(Stb, kPitch128, 16, 32 * ks));
+      Op<P>::mma2(XY[0], XY[1], fxy[ks], lds_frag<P>(Stb, ks), lds_frag<P>(Stb, 4 + ks));
     GDN_LOAD_XY(cn);
     if (x_wave) {
 #pragma unroll
@@ -482,7 +529,7 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
           const int row = 16 * rt + acc_row(r);
           rv[r] = Vs[row * kLdV + 16 * ct + acc_col()] - G_s[row] * XY[ct][r];
         }
-        put_acc_t<P>(Rtb, kPitch64, 16 * rt, 16 * ct, rv);
+        lds_put4<P>(Rtb, 2, 16 * rt + lr, 16 * ct + lc, rv);
       }
     }
     block_sync_lds();
@@ -491,15 +538,16 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
       f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int ks = 0; ks < kChunk / 32; ++ks)
-        Op<P>::mma2(acc[0], acc[1], fd[ks], frag<P>(Rtb, kPitch64, 0, 32 * ks), frag<P>(Rtb, kPitch64, 16, 32 * ks));
+        if (ks == 0 || rt >= 2)
+          Op<P>::mma2(acc[0], acc[1], fd[ks], lds_frag<P>(Rtb, ks), lds_frag<P>(Rtb, 2 + ks));
       GDN_LOAD_D(cn);
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        put_acc_t<P>(Dtb, kPitch64, 16 * rt, 16 * ct, acc[ct]);
+        lds_put4<P>(Dtb, 2, 16 * rt + lr, 16 * ct + lc, acc[ct]);
         f32x4 ds;
 #pragma unroll
         for (int r = 0; r < 4; ++r) ds[r] = acc[ct][r] * ksc_s[16 * rt + acc_row(r)];
-        put_acc_t<P>(Dsb, kPitch64, 16 * rt, 16 * ct, ds);
+        lds_put4<P>(Dsb, 2, 16 * rt + lr, 16 * ct + lc, ds);
       }
     }
     block_sync_lds();
@@ -508,22 +556,22 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
       f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int ks = 0; ks < kChunk / 32; ++ks)
-        Op<P>::mma2(acc[0], acc[1], fd[ks], frag<P>(Dtb, kPitch64, 0, 32 * ks), frag<P>(Dtb, kPitch64, 16, 32 * ks));
+        if (ks == 0 || rt >= 2)
+          Op<P>::mma2(acc[0], acc[1], fd[ks], lds_frag<P>(Dtb, ks), lds_frag<P>(Dtb, 2 + ks));
       GDN_LOAD_D(cn);
-      // Stage this wave's 16 x 32 rows of O in the (now dead) R^T buffer,
-      // then write them out with one 16-byte store per lane (bf16) or two (fp32).
-      static_assert(4 * 16 * kLdO * sizeof(float) <= sizeof(Rtb), "O staging must fit the R^T buffer");
-      float *Os = reinterpret_cast<float *>(Rtb) + rt * 16 * kLdO;
+      // Stage this wave's 16 x 32 rows of O in LDS, then write them out with
+      // one 16-byte store per lane (bf16) or two (fp32).
+      float *Ow = Os + rt * 16 * kLdOs;
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = 16 * rt + acc_row(r);
-          Os[acc_row(r) * kLdO + 16 * ct + acc_col()] = scale * (G_s[row] * XY[ct][r] + acc[ct][r]);
+          Ow[acc_row(r) * kLdOs + 16 * ct + acc_col()] = scale * (G_s[row] * XY[ct][r] + acc[ct][r]);
         }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave reads back only its own rows
       const int orow = lane >> 2, oc = 8 * (lane & 3);
-      const float *src = Os + orow * kLdO + oc;
+      const float *src = Ow + orow * kLdOs + oc;
       const f32x4 a = *reinterpret_cast<const f32x4 *>(src);
       const f32x4 b = *reinterpret_cast<const f32x4 *>(src + 4);
       if (16 * rt + orow < len) {
@@ -537,11 +585,11 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
     S[1] = S[1] * g_end;
 #pragma unroll
     for (int ks = 0; ks < kChunk / 32; ++ks)
-      Op<P>::mma2(S[0], S[1], fk[ks], frag<P>(Dsb, kPitch64, 0, 32 * ks), frag<P>(Dsb, kPitch64, 16, 32 * ks));
+      Op<P>::mma2(S[0], S[1], fk[ks], lds_frag<P>(Dsb, ks), lds_frag<P>(Dsb, 2 + ks));
     GDN_LOAD_KT(cn);
     block_sync_lds();                        // every LDS read of chunk ci is done
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) put_acc_t<P>(Stb, kPitch128, 16 * wave, 16 * ct, S[ct]);
+    for (int ct = 0; ct < 2; ++ct) lds_put4<P>(Stb, 4, 16 * wave + lr, 16 * ct + lc, S[ct]);
     GDN_COMMIT_VG(cn);
   }
 #undef GDN_LOAD_XY
