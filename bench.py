@@ -123,6 +123,72 @@ def summarize_rocprof(db_path: str) -> str:
     return "\n".join(lines)
 
 
+def _pmc_means(db_path: str, counter: str, reduce=None) -> dict:
+    """Mean (or `reduce`) over dispatches of one counter, by short kernel name."""
+    import collections
+    import sqlite3
+    db = sqlite3.connect(db_path)
+    per = collections.defaultdict(float)
+    for k, d, n, v in db.execute("select kernel_name, dispatch_id, counter_name, value from counters_collection"):
+        if n == counter:
+            per[(k, d)] += v
+    agg = collections.defaultdict(list)
+    for (k, d), v in per.items():
+        agg[k.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]].append(v)
+    return {k: (reduce(v) if reduce else sum(v) / len(v)) for k, v in agg.items()}
+
+
+def write_traffic(dbs):
+    """profiles/traffic.json: HBM bytes per launch of each kernel, from
+    FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by what the same
+    counters read for the plain 268,435,456-byte device copy (--calibrate-copy)
+    in the same run."""
+    copy_bytes = 256 << 20
+    runs = {}
+    for name, (fdb, wdb) in zip(("prefill", "decode_b64", "decode_b1"), zip(dbs[0::2], dbs[1::2])):
+        f, wr = _pmc_means(fdb, "FETCH_SIZE"), _pmc_means(wdb, "WRITE_SIZE")
+        # The calibration copy is the largest copyBuffer dispatch of the run.
+        cf = max(v for k, v in _pmc_means(fdb, "FETCH_SIZE", max).items() if "copyBuffer" in k) * 1024.0
+        cw = max(v for k, v in _pmc_means(wdb, "WRITE_SIZE", max).items() if "copyBuffer" in k) * 1024.0
+        runs[name] = (f, wr, copy_bytes / cf, copy_bytes / cw)
+
+    def pick(run, sub):
+        f, wr, ff, fw = runs[run]
+        keys = [k for k in f if sub in k]
+        if not keys:
+            return None
+        return (sum(f[k] for k in keys) * 1024.0 * ff, sum(wr.get(k, 0.0) for k in keys) * 1024.0 * fw)
+
+    kernels = {}
+    for key, run, subs, what in (
+            ("prefill_core", "prefill", ("chunk_local", "chunk_state"),
+             "gdn_prefill_chunked on the T=4096, Hv=48 bf16 workload (chunk_local + chunk_state)"),
+            ("prefill_prep", "prefill", ("prep_kernel",), "gdn_conv_gate_prep, T=4096 Hv=48 bf16"),
+            ("prefill_norm", "prefill", ("norm_kernel",), "gdn_gated_rmsnorm, T=4096 Hv=48 bf16"),
+            ("decode_b64", "decode_b64", ("decode_kernel",), "gdn_decode_step, batch 64, Hv=32"),
+            ("decode_fused_b64", "decode_b64", ("decode_fused_kernel",), "gdn_decode_fused, batch 64, Hv=32"),
+            ("decode_b1", "decode_b1", ("decode_kernel",), "gdn_decode_step, batch 1, Hv=32"),
+            ("decode_fused_b1", "decode_b1", ("decode_fused_kernel",), "gdn_decode_fused, batch 1, Hv=32")):
+        tot = [pick(run, sub) for sub in subs]
+        if any(t is None for t in tot):
+            continue
+        kernels[key] = {"what": what, "fetch_bytes": int(sum(t[0] for t in tot)),
+                        "write_bytes": int(sum(t[1] for t in tot))}
+    rec = {"source_sha256": kernel_source_hash(),
+           "note": "HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch, separate "
+                   "runs), scaled by what the same counters read for a plain 256 MiB device copy in the same run.",
+           "calibration": {k: {"fetch_factor": round(v[2], 4), "write_factor": round(v[3], 4)}
+                           for k, v in runs.items()},
+           "kernels": kernels,
+           "commands": [f"rocprofv3 --pmc {c} -d <dir> -o run -- python3 bench.py {o} --calibrate-copy"
+                        for o in ("--only prefill --steps 2 --warmup 1 --no-cpu-baseline",
+                                  "--only decode-b64 --no-graph", "--only decode-b1 --no-graph")
+                        for c in ("FETCH_SIZE", "WRITE_SIZE")]}
+    with open(os.path.join(PROFILES, "traffic.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(kernels, indent=1))
+
+
 def bench_prefill(steps: int, warmup: int):
     w = wl.WORKLOADS[3]
     x = wl.generate(w)
@@ -187,7 +253,7 @@ def decode_step_bytes(w: wl.Workload) -> int:
             + 2 * N * Hv * act + C * 4 * 4 + 2 * Hv * 4 + d * 4)
 
 
-def bench_decode(wid: int, warmup_steps: int = 32):
+def bench_decode(wid: int, warmup_steps: int = 32, graphs: bool = True):
     """Time the workload's whole decode loop four ways: the three calls per
     step (prep, step, norm) and the single fused call, each with plain
     launches and as one captured HIP graph replayed once."""
@@ -244,7 +310,7 @@ def bench_decode(wid: int, warmup_steps: int = 32):
     reset()
     modes["fused"] = timed(lambda: [fused_step(s) for s in range(steps)])
     # The whole loop captured as one graph, replayed once untimed, then timed.
-    for name, fn in (("three_call_graph", three_step), ("fused_graph", fused_step)):
+    for name, fn in ((("three_call_graph", three_step), ("fused_graph", fused_step)) if graphs else ()):
         reset()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
@@ -259,7 +325,7 @@ def bench_decode(wid: int, warmup_steps: int = 32):
     per = {k: {"us_per_step": round(v * 1e3 / steps, 2), "tokens_per_s": round(N * steps / (v * 1e-3), 1)}
            for k, v in modes.items()}
     step_bytes = decode_step_bytes(w)
-    f_us = modes["fused_graph"] * 1e3 / steps
+    f_us = modes["fused_graph" if graphs else "fused"] * 1e3 / steps
     gbs = step_bytes / (f_us * 1e-6) / 1e9
     kb = decode_kernel_bytes(w)
     kgbs = kb / (k_ms * 1e-3) / 1e9
@@ -268,7 +334,8 @@ def bench_decode(wid: int, warmup_steps: int = 32):
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4),
                          "traffic": measured_traffic("decode_fused_b64" if N > 1 else "decode_fused_b1"),
-                         "kernel": "gdn_decode_fused (graph replay; launch duration = loop time / steps)",
+                         "kernel": "gdn_decode_fused (%s; launch duration = loop time / steps)"
+                                   % ("graph replay" if graphs else "plain launches"),
                          "bytes_per_launch": step_bytes, "avg_launch_us": round(f_us, 2)},
             "roofline_decode_step": {"bound": "hbm", "achieved": round(kgbs, 1), "peak": HBM_PEAK_GBS,
                                      "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4),
@@ -277,7 +344,12 @@ def bench_decode(wid: int, warmup_steps: int = 32):
                                      "bytes_per_launch": kb, "avg_launch_us": round(k_ms * 1e3, 2)}}
 
 
-def cpu_baseline():
+def cpu_baseline(max_threads: int = 16):
+    """The fp64 oracle over the whole prefill workload, in two arms: one
+    thread, and the V-heads split over up to `max_threads` threads (the
+    heads are independent; each thread runs the oracle's delta rule on its
+    share, and ctypes releases the GIL during the C call)."""
+    import threading
     import oracle
     w = wl.WORKLOADS[3]
     x = wl.generate(w)
@@ -290,14 +362,43 @@ def cpu_baseline():
         else:
             xf[k] = v.astype(np.float64)
     orc = oracle.default()
-    t0 = time.perf_counter()
-    orc.layer(xf["cu_seqlens"], w.n_qk_heads, w.n_v_heads, w.head_dim, xf["qkv"], xf["z"], xf["b"], xf["a"],
-              xf["conv_w"], xf["dt_bias"], xf["A_log"], xf["norm_w"], xf["conv0"], xf["S0"])
-    dt = time.perf_counter() - t0
     T = int(x["cu_seqlens"][-1])
-    return {"value": round(T / dt, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"the whole prefill workload once ({T} tokens x 48 V-heads), fp64, one thread, "
-                      f"{dt:.1f} s"}
+    Hqk, Hv, d = w.n_qk_heads, w.n_v_heads, w.head_dim
+    args = (xf["cu_seqlens"], Hqk, Hv, d, xf["qkv"], xf["z"], xf["b"], xf["a"], xf["conv_w"], xf["dt_bias"],
+            xf["A_log"], xf["norm_w"], xf["conv0"], xf["S0"])
+
+    t0 = time.perf_counter()
+    orc.layer(*args)
+    dt1 = time.perf_counter() - t0
+
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    nt = max(1, min(max_threads, avail, Hv))
+    groups = [list(range(i, Hv, nt)) for i in range(nt)]
+    t0 = time.perf_counter()
+    r = orc.conv_gate_prep(xf["cu_seqlens"], Hqk, Hv, d, xf["qkv"], xf["b"], xf["a"], xf["conv_w"], xf["dt_bias"],
+                           xf["A_log"], xf["conv0"])
+    outs = [None] * nt
+
+    def work(i):
+        outs[i] = orc.delta_rule(xf["cu_seqlens"], Hqk, Hv, d, r["q"], r["k"], r["v"], r["beta"], r["g"],
+                                 xf["S0"], heads=groups[i])
+    th = [threading.Thread(target=work, args=(i,)) for i in range(nt)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    o = np.empty_like(outs[0][0])
+    for i, hs in enumerate(groups):
+        o[:, hs] = outs[i][0][:, hs]
+    orc.gated_rmsnorm(o, xf["z"].reshape(T, Hv, d), xf["norm_w"])
+    dtn = time.perf_counter() - t0
+    return {"value": round(T / dtn, 2), "unit": "tokens/s", "cores": nt, "kind": "oracle",
+            "sample": f"the whole prefill workload once ({T} tokens x {Hv} V-heads), fp64; V-heads split over "
+                      f"{nt} threads, {dtn:.2f} s",
+            "one_thread": {"value": round(T / dt1, 2), "unit": "tokens/s", "cores": 1, "seconds": round(dt1, 2)}}
 
 
 def main():
@@ -313,9 +414,16 @@ def main():
                     help="print a per-kernel summary of a rocprofv3 results database and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy 4 times (reference for HBM byte counters)")
+    ap.add_argument("--no-graph", action="store_true", help="decode: plain launches only (for counter runs)")
+    ap.add_argument("--write-traffic", nargs=6, metavar="DB", default=None,
+                    help="write profiles/traffic.json from six rocprofv3 --pmc databases: FETCH_SIZE and "
+                         "WRITE_SIZE runs of --only prefill, --only decode-b64, --only decode-b1 (in that order)")
     a = ap.parse_args()
     if a.summarize_rocprof:
         print(summarize_rocprof(a.summarize_rocprof))
+        return
+    if a.write_traffic:
+        write_traffic(a.write_traffic)
         return
     if a.gpus != 1:
         print(f"bench.py measures one GPU only: the mixer's path here runs on a single MI355X; "
@@ -335,7 +443,7 @@ def main():
         torch.cuda.synchronize()
         log("copy calibration: 4 x 268435456 bytes")
     if a.only in ("decode-b1", "decode-b64"):
-        d = bench_decode(2 if a.only == "decode-b1" else 4)
+        d = bench_decode(2 if a.only == "decode-b1" else 4, graphs=not a.no_graph)
         print(json.dumps(d), flush=True)
         return
     log("prefill workload: T=4096 Hqk=16 Hv=48 bf16")
@@ -346,7 +454,7 @@ def main():
         decode = []
         for wid in (2, 4):
             log(f"decode workload {wid}")
-            decode.append(bench_decode(wid))
+            decode.append(bench_decode(wid, graphs=not a.no_graph))
             log(json.dumps(decode[-1]))
     cpu = None
     if not a.no_cpu_baseline and a.only is None:
