@@ -324,6 +324,13 @@ __device__ __forceinline__ size_t frag_lane_off(int KS, int r, int k) {
 
 template <Prec P> struct FragIO;
 template <> struct FragIO<Prec::F32> {
+  // The whole fragment (rt, ks) of this lane (a wave stores a block with
+  // coalesced 16-byte pieces).
+  static __device__ __forceinline__ void store(uint8_t *m, int KS, int rt, int ks, const Op<Prec::F32>::Frag &f) {
+    uint8_t *b = m + static_cast<size_t>(rt * KS + ks) * kFragBlk + lane_id() * 32;
+    *reinterpret_cast<f32x4 *>(b) = f.a;
+    *reinterpret_cast<f32x4 *>(b + 16) = f.b;
+  }
   // Four consecutive indices k .. k+3 (k % 4 == 0) of row r.
   static __device__ __forceinline__ void put4(uint8_t *m, int KS, int r, int k, f32x4 x) {
     *reinterpret_cast<f32x4 *>(m + frag_lane_off(KS, r, k) + (k & 7) * 4) = x;
@@ -337,6 +344,11 @@ template <> struct FragIO<Prec::F32> {
   }
 };
 template <> struct FragIO<Prec::BF16X3> {
+  static __device__ __forceinline__ void store(uint8_t *m, int KS, int rt, int ks, const Op<Prec::BF16X3>::Frag &f) {
+    uint8_t *b = m + static_cast<size_t>(rt * KS + ks) * kFragBlk + lane_id() * 16;
+    *reinterpret_cast<bf16x8 *>(b) = f.hi;
+    *reinterpret_cast<bf16x8 *>(b + 1024) = f.lo;
+  }
   static __device__ __forceinline__ void put4(uint8_t *m, int KS, int r, int k, f32x4 x) {
     bf16x4 hi, lo;
     split4(x, hi, lo);

@@ -17,6 +17,7 @@ namespace {
 constexpr int kNormThreads = 256;
 constexpr int kLanesPerRow = 16;             // 8 values per lane
 constexpr int kRowsPerBlock = kNormThreads / kLanesPerRow;
+constexpr int kRowsPerThread = 1;
 
 // 8 consecutive activation values <-> two float4.
 __device__ __forceinline__ void load8(const float *p, size_t i, float4 &a, float4 &b) {
@@ -44,39 +45,47 @@ __device__ __forceinline__ void store8(bf16_t *p, size_t i, float4 a, float4 b) 
 }
 
 // 16 lanes per row, 8 values per lane (16-byte bf16 or 32-byte fp32 accesses),
-// 4 rows per wave, 16 rows per block.
+// 4 rows per wave at a time; each thread handles kRowsPerThread rows that
+// lie kRowsPerBlock apart, all loaded before any is used.
 template <typename TA>
 __global__ __launch_bounds__(kNormThreads) void norm_kernel(NormParams p) {
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + threadIdx.x / kLanesPerRow;
-  if (row >= p.n_rows) return;
   const int sub = threadIdx.x % kLanesPerRow;
-  const size_t i = static_cast<size_t>(row) * kHeadDim + 8 * sub;
-  float4 o0, o1, z0, z1;
-  load8(static_cast<const TA *>(p.o), i, o0, o1);
-  load8(static_cast<const TA *>(p.z), i, z0, z1);
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock * kRowsPerThread + threadIdx.x / kLanesPerRow;
   const float4 w0 = *reinterpret_cast<const float4 *>(p.w + 8 * sub);
   const float4 w1 = *reinterpret_cast<const float4 *>(p.w + 8 * sub + 4);
-  float ss = o0.x * o0.x + o0.y * o0.y + o0.z * o0.z + o0.w * o0.w +
-             o1.x * o1.x + o1.y * o1.y + o1.z * o1.z + o1.w * o1.w;
+  float4 o0[kRowsPerThread], o1[kRowsPerThread], z0[kRowsPerThread], z1[kRowsPerThread];
+#pragma unroll
+  for (int u = 0; u < kRowsPerThread; ++u) {
+    const int64_t row = min(row0 + u * kRowsPerBlock, p.n_rows - 1);
+    const size_t i = static_cast<size_t>(row) * kHeadDim + 8 * sub;
+    load8(static_cast<const TA *>(p.o), i, o0[u], o1[u]);
+    load8(static_cast<const TA *>(p.z), i, z0[u], z1[u]);
+  }
   static_assert(kLanesPerRow == 16, "one row per 16-lane DPP row");
-  ss = row16_sum(ss);
-  const float inv = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + p.eps);
-  float4 y0, y1;
-  y0.x = o0.x * inv * w0.x * siluf_(z0.x);
-  y0.y = o0.y * inv * w0.y * siluf_(z0.y);
-  y0.z = o0.z * inv * w0.z * siluf_(z0.z);
-  y0.w = o0.w * inv * w0.w * siluf_(z0.w);
-  y1.x = o1.x * inv * w1.x * siluf_(z1.x);
-  y1.y = o1.y * inv * w1.y * siluf_(z1.y);
-  y1.z = o1.z * inv * w1.z * siluf_(z1.z);
-  y1.w = o1.w * inv * w1.w * siluf_(z1.w);
-  store8(static_cast<TA *>(p.y), i, y0, y1);
+#pragma unroll
+  for (int u = 0; u < kRowsPerThread; ++u) {
+    const int64_t row = row0 + u * kRowsPerBlock;
+    float ss = o0[u].x * o0[u].x + o0[u].y * o0[u].y + o0[u].z * o0[u].z + o0[u].w * o0[u].w +
+               o1[u].x * o1[u].x + o1[u].y * o1[u].y + o1[u].z * o1[u].z + o1[u].w * o1[u].w;
+    ss = row16_sum(ss);
+    const float inv = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + p.eps);
+    float4 y0, y1;
+    y0.x = o0[u].x * inv * w0.x * siluf_(z0[u].x);
+    y0.y = o0[u].y * inv * w0.y * siluf_(z0[u].y);
+    y0.z = o0[u].z * inv * w0.z * siluf_(z0[u].z);
+    y0.w = o0[u].w * inv * w0.w * siluf_(z0[u].w);
+    y1.x = o1[u].x * inv * w1.x * siluf_(z1[u].x);
+    y1.y = o1[u].y * inv * w1.y * siluf_(z1[u].y);
+    y1.z = o1[u].z * inv * w1.z * siluf_(z1[u].z);
+    y1.w = o1[u].w * inv * w1.w * siluf_(z1[u].w);
+    if (row < p.n_rows) store8(static_cast<TA *>(p.y), static_cast<size_t>(row) * kHeadDim + 8 * sub, y0, y1);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_norm(const NormParams &p, gdn_dtype act, hipStream_t s) {
-  const int64_t blocks = (p.n_rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int64_t blocks = (p.n_rows + kRowsPerBlock * kRowsPerThread - 1) / (kRowsPerBlock * kRowsPerThread);
   if (act == GDN_BF16)
     hipLaunchKernelGGL(norm_kernel<bf16_t>, dim3(static_cast<unsigned>(blocks)), dim3(kNormThreads), 0, s, p);
   else

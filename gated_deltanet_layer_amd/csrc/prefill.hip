@@ -104,14 +104,17 @@ template <> __device__ __forceinline__ Op<Prec::BF16X3>::Frag make_frag<Prec::BF
 
 // ---------------------------------------------------------------------------
 // chunk_local: per (chunk, K-head), 4 waves, ~72 KB of LDS (two blocks per CU).
-//  1. K and Q rows of the chunk -> operand blocks in the workspace (K also
-//     into LDS), K^T rows -> operand blocks.
-//  2. Wave w computes row tile w of the lower triangles of K K^T and Q K^T.
-//  3. The V-heads that use this K-head are solved in parallel, one per wave
-//     (up to kSolveWaves at a time): decays, P, L = I + A, and L^-1 by
-//     blocked forward substitution done in place in the wave's own LDS
-//     region, then Tm = L^-1 diag(beta). Only wave-level ordering is needed
-//     inside a solve.
+//  1. K rows of the chunk into LDS; Q rows into registers as the A fragments
+//     of wave w's row tile, stored to the workspace as they are.
+//  2. K and K^T operand blocks to the workspace, a whole fragment per lane
+//     read out of LDS; wave w computes row tile w of the lower triangles of
+//     K K^T and Q K^T.
+//  3. For the V-heads that use this K-head (kSolveWaves at a time): decays
+//     and beta; L = I + A into LDS and P to the workspace, one fragment
+//     block per step spread over all waves; L^-1 by blocked forward
+//     substitution in place, one wave per V-head; Tm = L^-1 diag(beta) to
+//     the workspace over all waves. Blocks of P and Tm above the diagonal
+//     32 x 32 blocks are all zero and are never written or read.
 constexpr int kSolveWaves = 3;
 constexpr int kTri = kChunk * (kChunk + 1) / 2;   // packed lower triangle incl. diagonal
 
@@ -122,8 +125,9 @@ __device__ __forceinline__ void wave_sync_lds() { asm volatile("s_waitcnt lgkmcn
 
 template <Prec P>
 __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(PrefillParams p, int64_t max_chunks) {
-  // Phase 1 holds K as blocked operand rows; phase 2 reuses the bytes for
-  // the solving waves' fp32 matrices (L, overwritten in place by L^-1).
+  using Frag = typename Op<P>::Frag;
+  // K as blocked operand rows first; then the solving waves' fp32 matrices
+  // (L, overwritten in place by L^-1) reuse the bytes.
   constexpr int kKbBytes = kChunk * kPitch128;
   constexpr int kLxBytes = kSolveWaves * kChunk * kLdS * 4;
   __shared__ __attribute__((aligned(16))) uint8_t buf[kKbBytes > kLxBytes ? kKbBytes : kLxBytes];
@@ -153,123 +157,128 @@ __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(PrefillParam
   uint8_t *wk = ws.qk + (static_cast<size_t>(cid) * p.n_qk + h) * kQkBytes;   // K rows, Q rows, K^T rows
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
-  // Q rows of this wave's Gram row tile, as A fragments (loaded up front).
+  // Q rows of this wave's row tile as A fragments (rows >= len are zero);
+  // they are also the Q operand blocks (wave, ks) of the workspace.
   const int rt = wave;
   const int qrow = 16 * rt + (lane & 15);
-  f32x4 qa[kHeadDim / 32], qb[kHeadDim / 32];
+  Frag fq[kHeadDim / 32];
   {
     const float *qp = qg + min(qrow, len - 1) * qk_stride + 8 * (lane >> 4);
+    f32x4 qa[kHeadDim / 32], qb[kHeadDim / 32];
 #pragma unroll
     for (int ks = 0; ks < kHeadDim / 32; ++ks) {
       qa[ks] = *reinterpret_cast<const f32x4 *>(qp + 32 * ks);
       qb[ks] = *reinterpret_cast<const f32x4 *>(qp + 32 * ks + 4);
     }
+    const bool qvalid = qrow < len;
+#pragma unroll
+    for (int ks = 0; ks < kHeadDim / 32; ++ks) {
+      fq[ks] = make_frag<P>(qvalid ? qa[ks] : zero4, qvalid ? qb[ks] : zero4);
+      FragIO<P>::store(wk + kKBytes, kHeadDim / 32, rt, ks, fq[ks]);
+    }
   }
-  {  // K and Q rows -> operand blocks (K also into LDS); rows >= len are zero.
+  {  // K rows -> blocked operand rows in LDS; rows >= len are zero.
     constexpr int kPer = kChunk * (kHeadDim / 4) / kLocalThreads;
-    f32x4 kb4[kPer], qb4[kPer];
+    f32x4 kb4[kPer];
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int idx = tid + u * kLocalThreads, r = idx / (kHeadDim / 4), c4 = idx % (kHeadDim / 4);
-      const size_t off = min(r, len - 1) * qk_stride + 4 * c4;
-      kb4[u] = *reinterpret_cast<const f32x4 *>(kg + off);
-      qb4[u] = *reinterpret_cast<const f32x4 *>(qg + off);
+      kb4[u] = *reinterpret_cast<const f32x4 *>(kg + min(r, len - 1) * qk_stride + 4 * c4);
     }
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int idx = tid + u * kLocalThreads, r = idx / (kHeadDim / 4), c4 = idx % (kHeadDim / 4);
-      const f32x4 kx = r < len ? kb4[u] : zero4, qx = r < len ? qb4[u] : zero4;
-      Op<P>::put4(Kb + r * kPitch128, 4 * c4, kx);
-      FragIO<P>::put4(wk, kHeadDim / 32, r, 4 * c4, kx);
-      FragIO<P>::put4(wk + kKBytes, kHeadDim / 32, r, 4 * c4, qx);
-    }
-  }
-  {  // K^T rows: element (i, r) of K^T is K[r][i]; 4 consecutive r per item.
-    constexpr int kTItems = kHeadDim * (kChunk / 4) / kLocalThreads;
-    f32x4 kt[kTItems];
-#pragma unroll
-    for (int u = 0; u < kTItems; ++u) {
-      const int item = tid + u * kLocalThreads, i = item % kHeadDim, r0 = 4 * (item / kHeadDim);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) kt[u][e] = kg[min(r0 + e, len - 1) * qk_stride + i];
-    }
-#pragma unroll
-    for (int u = 0; u < kTItems; ++u) {
-      const int item = tid + u * kLocalThreads, i = item % kHeadDim, r0 = 4 * (item / kHeadDim);
-      f32x4 x;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = r0 + e < len ? kt[u][e] : 0.f;
-      FragIO<P>::put4(wk + 2 * kKBytes, kChunk / 32, i, r0, x);
+      Op<P>::put4(Kb + r * kPitch128, 4 * c4, r < len ? kb4[u] : zero4);
     }
   }
   block_sync_lds();
 
+  // K rows (4 x 4 blocks) and K^T rows (8 x 2 blocks) to the workspace, read
+  // out of LDS a whole fragment at a time: wave w stores blocks w, w + 4, ..
+#pragma unroll
+  for (int b = wave; b < 16; b += 4) {
+    FragIO<P>::store(wk, kHeadDim / 32, b >> 2, b & 3, frag<P>(Kb, kPitch128, 16 * (b >> 2), 32 * (b & 3)));
+    FragIO<P>::store(wk + 2 * kKBytes, kChunk / 32, b >> 1, b & 1,
+                     frag_t<P>(Kb, kPitch128, 16 * (b >> 1), 32 * (b & 1)));
+  }
   // Row tile rt of the lower triangles of K K^T and Q K^T.
-  {
-    const bool qvalid = qrow < len;
-    for (int ct = 0; ct <= rt; ++ct) {
-      f32x4 ak = zero4, aq = zero4;
+  for (int ct = 0; ct <= rt; ++ct) {
+    f32x4 ak = zero4, aq = zero4;
 #pragma unroll
-      for (int ks = 0; ks < kHeadDim / 32; ++ks) {
-        const typename Op<P>::Frag b = frag<P>(Kb, kPitch128, ct * 16, ks * 32);
-        Op<P>::mma(ak, frag<P>(Kb, kPitch128, rt * 16, ks * 32), b);
-        Op<P>::mma(aq, make_frag<P>(qvalid ? qa[ks] : zero4, qvalid ? qb[ks] : zero4), b);
-      }
+    for (int ks = 0; ks < kHeadDim / 32; ++ks) {
+      const Frag b = frag<P>(Kb, kPitch128, ct * 16, ks * 32);
+      Op<P>::mma(ak, frag<P>(Kb, kPitch128, rt * 16, ks * 32), b);
+      Op<P>::mma(aq, fq[ks], b);
+    }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * rt + acc_row(r), col = 16 * ct + acc_col();
-        if (col <= row) {
-          Gk[tri(row, col)] = ak[r];
-          Gq[tri(row, col)] = aq[r];
-        }
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * rt + acc_row(r), col = 16 * ct + acc_col();
+      if (col <= row) {
+        Gk[tri(row, col)] = ak[r];
+        Gq[tri(row, col)] = aq[r];
       }
     }
   }
   block_sync_lds();   // K is dead from here: buf becomes the solving waves' matrices
 
+  // The 16 x 32 blocks (rt, ks) of a 64 x 64 lower-triangular operand that
+  // are not all zero (blocks (0, 1) and (1, 1) are).
+  constexpr int kLowBlocks = 6;
+  const int low_rt[kLowBlocks] = {0, 1, 2, 2, 3, 3};
+  const int low_ks[kLowBlocks] = {0, 0, 0, 1, 0, 1};
+
   const int nvh = p.n_v / p.n_qk;
   for (int u0 = 0; u0 < nvh; u0 += kSolveWaves) {
-    const int u = u0 + wave;
-    if (wave < kSolveWaves && u < nvh) {
-      const int j = h + u * p.n_qk;
-      float *Lx = reinterpret_cast<float *>(buf) + wave * kChunk * kLdS;
-      double *gam = gam_s[wave];
-      float *bet = bet_s[wave];
-      // Cumulative log-decay (0 past len, so gam stays at its last value) and
-      // beta. gam reaches a few hundred inside a chunk and only its
-      // differences gam_r - gam_m are used: in fp32 they would lose
-      // ~|gam| * 6e-8 to cancellation, so the scan and the differences are fp64.
-      {
-        const size_t e = static_cast<size_t>(t0 + min(lane, len - 1)) * p.n_v + j;
-        const double gr = lane < len ? static_cast<double>(p.g[e]) : 0.0;
-        const float br = lane < len ? p.beta[e] : 0.f;
-        const double gm = wave_inclusive_scan_d(gr);
-        gam[lane] = gm;
-        bet[lane] = br;
-        ws.gam[(static_cast<size_t>(cid) * p.n_v + j) * kChunk + lane] = gm;
-      }
-      wave_sync_lds();
+    const int nu = min(kSolveWaves, nvh - u0);   // V-heads of this round, slot s = head u0 + s
+    if (u0 > 0) block_sync_lds();                // the previous round's readers are done
+    // Cumulative log-decay (0 past len, so gam stays at its last value) and
+    // beta, one wave per V-head. gam reaches a few hundred inside a chunk and
+    // only its differences gam_r - gam_m are used: in fp32 they would lose
+    // ~|gam| * 6e-8 to cancellation, so the scan and the differences are fp64.
+    if (wave < nu) {
+      const int j = h + (u0 + wave) * p.n_qk;
+      const size_t e = static_cast<size_t>(t0 + min(lane, len - 1)) * p.n_v + j;
+      const double gr = lane < len ? static_cast<double>(p.g[e]) : 0.0;
+      const float br = lane < len ? p.beta[e] : 0.f;
+      const double gm = wave_inclusive_scan_d(gr);
+      gam_s[wave][lane] = gm;
+      bet_s[wave][lane] = br;
+      ws.gam[(static_cast<size_t>(cid) * p.n_v + j) * kChunk + lane] = gm;
+    }
+    block_sync_lds();
 
-      uint8_t *wv = ws.v + (static_cast<size_t>(cid) * p.n_v + j) * kVBytes;   // Tm, then P
-      // L = I + A into LDS and P to the workspace, 4 consecutive m per item.
-      for (int it = lane; it < kChunkMat / 4; it += kWave) {
-        const int r = it / (kChunk / 4), m0 = 4 * (it % (kChunk / 4));
-        f32x4 pv = zero4;
+    // L = I + A into LDS and P to the workspace, one fragment block per step,
+    // spread over all waves: lane l owns row 16 rt + l % 16, columns
+    // 32 ks + 8 (l / 16) + 0..7 of the block.
+    for (int item = wave; item < nu * kLowBlocks; item += kLocalThreads / kWave) {
+      const int s = item / kLowBlocks, bl = item % kLowBlocks;
+      const int brt = low_rt[bl], bks = low_ks[bl];
+      const int j = h + (u0 + s) * p.n_qk;
+      float *Lx = reinterpret_cast<float *>(buf) + s * kChunk * kLdS;
+      const double *gam = gam_s[s];
+      const int r = 16 * brt + (lane & 15), m0 = 32 * bks + 8 * (lane >> 4);
+      const double gr = gam[r];
+      const float br = bet_s[s][r];
+      f32x4 pa, pb;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int m = m0 + e;
-          float lv = r == m ? 1.f : 0.f;
-          if (m <= r) {
-            const float dec = expf(static_cast<float>(gam[r] - gam[m]));
-            pv[e] = dec * Gq[tri(r, m)];
-            if (m < r) lv = bet[r] * dec * Gk[tri(r, m)];
-          }
-          Lx[r * kLdS + m] = lv;
+      for (int e = 0; e < 8; ++e) {
+        const int m = m0 + e;
+        float pv = 0.f, lv = m == r ? 1.f : 0.f;
+        if (m <= r) {
+          const float dec = expf(static_cast<float>(gr - gam[m]));
+          pv = dec * Gq[tri(r, m)];
+          if (m < r) lv = br * dec * Gk[tri(r, m)];
         }
-        FragIO<P>::put4(wv + kMatBytes, kChunk / 32, r, m0, pv);
+        Lx[r * kLdS + m] = lv;
+        if (e < 4) pa[e] = pv; else pb[e - 4] = pv;
       }
-      wave_sync_lds();
+      uint8_t *wv = ws.v + (static_cast<size_t>(cid) * p.n_v + j) * kVBytes;   // Tm, then P
+      FragIO<P>::store(wv + kMatBytes, kChunk / 32, brt, bks, make_frag<P>(pa, pb));
+    }
+    block_sync_lds();
 
+    if (wave < nu) {
+      float *Lx = reinterpret_cast<float *>(buf) + wave * kChunk * kLdS;
       // Diagonal blocks X_bb = L_bb^-1 by forward substitution: lane 16 b + c
       // owns column c of block b and writes it over L_bb.
       {
@@ -320,15 +329,27 @@ __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(PrefillParam
           wave_sync_lds();
         }
       }
+    }
+    block_sync_lds();
 
-      // Tm = X diag(beta) (lower triangle) to the workspace.
-      for (int it = lane; it < kChunkMat / 4; it += kWave) {
-        const int r = it / (kChunk / 4), m0 = 4 * (it % (kChunk / 4));
-        f32x4 tv;
+    // Tm = X diag(beta) (lower triangle) to the workspace, one fragment block
+    // per step over all waves.
+    for (int item = wave; item < nu * kLowBlocks; item += kLocalThreads / kWave) {
+      const int s = item / kLowBlocks, bl = item % kLowBlocks;
+      const int brt = low_rt[bl], bks = low_ks[bl];
+      const int j = h + (u0 + s) * p.n_qk;
+      const float *Lx = reinterpret_cast<const float *>(buf) + s * kChunk * kLdS;
+      const float *bet = bet_s[s];
+      const int r = 16 * brt + (lane & 15), m0 = 32 * bks + 8 * (lane >> 4);
+      f32x4 ta, tb;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) tv[e] = m0 + e <= r ? Lx[r * kLdS + m0 + e] * bet[m0 + e] : 0.f;
-        FragIO<P>::put4(wv, kChunk / 32, r, m0, tv);
+      for (int e = 0; e < 8; ++e) {
+        const int m = m0 + e;
+        const float tv = m <= r ? Lx[r * kLdS + m] * bet[m] : 0.f;
+        if (e < 4) ta[e] = tv; else tb[e - 4] = tv;
       }
+      uint8_t *wv = ws.v + (static_cast<size_t>(cid) * p.n_v + j) * kVBytes;
+      FragIO<P>::store(wv, kChunk / 32, brt, bks, make_frag<P>(ta, tb));
     }
   }
 }
