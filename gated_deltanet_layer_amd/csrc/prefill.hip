@@ -62,7 +62,7 @@ constexpr int kLdV = kSlab + 4;           // fp32 pitch of the V slab in LDS
 //   per (chunk, V-head): Tm (64 x 64, 4 x 2 blocks) and P (same): 32 KB
 //   per (chunk, V-head): gam, 64 fp64
 constexpr size_t kKBytes = 16 * kFragBlk;
-constexpr size_t kQkBytes = 3 * kKBytes;
+constexpr size_t kQkBytes = 2 * kKBytes;
 constexpr size_t kMatBytes = 8 * kFragBlk;
 constexpr size_t kVBytes = 2 * kMatBytes;
 
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(PrefillParam
   const size_t qk_stride = static_cast<size_t>(p.n_qk) * kHeadDim;
   const float *kg = p.k + t0 * qk_stride + h * kHeadDim;
   const float *qg = p.q + t0 * qk_stride + h * kHeadDim;
-  uint8_t *wk = ws.qk + (static_cast<size_t>(cid) * p.n_qk + h) * kQkBytes;   // K rows, Q rows, K^T rows
+  uint8_t *wk = ws.qk + (static_cast<size_t>(cid) * p.n_qk + h) * kQkBytes;   // K rows, Q rows
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
   // Q rows of this wave's row tile as A fragments (rows >= len are zero);
@@ -193,14 +193,11 @@ __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(PrefillParam
   }
   block_sync_lds();
 
-  // K rows (4 x 4 blocks) and K^T rows (8 x 2 blocks) to the workspace, read
-  // out of LDS a whole fragment at a time: wave w stores blocks w, w + 4, ..
+  // K rows (4 x 4 blocks) to the workspace, read out of LDS a whole
+  // fragment at a time: wave w stores blocks w, w + 4, ..
 #pragma unroll
-  for (int b = wave; b < 16; b += 4) {
+  for (int b = wave; b < 16; b += 4)
     FragIO<P>::store(wk, kHeadDim / 32, b >> 2, b & 3, frag<P>(Kb, kPitch128, 16 * (b >> 2), 32 * (b & 3)));
-    FragIO<P>::store(wk + 2 * kKBytes, kChunk / 32, b >> 1, b & 1,
-                     frag_t<P>(Kb, kPitch128, 16 * (b >> 1), 32 * (b & 1)));
-  }
   // Row tile rt of the lower triangles of K K^T and Q K^T.
   for (int ct = 0; ct <= rt; ++ct) {
     f32x4 ak = zero4, aq = zero4;
@@ -398,18 +395,79 @@ template <> __device__ __forceinline__ void lds_put4<Prec::BF16X3>(uint8_t *buf,
   *reinterpret_cast<bf16x4 *>(b + kLdsBlk / 2) = lo;
 }
 
+// K rows of the current chunk in LDS, for the transposed (K^T) fragments of
+// the state update: BF16X3 keeps the hi and lo planes as bf16, F32 one fp32
+// plane. Row pitch kLdKt elements: rows stay 8-byte aligned and the gathers
+// of a wave (lane groups 16 g reading rows 8 g + e) fall on distinct banks.
+constexpr int kLdKt = kHeadDim + 4;
+
+template <Prec P> struct KtLds;
+template <> struct KtLds<Prec::BF16X3> {
+  static constexpr int kBytes = 2 * kChunk * kLdKt * 2;
+  // Store this lane's fragment (rt, ks) of K rows: row 16 rt + l % 16,
+  // indices 32 ks + 8 (l / 16) .. +7.
+  static __device__ __forceinline__ void put(uint8_t *buf, int rt, int ks, const Op<Prec::BF16X3>::Frag &f) {
+    const int l = lane_id();
+    __bf16 *hi = reinterpret_cast<__bf16 *>(buf);
+    __bf16 *lo = hi + kChunk * kLdKt;
+    const int off = (16 * rt + (l & 15)) * kLdKt + 32 * ks + 8 * (l >> 4);
+    *reinterpret_cast<bf16x4 *>(hi + off) = __builtin_shufflevector(f.hi, f.hi, 0, 1, 2, 3);
+    *reinterpret_cast<bf16x4 *>(hi + off + 4) = __builtin_shufflevector(f.hi, f.hi, 4, 5, 6, 7);
+    *reinterpret_cast<bf16x4 *>(lo + off) = __builtin_shufflevector(f.lo, f.lo, 0, 1, 2, 3);
+    *reinterpret_cast<bf16x4 *>(lo + off + 4) = __builtin_shufflevector(f.lo, f.lo, 4, 5, 6, 7);
+  }
+  // Fragment (it, ks) of K^T: row i = 16 it + l % 16, indices (tokens)
+  // t = 32 ks + 8 (l / 16) .. +7.
+  static __device__ __forceinline__ Op<Prec::BF16X3>::Frag get(const uint8_t *buf, int it, int ks) {
+    const int l = lane_id();
+    const __bf16 *hi = reinterpret_cast<const __bf16 *>(buf);
+    const __bf16 *lo = hi + kChunk * kLdKt;
+    const int off = (32 * ks + 8 * (l >> 4)) * kLdKt + 16 * it + (l & 15);
+    Op<Prec::BF16X3>::Frag f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      f.hi[e] = hi[off + e * kLdKt];
+      f.lo[e] = lo[off + e * kLdKt];
+    }
+    return f;
+  }
+};
+template <> struct KtLds<Prec::F32> {
+  static constexpr int kBytes = kChunk * kLdKt * 4;
+  static __device__ __forceinline__ void put(uint8_t *buf, int rt, int ks, const Op<Prec::F32>::Frag &f) {
+    const int l = lane_id();
+    float *k = reinterpret_cast<float *>(buf) + (16 * rt + (l & 15)) * kLdKt + 32 * ks + 8 * (l >> 4);
+    *reinterpret_cast<f32x4 *>(k) = f.a;
+    *reinterpret_cast<f32x4 *>(k + 4) = f.b;
+  }
+  static __device__ __forceinline__ Op<Prec::F32>::Frag get(const uint8_t *buf, int it, int ks) {
+    const int l = lane_id();
+    const float *k = reinterpret_cast<const float *>(buf) + (32 * ks + 8 * (l >> 4)) * kLdKt + 16 * it + (l & 15);
+    Op<Prec::F32>::Frag f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f.a[e] = k[e * kLdKt];
+      f.b[e] = k[(e + 4) * kLdKt];
+    }
+    return f;
+  }
+};
+
 // ---------------------------------------------------------------------------
 // chunk_state: per (sequence, V-head, 32-column slab). 8 waves; wave w has
 // rt = w % 4. Per chunk:
 //   X/Y : waves 0-3 X = K S, waves 4-7 Y = Q S (rows 16 rt, both column tiles)
-//   R   : waves 0-3 R = V - diag(Gam) X            -> R^T in LDS
-//   D   : waves 0-3 D = Tm R (rows 16 rt)          -> D^T and (diag(k~) D)^T
+//   R   : waves 0-3 R = V - diag(Gam) X            -> R in LDS
+//   D   : waves 0-3 D = Tm R (rows 16 rt)          -> D and diag(k~) D
 //         in LDS, k~_r = exp(gam_n - gam_r)
 //   O   : waves 4-7 O = s (diag(Gam) Y + P D)      (rows 16 rt)
 //   S   : all waves S <- Gam_n S + K^T diag(k~) D  (state rows 16 w)
 // Left operands stay in registers: K or Q rows (4 fragments), Tm or P rows
-// (2), K^T rows (2); each set is reloaded for the next chunk right after its
-// last use in this one, so its loads overlap the rest of the chunk.
+// (2); each set is reloaded for the next chunk right after its last use in
+// this one, so its loads overlap the rest of the chunk. The K^T fragments of
+// the state update are not loaded: the x-waves leave their K fragments in
+// LDS and every wave gathers its K^T fragments from there (the kernel is
+// bound by how many bytes a CU pulls from L2 per chunk).
 template <Prec P, typename TA>
 __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParams p, int64_t max_chunks) {
   using Frag = typename Op<P>::Frag;
@@ -419,6 +477,7 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
   __shared__ __attribute__((aligned(16))) uint8_t Dsb[4 * kLdsBlk];    // diag(k~) D: B of K^T (.)
   __shared__ __attribute__((aligned(16))) float Vs[kChunk * kLdV];    // V rows of the slab (fp32)
   __shared__ __attribute__((aligned(16))) float Os[4 * 16 * kLdOs];   // O staging, 16 rows per y-wave
+  __shared__ __attribute__((aligned(16))) uint8_t Ktb[KtLds<P>::kBytes];   // K rows of the chunk
   __shared__ float G_s[kChunk];            // exp(gam_r)
   __shared__ float ksc_s[kChunk];          // exp(gam_n - gam_r)
 
@@ -474,10 +533,9 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
   const uint8_t *v0 = ws.v + (static_cast<size_t>(cid0) * p.n_v + j) * kVBytes;
   const uint8_t *xy_src0 = qk0 + (x_wave ? 0 : kKBytes);             // K rows or Q rows
   const uint8_t *d_src0 = v0 + (x_wave ? 0 : kMatBytes);             // Tm rows or P rows
-  const uint8_t *kt_src0 = qk0 + 2 * kKBytes;                        // K^T rows
   const int v_row = tid / (kSlab / 4), v_c4 = tid % (kSlab / 4);
 
-  Frag fxy[kHeadDim / 32], fd[kChunk / 32], fk[kChunk / 32];
+  Frag fxy[kHeadDim / 32], fd[kChunk / 32];
   f32x4 pvv;
   double pg = 0.0, pg_end = 0.0;
 
@@ -489,9 +547,6 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
 #define GDN_LOAD_D(c)                                                                                \
   _Pragma("unroll") for (int ks = 0; ks < kChunk / 32; ++ks)                                         \
     if (ks == 0 || rt >= 2) fd[ks] = FragIO<P>::load(d_src0 + (c) * v_step, kChunk / 32, rt, ks)
-#define GDN_LOAD_KT(c)                                                                               \
-  _Pragma("unroll") for (int ks = 0; ks < kChunk / 32; ++ks)                                         \
-    fk[ks] = FragIO<P>::load(kt_src0 + (c) * qk_step, kChunk / 32, wave, ks)
   // V slab piece and gam of chunk c (committed to LDS after the chunk before it).
 #define GDN_LOAD_VG(c)                                                                               \
   do {                                                                                               \
@@ -520,7 +575,6 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
   if (nchunks > 0) {
     GDN_LOAD_XY(0);
     GDN_LOAD_D(0);
-    GDN_LOAD_KT(0);
     GDN_LOAD_VG(0);
     GDN_COMMIT_VG(0);
   }
@@ -540,6 +594,10 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
 #pragma unroll
     for (int ks = 0; ks < kHeadDim / 32; ++ks)
       Op<P>::mma2(XY[0], XY[1], fxy[ks], lds_frag<P>(Stb, ks), lds_frag<P>(Stb, 4 + ks));
+    if (x_wave) {  // K of this chunk to LDS for the K^T fragments of the state update
+#pragma unroll
+      for (int ks = 0; ks < kHeadDim / 32; ++ks) KtLds<P>::put(Ktb, rt, ks, fxy[ks]);
+    }
     GDN_LOAD_XY(cn);
     if (x_wave) {
 #pragma unroll
@@ -606,8 +664,7 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
     S[1] = S[1] * g_end;
 #pragma unroll
     for (int ks = 0; ks < kChunk / 32; ++ks)
-      Op<P>::mma2(S[0], S[1], fk[ks], lds_frag<P>(Dsb, ks), lds_frag<P>(Dsb, 2 + ks));
-    GDN_LOAD_KT(cn);
+      Op<P>::mma2(S[0], S[1], KtLds<P>::get(Ktb, wave, ks), lds_frag<P>(Dsb, ks), lds_frag<P>(Dsb, 2 + ks));
     block_sync_lds();                        // every LDS read of chunk ci is done
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) lds_put4<P>(Stb, 4, 16 * wave + lr, 16 * ct + lc, S[ct]);
@@ -615,7 +672,6 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
   }
 #undef GDN_LOAD_XY
 #undef GDN_LOAD_D
-#undef GDN_LOAD_KT
 #undef GDN_LOAD_VG
 #undef GDN_COMMIT_VG
 

@@ -57,9 +57,9 @@ def test_default_config(lib):
 
 def test_workspace_size(lib):
     cfg = B.make_config(16, 48)
-    # (ceil(T/64) + N) chunks x (Hqk x K, Q, K^T operands + Hv x (Tm, P operands + 64 fp64))
+    # (ceil(T/64) + N) chunks x (Hqk x K, Q operands + Hv x (Tm, P operands + 64 fp64))
     chunks = 64 + 1
-    assert B.gdn_prefill_workspace_bytes(cfg, 1, 4096) == chunks * (16 * 3 * 64 * 128 * 4 + 48 * (2 * 64 * 64 * 4 + 64 * 8))
+    assert B.gdn_prefill_workspace_bytes(cfg, 1, 4096) == chunks * (16 * 2 * 64 * 128 * 4 + 48 * (2 * 64 * 64 * 4 + 64 * 8))
     assert B.gdn_prefill_workspace_bytes(cfg, 1, 0) == 0
     bad = B.make_config(16, 40)
     assert B.gdn_prefill_workspace_bytes(bad, 1, 64) == 0
