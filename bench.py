@@ -3,8 +3,10 @@
 One step = one pass of the whole mixer over the prefill workload
 (T = 4096 tokens, 16 K-heads, 48 V-heads, bf16 activations, one sequence):
 gdn_conv_gate_prep -> gdn_prefill_chunked -> gdn_gated_rmsnorm, inputs
-already resident in HBM. ``value`` is tokens per second over exactly
-``--steps`` timed steps after ``--warmup`` untimed ones.
+already resident in HBM. The steps run twice: as plain launches, and as
+the step captured in a HIP graph and replayed; ``value`` is tokens per
+second over exactly ``--steps`` timed steps (after ``--warmup`` untimed
+ones) of the faster of the two, both reported under "prefill_modes".
 
 The same run also times the decode path on the batch-1 workload (32 V-heads,
 1024 consecutive steps) and the batch-64 workload (256 steps), and reports
@@ -219,12 +221,32 @@ def bench_prefill(steps: int, warmup: int):
         step(core_ev[i])
     end.record()
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
+    plain_ms = start.elapsed_time(end)
     core_ms = float(np.mean([a.elapsed_time(b) for a, b in core_ev]))
+    # The same step captured once as a HIP graph (four kernel nodes, no
+    # memset nodes) and replayed: what a caller that captures its layer gets.
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    graph_ms = start.elapsed_time(end)
+    del g
+    total_ms = min(plain_ms, graph_ms)
     n_chunk_heads = ((T + CHUNK - 1) // CHUNK) * w.n_v_heads
     flops = FLOP_PER_CHUNK_HEAD * n_chunk_heads
     achieved = flops / (core_ms * 1e-3) / 1e12
     return dict(total_ms=total_ms, ms_per_step=total_ms / steps, tokens=T, core_ms=core_ms,
+                modes={"plain": {"ms_per_step": round(plain_ms / steps, 4),
+                                 "tokens_per_s": round(T * steps / (plain_ms * 1e-3), 1)},
+                       "graph": {"ms_per_step": round(graph_ms / steps, 4),
+                                 "tokens_per_s": round(T * steps / (graph_ms * 1e-3), 1)}},
                 roofline={"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
                           "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                           "traffic": measured_traffic("prefill_core"),
@@ -470,6 +492,7 @@ def main():
         "dtype": "bf16 in/out, fp32 state and arithmetic", "data": "synthetic (seeded)",
         "config": {"workload": "prefill T=4096, 1 sequence, Hqk=16, Hv=48, d=128, chunk 64, bf16, zero states",
                    "global_batch": 1, "seq_len": pre["tokens"], "parallelism": "single GPU"},
+        "prefill_modes": pre["modes"],
         "roofline": pre["roofline"],
         "decode": decode,
         "cpu_baseline": cpu,

@@ -123,3 +123,43 @@ def test_graph_replay_matches_eager(fused):
             assert np.array_equal(a, b), f"replay {rep}: {name} differs from the eager loop"
         # Eager work between replays.
         (t["z"].float() * 2.0).sum().item()
+
+
+def test_prefill_graph_replay_matches_eager():
+    """The prefill step (prep, chunked delta rule, norm) captured in a HIP
+    graph: every replay equals the eager step bit for bit."""
+    w = wl.custom("prefill", 2, 2, 4, "bf16", seed=313, lengths=[150, 77], s0_std=0.02)
+    x = wl.generate(w)
+    t = {k: P.dev(v) for k, v in x.items()}
+    cfg = B.make_config(w.n_qk_heads, w.n_v_heads, w.act)
+    cu = x["cu_seqlens"]
+    N, T = len(cu) - 1, int(cu[-1])
+    run = Lyr.Prefill(cfg, N, T)
+    conv_out = torch.empty_like(t["conv0"])
+    S_out = torch.empty_like(t["S0"])
+
+    def step():
+        run(t["cu_seqlens"], t["qkv"], t["z"], t["b"], t["a"], t["conv_w"], t["dt_bias"], t["A_log"],
+            t["norm_w"], t["conv0"], conv_out, t["S0"], S_out)
+
+    def state():
+        return P.bits(run.y).copy(), P.bits(S_out).copy(), P.bits(conv_out).copy()
+
+    say("case prefill graph replay: eager")
+    step()
+    torch.cuda.synchronize()
+    ref = state()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        say(f"  replay {rep}")
+        run.y.zero_()
+        S_out.zero_()
+        conv_out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("y", "S", "conv"), state(), ref):
+            assert np.array_equal(a, b), f"replay {rep}: {name} differs from the eager step"
+        (t["z"].float() * 2.0).sum().item()
