@@ -25,6 +25,7 @@ _LIB = os.path.join(_HERE, "libgdn_oracle.so")
 CONV_K = 4
 L2_EPS = 1e-6
 NORM_EPS = 1e-6
+L2_CLAMP, L2_RSQRT = 0, 1   # L2-norm forms of q and k (see conv_gate_prep)
 
 _lib = None
 
@@ -50,7 +51,7 @@ def load(path: Optional[str] = None):
         return _lib
     lib = ctypes.CDLL(path or build())
     lib.gdno_conv_gate_prep.argtypes = [ctypes.c_int, _I, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                        _D, _D, _D, _D, _D, _D, _D, ctypes.c_double,
+                                        _D, _D, _D, _D, _D, _D, _D, ctypes.c_double, ctypes.c_int,
                                         _D, _D, _D, _D, _D, _D]
     lib.gdno_conv_gate_prep.restype = None
     lib.gdno_delta_rule.argtypes = [ctypes.c_int, _I, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -94,8 +95,12 @@ class Oracle:
         return self.lib.gdno_silu(float(x))
 
     def conv_gate_prep(self, cu, n_qk_heads: int, n_v_heads: int, head_dim: int,
-                       qkv, b, a, conv_w, dt_bias, A_log, conv_in, l2_eps: float = L2_EPS):
-        """Conv + SiLU + split + L2 clamp-norm + gates. Returns a dict of fp64 arrays."""
+                       qkv, b, a, conv_w, dt_bias, A_log, conv_in, l2_eps: float = L2_EPS,
+                       l2_mode: int = L2_CLAMP):
+        """Conv + SiLU + split + L2 norm + gates. Returns a dict of fp64 arrays.
+
+        ``l2_mode``: L2_CLAMP (x / max(|x|, eps), the page's form) or L2_RSQRT
+        (x / sqrt(sum x^2 + eps), the HF form the page notes)."""
         cu = _cu(cu)
         N, T = len(cu) - 1, int(cu[-1])
         Hqk, Hv, d = n_qk_heads, n_v_heads, head_dim
@@ -107,7 +112,7 @@ class Oracle:
                    k=np.empty((T, Hqk, d)), v=np.empty((T, Hv, d)),
                    beta=np.empty((T, Hv)), g=np.empty((T, Hv)))
         self.lib.gdno_conv_gate_prep(N, cu.ctypes.data_as(_I), Hqk, Hv, d, _p(qkv), _p(b), _p(a),
-                                     _p(conv_w), _p(dt_bias), _p(A_log), _p(conv_in), float(l2_eps),
+                                     _p(conv_w), _p(dt_bias), _p(A_log), _p(conv_in), float(l2_eps), int(l2_mode),
                                      _p(out["conv_out"]), _p(out["q"]), _p(out["k"]), _p(out["v"]),
                                      _p(out["beta"]), _p(out["g"]))
         return out
@@ -148,10 +153,10 @@ class Oracle:
 
     def layer(self, cu, n_qk_heads: int, n_v_heads: int, head_dim: int, qkv, z, b, a,
               conv_w, dt_bias, A_log, norm_w, conv_in, S_in, heads=None,
-              l2_eps: float = L2_EPS, norm_eps: float = NORM_EPS):
+              l2_eps: float = L2_EPS, norm_eps: float = NORM_EPS, l2_mode: int = L2_CLAMP):
         """The whole mixer: prep, recurrent delta rule, gated RMSNorm. fp64 dict out."""
         r = self.conv_gate_prep(cu, n_qk_heads, n_v_heads, head_dim, qkv, b, a, conv_w,
-                                dt_bias, A_log, conv_in, l2_eps)
+                                dt_bias, A_log, conv_in, l2_eps, l2_mode)
         o, S_out = self.delta_rule(cu, n_qk_heads, n_v_heads, head_dim, r["q"], r["k"], r["v"],
                                    r["beta"], r["g"], S_in, heads=heads)
         T = int(_cu(cu)[-1])

@@ -63,13 +63,15 @@ static double silu(double x) { return x * sigmoid(x); }
  *
  * SiLU runs over all C channels (q and k too) before the split.
  * q_h = y[d*h ..], k_h = y[d*Hqk + d*h ..], v_j = y[2*d*Hqk + d*j ..].
- * q and k are normalised in the clamp form x / max(||x||_2, l2_eps).
+ * q and k are normalised in the clamp form x / max(||x||_2, l2_eps)
+ * (l2_mode 0, the page's canonical form), or, with l2_mode 1, in the form
+ * x / sqrt(sum x^2 + l2_eps) that the page notes for the HF checkpoint.
  * beta = sigmoid(b); g = -exp(A_log) * softplus(a + dt_bias).
  */
 void gdno_conv_gate_prep(int n_seqs, const int *cu, int Hqk, int Hv, int d,
                          const double *qkv, const double *b, const double *a,
                          const double *conv_w, const double *dt_bias, const double *A_log,
-                         const double *conv_in, double l2_eps,
+                         const double *conv_in, double l2_eps, int l2_mode,
                          double *conv_out, double *q, double *k, double *v,
                          double *beta, double *g)
 {
@@ -100,7 +102,8 @@ void gdno_conv_gate_prep(int n_seqs, const int *cu, int Hqk, int Hv, int d,
                     }
                     const double nrm = sqrt(ss);
                     const double den = nrm > l2_eps ? nrm : l2_eps;
-                    for (int i = 0; i < d; ++i) dst[i] /= den;
+                    const double den_hf = sqrt(ss + l2_eps);
+                    for (int i = 0; i < d; ++i) dst[i] /= (l2_mode == 1 ? den_hf : den);
                 }
             }
             for (int jh = 0; jh < Hv; ++jh) {

@@ -194,9 +194,9 @@ def pin_scalar_functions(orc):
     assert orc.sigmoid(-800.0) == 0.0 and orc.sigmoid(800.0) == 1.0
 
 
-def _prep(orc, x, Hqk, Hv, d):
+def _prep(orc, x, Hqk, Hv, d, l2_mode=0):
     return orc.conv_gate_prep(x["cu_seqlens"], Hqk, Hv, d, x["qkv"], x["b"], x["a"], x["conv_w"],
-                              x["dt_bias"], x["A_log"], x["conv0"])
+                              x["dt_bias"], x["A_log"], x["conv0"], l2_mode=l2_mode)
 
 
 def pin_conv_against_library_correlation(orc):
@@ -263,6 +263,36 @@ def pin_l2_clamp(orc):
     _close(r["q"][0, 1], (tiny / 2.0) / 1e-6, 1e-8, "tiny head divided by eps")
     assert abs(np.linalg.norm(r["q"][0, 2]) - 1.0) < 1e-14
     assert np.allclose(np.linalg.norm(r["k"][0], axis=-1), 1.0, atol=1e-14)
+
+
+def pin_l2_rsqrt_form(orc):
+    """The HF form x / sqrt(sum x^2 + 1e-6): zero head -> 0; a head of 8 equal
+    entries s with 8 s^2 = 1e-6 -> every entry s / sqrt(2e-6) = 1/4 exactly
+    (the clamp form would give 1/sqrt(8)); an O(1) head -> x / |x| shrunk by
+    the factor 1 / sqrt(1 + 1e-6 / |x|^2)."""
+    Hqk, Hv, d = 3, 3, 8
+    x = _layer_inputs(93, [1], Hqk, Hv, d)
+    C = d * (2 * Hqk + Hv)
+    x["conv_w"] = np.zeros((C, 4))
+    x["conv_w"][:, 3] = 1.0                       # identity conv, then silu
+    s_target = 1e-3 / math.sqrt(8.0)
+    c = 2.0 * s_target                            # solve silu(c) = s_target by Newton steps
+    for _ in range(60):
+        sg = 1.0 / (1.0 + math.exp(-c))
+        c -= (c * sg - s_target) / (sg + c * sg * (1.0 - sg))
+    x["qkv"][0, 0:d] = 0.0                        # q head 0: zero
+    x["qkv"][0, d:2 * d] = c                      # q head 1: 8 x s_target
+    x["qkv"][0, 2 * d:3 * d] = 3.0                # q head 2: silu(3) each
+    r = _prep(orc, x, Hqk, Hv, d, l2_mode=1)
+    assert np.all(r["q"][0, 0] == 0.0)
+    _close(r["q"][0, 1], np.full(d, 0.25), 1e-12, "8 s with 8 s^2 = eps")
+    s3 = 3.0 / (1.0 + math.exp(-3.0))
+    _close(r["q"][0, 2], np.full(d, s3 / math.sqrt(d * s3 * s3 + 1e-6)), 1e-14, "O(1) head")
+    assert abs(r["q"][0, 2, 0] - 1.0 / math.sqrt(d)) > 1e-9      # eps is felt even here
+    rc = _prep(orc, x, Hqk, Hv, d)
+    _close(rc["q"][0, 1], np.full(d, 1.0 / math.sqrt(d)), 1e-12, "clamp form on the same head")
+    for name in ("v", "beta", "g"):
+        assert np.array_equal(r[name], rc[name]), name
 
 
 def pin_gates(orc):

@@ -37,6 +37,10 @@ MUTANTS = [
      "const double den = sqrt(ss + l2_eps);", False),
     ("l2_eps_on_square", "const double den = nrm > l2_eps ? nrm : l2_eps;",
      "const double den = ss > l2_eps ? nrm : l2_eps;", False),
+    ("l2_rsqrt_eps_outside", "const double den_hf = sqrt(ss + l2_eps);",
+     "const double den_hf = sqrt(ss) + l2_eps;", False),
+    ("l2_rsqrt_no_eps", "const double den_hf = sqrt(ss + l2_eps);", "const double den_hf = sqrt(ss);", False),
+    ("l2_mode_ignored", "dst[i] /= (l2_mode == 1 ? den_hf : den);", "dst[i] /= den;", False),
     ("g_no_dt_bias", "softplus(a[e] + dt_bias[jh])", "softplus(a[e])", False),
     ("g_no_exp", "-exp(A_log[jh]) * softplus", "-A_log[jh] * softplus", False),
     ("softplus_unstable_tail", "log1p(exp(-fabs(x)))", "log1p(exp(-x))", False),
