@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 
 GDN_OK, GDN_E_INVALID_ARG, GDN_E_UNSUPPORTED, GDN_E_HIP, GDN_E_WORKSPACE = 0, 1, 2, 3, 4
 GDN_F32, GDN_BF16 = 0, 1
+GDN_L2_CLAMP, GDN_L2_RSQRT = 0, 1
 HEAD_DIM = 128
 CONV_K = 4
 
@@ -42,7 +43,7 @@ class gdn_config(ctypes.Structure):
     _fields_ = [("n_qk_heads", ctypes.c_int32), ("n_v_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("conv_kernel", ctypes.c_int32),
                 ("l2_eps", ctypes.c_float), ("norm_eps", ctypes.c_float),
-                ("act_dtype", ctypes.c_int)]
+                ("act_dtype", ctypes.c_int), ("l2_mode", ctypes.c_int)]
 
 
 _P = ctypes.c_void_p
@@ -83,11 +84,16 @@ def load(path: Optional[str] = None):
 
 
 def make_config(n_qk_heads: int, n_v_heads: int, act: str = "bf16", l2_eps: float = 1e-6,
-                norm_eps: float = 1e-6, head_dim: int = HEAD_DIM, conv_kernel: int = CONV_K) -> gdn_config:
+                norm_eps: float = 1e-6, head_dim: int = HEAD_DIM, conv_kernel: int = CONV_K,
+                l2_mode: str = "clamp") -> gdn_config:
+    """``l2_mode``: "clamp" (x / max(|x|, eps)) or "rsqrt" (x / sqrt(sum x^2 + eps))."""
+    if l2_mode not in ("clamp", "rsqrt"):
+        raise ValueError(f"l2_mode: {l2_mode!r}, expected 'clamp' or 'rsqrt'")
     c = gdn_config()
     c.n_qk_heads, c.n_v_heads, c.head_dim, c.conv_kernel = n_qk_heads, n_v_heads, head_dim, conv_kernel
     c.l2_eps, c.norm_eps = l2_eps, norm_eps
     c.act_dtype = GDN_BF16 if act == "bf16" else GDN_F32
+    c.l2_mode = GDN_L2_RSQRT if l2_mode == "rsqrt" else GDN_L2_CLAMP
     return c
 
 

@@ -20,6 +20,7 @@ gdn_status check_config(const gdn_config *cfg) {
   if (cfg->n_qk_heads < 1 || cfg->n_v_heads < 1) return GDN_E_INVALID_ARG;
   if (cfg->n_v_heads % cfg->n_qk_heads != 0) return GDN_E_INVALID_ARG;
   if (cfg->act_dtype != GDN_F32 && cfg->act_dtype != GDN_BF16) return GDN_E_INVALID_ARG;
+  if (cfg->l2_mode != GDN_L2_CLAMP && cfg->l2_mode != GDN_L2_RSQRT) return GDN_E_INVALID_ARG;
   if (!finite_nonneg(cfg->l2_eps) || !finite_nonneg(cfg->norm_eps)) return GDN_E_INVALID_ARG;
   if (cfg->head_dim != kHeadDim) return GDN_E_UNSUPPORTED;
   if (cfg->conv_kernel != gdn::kConvK) return GDN_E_UNSUPPORTED;
@@ -69,6 +70,7 @@ gdn_config gdn_default_config(int32_t n_qk_heads, int32_t n_v_heads, gdn_dtype a
   c.l2_eps = 1e-6f;
   c.norm_eps = 1e-6f;
   c.act_dtype = act;
+  c.l2_mode = GDN_L2_CLAMP;
   return c;
 }
 
@@ -136,6 +138,7 @@ gdn_status gdn_conv_gate_prep(const gdn_config *cfg, int32_t n_seqs, int32_t n_t
   p.beta = beta;
   p.g = g;
   p.l2_eps = cfg->l2_eps;
+  p.l2_mode = cfg->l2_mode;
   return launched(gdn::launch_prep(p, cfg->act_dtype, static_cast<hipStream_t>(stream)));
 }
 
@@ -272,6 +275,7 @@ gdn_status gdn_decode_fused(const gdn_config *cfg, int32_t n_seqs, const void *q
   p.S_out = S_out;
   p.y = y;
   p.l2_eps = cfg->l2_eps;
+  p.l2_mode = cfg->l2_mode;
   p.norm_eps = cfg->norm_eps;
   return launched(gdn::launch_decode_fused(p, cfg->act_dtype, static_cast<hipStream_t>(stream)));
 }

@@ -5,7 +5,8 @@
 //
 // Method: the xwen CLAUDE.md page, section "Architecture cheat sheet", gated
 // DeltaNet paragraph: causal depthwise conv (kernel 4, no bias) over the
-// fused stream, SiLU over all of it, q | k | v split, x / max(||x||, eps),
+// fused stream, SiLU over all of it, q | k | v split, x / max(||x||, eps)
+// (or the HF form x / sqrt(sum x^2 + eps) the same paragraph notes, by config),
 // K-head j mod Hqk for V-head j (tiled repeat), beta = sigmoid(b),
 // g = -exp(A_log) softplus(a + dt_bias) (section "GGUF facts that differ
 // from the HF checkpoint" for -exp(A_log) and the multiply-ready norm
@@ -91,7 +92,7 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedDecode
     y1 = siluf_(y1);
     if (wave < 2) {
       const float ss = wave_sum(y0 * y0 + y1 * y1);
-      const float inv = 1.0f / fmaxf(sqrtf(ss), p.l2_eps);
+      const float inv = l2_inv(ss, p.l2_eps, p.l2_mode == GDN_L2_RSQRT);
       y0 *= inv;
       y1 *= inv;
     }

@@ -72,6 +72,12 @@ __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf
 __device__ __forceinline__ float softplusf_(float x) { return fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x))); }
 __device__ __forceinline__ float siluf_(float x) { return x / (1.0f + expf(-x)); }
 
+// 1 / (L2 norm) of a q or k head from its sum of squares: the clamp form
+// 1 / max(sqrt(ss), eps), or with rsqrt_form the form 1 / sqrt(ss + eps).
+__device__ __forceinline__ float l2_inv(float ss, float eps, bool rsqrt_form) {
+  return rsqrt_form ? 1.0f / sqrtf(ss + eps) : 1.0f / fmaxf(sqrtf(ss), eps);
+}
+
 // ------------------------------------------------------ wave primitives
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 

@@ -28,6 +28,7 @@ struct PrepParams {
   void *st_out;
   float *q, *k, *v, *beta, *g;
   float l2_eps;
+  int l2_mode;   // gdn_l2_mode
 };
 hipError_t launch_prep(const PrepParams &p, gdn_dtype act, hipStream_t s);
 
@@ -50,6 +51,7 @@ struct FusedDecodeParams {
   float *S_out;
   void *y;
   float l2_eps, norm_eps;
+  int l2_mode;   // gdn_l2_mode
 };
 hipError_t launch_decode_fused(const FusedDecodeParams &p, gdn_dtype act, hipStream_t s);
 

@@ -3,7 +3,8 @@
 //
 // Method: the xwen CLAUDE.md page, section "Architecture cheat sheet", gated
 // DeltaNet paragraph (conv over the whole fused width, SiLU over all of it,
-// q | k | v split, x / max(||x||, eps), beta = sigmoid, g = ssm_a * softplus
+// q | k | v split, x / max(||x||, eps) (or the HF form x / sqrt(sum x^2 +
+// eps) the same paragraph notes, by config), beta = sigmoid, g = ssm_a * softplus
 // with ssm_a = -exp(A_log) per the section "GGUF facts that differ from the
 // HF checkpoint").
 //
@@ -86,7 +87,7 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void prep_kernel(PrepParams p) 
       y1 = siluf_(y1);
       if (is_qk) {
         const float ss = wave_sum(y0 * y0 + y1 * y1);
-        const float inv = 1.0f / fmaxf(sqrtf(ss), p.l2_eps);
+        const float inv = l2_inv(ss, p.l2_eps, p.l2_mode == GDN_L2_RSQRT);
         y0 *= inv;
         y1 *= inv;
       }

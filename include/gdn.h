@@ -78,6 +78,11 @@ typedef enum {
 
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
 
+/* Form of the q/k L2 norm. GDN_L2_CLAMP is the page's canonical form
+ * x / max(||x||, l2_eps); GDN_L2_RSQRT is x / sqrt(sum x^2 + l2_eps), the form
+ * the page notes for the HF checkpoint (the two differ only near zero). */
+typedef enum { GDN_L2_CLAMP = 0, GDN_L2_RSQRT = 1 } gdn_l2_mode;
+
 typedef void *gdn_stream_t;  /* a hipStream_t */
 
 typedef struct {
@@ -85,13 +90,14 @@ typedef struct {
     int32_t n_v_heads;       /* Hv >= 1, a multiple of Hqk */
     int32_t head_dim;        /* d; only 128 is implemented */
     int32_t conv_kernel;     /* only 4 is implemented */
-    float l2_eps;            /* q/k clamp-form L2 norm epsilon (the page: 1e-6) */
+    float l2_eps;            /* q/k L2 norm epsilon (the page: 1e-6) */
     float norm_eps;          /* gated RMSNorm epsilon (the page: 1e-6) */
     gdn_dtype act_dtype;     /* qkv, logits, conv state, o, z, y */
+    gdn_l2_mode l2_mode;     /* GDN_L2_CLAMP (default) or GDN_L2_RSQRT */
 } gdn_config;
 
 /* A config with the page's values: Hqk, Hv as given, d = 128, kernel 4,
- * both epsilons 1e-6, activations of type `act`. */
+ * both epsilons 1e-6, the clamp-form L2 norm, activations of type `act`. */
 GDN_API gdn_config gdn_default_config(int32_t n_qk_heads, int32_t n_v_heads, gdn_dtype act);
 
 /*

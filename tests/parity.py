@@ -82,15 +82,16 @@ def inputs_f64(x: dict, act: str) -> dict:
     return out
 
 
-def oracle_layer(w: wl.Workload, xf: dict, cu, heads=None):
+def oracle_layer(w: wl.Workload, xf: dict, cu, heads=None, l2_mode: str = "clamp"):
     return oracle.default().layer(cu, w.n_qk_heads, w.n_v_heads, w.head_dim, xf["qkv"], xf["z"], xf["b"],
                                   xf["a"], xf["conv_w"], xf["dt_bias"], xf["A_log"], xf["norm_w"],
-                                  xf["conv0"], xf["S0"], heads=heads)
+                                  xf["conv0"], xf["S0"], heads=heads,
+                                  l2_mode=oracle.L2_RSQRT if l2_mode == "rsqrt" else oracle.L2_CLAMP)
 
 
-def gpu_prefill(w: wl.Workload, x: dict, inplace: bool = False):
+def gpu_prefill(w: wl.Workload, x: dict, inplace: bool = False, l2_mode: str = "clamp"):
     """Run prep -> chunked prefill -> gated RMSNorm on the GPU; host copies of every output."""
-    cfg = B.make_config(w.n_qk_heads, w.n_v_heads, w.act)
+    cfg = B.make_config(w.n_qk_heads, w.n_v_heads, w.act, l2_mode=l2_mode)
     cu = x["cu_seqlens"]
     N, T = len(cu) - 1, int(cu[-1])
     run = Lyr.Prefill(cfg, N, T)
@@ -105,10 +106,10 @@ def gpu_prefill(w: wl.Workload, x: dict, inplace: bool = False):
                 conv_out_bits=bits(conv_out))
 
 
-def gpu_decode(w: wl.Workload, x: dict):
+def gpu_decode(w: wl.Workload, x: dict, l2_mode: str = "clamp"):
     """Run the decode loop (prep -> step -> norm per step) on the GPU.
     Returns y, o [steps, N, Hv, d], final S and conv state."""
-    cfg = B.make_config(w.n_qk_heads, w.n_v_heads, w.act)
+    cfg = B.make_config(w.n_qk_heads, w.n_v_heads, w.act, l2_mode=l2_mode)
     steps, N = x["qkv"].shape[:2]
     run = Lyr.Decode(cfg, N)
     t = {k: dev(v) for k, v in x.items()}
@@ -123,10 +124,10 @@ def gpu_decode(w: wl.Workload, x: dict):
     return dict(y=host(ys), o=host(os_), S_out=host(S), conv_out_bits=bits(conv), conv_out=conv)
 
 
-def gpu_decode_fused(w: wl.Workload, x: dict):
+def gpu_decode_fused(w: wl.Workload, x: dict, l2_mode: str = "clamp"):
     """Run the decode loop as one gdn_decode_fused launch per step on the GPU.
     Returns y [steps, N, Hv, d], final S and conv state."""
-    cfg = B.make_config(w.n_qk_heads, w.n_v_heads, w.act)
+    cfg = B.make_config(w.n_qk_heads, w.n_v_heads, w.act, l2_mode=l2_mode)
     steps, N = x["qkv"].shape[:2]
     t = {k: dev(v) for k, v in x.items()}
     run = Lyr.DecodeFused(cfg, N, t["conv0"].clone())

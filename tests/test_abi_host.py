@@ -155,3 +155,15 @@ def test_decode_fused_validation(lib):
     assert call(1, q) == B.GDN_E_INVALID_ARG
     assert call(1, p, B.make_config(2, 4, head_dim=64)) == B.GDN_E_UNSUPPORTED
     assert lib.gdn_decode_fused(None, 1, *p, None) == B.GDN_E_INVALID_ARG
+
+
+def test_l2_mode_validation(lib):
+    c = lib.gdn_default_config(2, 4, B.GDN_BF16)
+    assert c.l2_mode == B.GDN_L2_CLAMP
+    assert B.make_config(2, 4, l2_mode="rsqrt").l2_mode == B.GDN_L2_RSQRT
+    bad = B.make_config(2, 4)
+    bad.l2_mode = 5
+    p = FAKE[:8]
+    assert lib.gdn_decode_step(ctypes.byref(bad), 1, *p, None) == B.GDN_E_INVALID_ARG
+    with pytest.raises(ValueError):
+        B.make_config(2, 4, l2_mode="hf")

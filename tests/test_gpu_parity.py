@@ -19,12 +19,12 @@ def say(*a):
     sys.stdout.flush()
 
 
-def compare_prefill(w, x, got, heads=None, seqs=None, report=None):
+def compare_prefill(w, x, got, heads=None, seqs=None, report=None, l2_mode="clamp"):
     """Check every output of a prefill run against the oracle (optionally on
     a sample of V-heads and sequences)."""
     xs = P.slice_seqs(x, seqs) if seqs is not None else x
     xf = P.inputs_f64(xs, w.act)
-    ref = P.oracle_layer(w, xf, xs["cu_seqlens"], heads=heads)
+    ref = P.oracle_layer(w, xf, xs["cu_seqlens"], heads=heads, l2_mode=l2_mode)
     cu = x["cu_seqlens"]
     rows = np.concatenate([np.arange(cu[n], cu[n + 1]) for n in (seqs if seqs is not None else range(len(cu) - 1))])
     sn = list(seqs) if seqs is not None else list(range(len(cu) - 1))
@@ -44,11 +44,11 @@ def compare_prefill(w, x, got, heads=None, seqs=None, report=None):
     return rep
 
 
-def compare_decode(w, x, got, seqs=None):
+def compare_decode(w, x, got, seqs=None, l2_mode="clamp"):
     steps, N = x["qkv"].shape[:2]
     seqs = list(range(N)) if seqs is None else list(seqs)
     xp = P.decode_as_packed(x, seqs)
-    ref = P.oracle_layer(w, P.inputs_f64(xp, w.act), xp["cu_seqlens"])
+    ref = P.oracle_layer(w, P.inputs_f64(xp, w.act), xp["cu_seqlens"], l2_mode=l2_mode)
     Hv, d = w.n_v_heads, w.head_dim
     rep = {}
     for name in ("o", "y"):
