@@ -343,7 +343,24 @@ def bench_decode(wid: int, warmup_steps: int = 32, graphs: bool = True):
         reset()
         modes[name] = timed(g.replay)
         del g
-    best = min(modes, key=modes.get)
+    # A 16-token draft block verified in one gdn_decode_verify call per block
+    # (the state and conv state after every token kept as snapshot planes).
+    K = 16
+    if steps % K == 0:
+        cvt = lambda a: a[:steps].reshape((steps // K, K) + a.shape[1:]).transpose(1, 2).contiguous()
+        vq, vz, vb, va = (cvt(t[k]) for k in ("qkv", "z", "b", "a"))           # [blocks][N][K]...
+        conv_snap = torch.empty((N, K) + tuple(t["conv0"].shape[1:]), dtype=t["conv0"].dtype, device="cuda")
+        S_snap = torch.empty((N, K) + tuple(t["S0"].shape[1:]), dtype=torch.float32, device="cuda")
+        vy = torch.empty_like(vz)
+
+        def verify_loop():
+            for blk in range(steps // K):
+                B.gdn_decode_verify(cfg, N, K, vq[blk], vb[blk], va[blk], vz[blk], t["conv_w"], t["dt_bias"],
+                                    t["A_log"], t["norm_w"], t["conv0"], conv_snap, t["S0"], S_snap, vy[blk])
+        verify_loop()
+        torch.cuda.synchronize()
+        modes["verify_k16"] = timed(verify_loop)
+    best = min((m for m in modes if m != "verify_k16"), key=modes.get)
     per = {k: {"us_per_step": round(v * 1e3 / steps, 2), "tokens_per_s": round(N * steps / (v * 1e-3), 1)}
            for k, v in modes.items()}
     step_bytes = decode_step_bytes(w)

@@ -29,7 +29,7 @@ CONV_K = 4
 
 # Every entry point include/gdn.h declares.
 EXPORTS = ("gdn_default_config", "gdn_conv_gate_prep", "gdn_prefill_chunked",
-           "gdn_prefill_workspace_bytes", "gdn_decode_step", "gdn_decode_fused",
+           "gdn_prefill_workspace_bytes", "gdn_decode_step", "gdn_decode_fused", "gdn_decode_verify",
            "gdn_gated_rmsnorm", "gdn_status_string", "gdn_version")
 
 
@@ -76,6 +76,8 @@ def load(path: Optional[str] = None):
     lib.gdn_decode_step.restype = ctypes.c_int
     lib.gdn_decode_fused.argtypes = [cfgp, ctypes.c_int32] + [_P] * 13 + [_P]
     lib.gdn_decode_fused.restype = ctypes.c_int
+    lib.gdn_decode_verify.argtypes = [cfgp, ctypes.c_int32, ctypes.c_int32] + [_P] * 13 + [_P]
+    lib.gdn_decode_verify.restype = ctypes.c_int
     lib.gdn_gated_rmsnorm.argtypes = [cfgp, ctypes.c_int64, _P, _P, _P, _P, _P]
     lib.gdn_gated_rmsnorm.restype = ctypes.c_int
     if path is None:
@@ -197,6 +199,22 @@ def gdn_decode_fused(cfg: gdn_config, n_seqs: int, qkv, beta_logit, alpha_logit,
     _check("gdn_decode_fused", s)
 
 
+def gdn_decode_verify(cfg: gdn_config, n_seqs: int, n_tokens: int, qkv, beta_logit, alpha_logit, z, conv_w,
+                      dt_bias, A_log, norm_w, conv_state_in, conv_snap, S_in, S_snap, y, stream=None):
+    Hqk, Hv, d, N, K = cfg.n_qk_heads, cfg.n_v_heads, cfg.head_dim, n_seqs, n_tokens
+    C, ad = d * (2 * Hqk + Hv), _act_dtype(cfg)
+    s = load().gdn_decode_verify(
+        ctypes.byref(cfg), N, K, _ptr(qkv, "qkv", ad, N * K * C), _ptr(beta_logit, "beta_logit", ad, N * K * Hv),
+        _ptr(alpha_logit, "alpha_logit", ad, N * K * Hv), _ptr(z, "z", ad, N * K * Hv * d),
+        _ptr(conv_w, "conv_w", torch.float32, C * CONV_K), _ptr(dt_bias, "dt_bias", torch.float32, Hv),
+        _ptr(A_log, "A_log", torch.float32, Hv), _ptr(norm_w, "norm_w", torch.float32, d),
+        _ptr(conv_state_in, "conv_state_in", ad, N * (CONV_K - 1) * C),
+        _ptr(conv_snap, "conv_snap", ad, N * K * (CONV_K - 1) * C),
+        _ptr(S_in, "S_in", torch.float32, N * Hv * d * d), _ptr(S_snap, "S_snap", torch.float32, N * K * Hv * d * d),
+        _ptr(y, "y", ad, N * K * Hv * d), _stream(stream))
+    _check("gdn_decode_verify", s)
+
+
 def gdn_gated_rmsnorm(cfg: gdn_config, n_rows: int, o, z, norm_w, y, stream=None):
     d, ad = cfg.head_dim, _act_dtype(cfg)
     s = load().gdn_gated_rmsnorm(
@@ -207,4 +225,4 @@ def gdn_gated_rmsnorm(cfg: gdn_config, n_rows: int, o, z, norm_w, y, stream=None
 
 __all__ = ["load", "make_config", "gdn_config", "GdnError", "status_string", "EXPORTS",
            "gdn_conv_gate_prep", "gdn_prefill_chunked", "gdn_prefill_workspace_bytes",
-           "gdn_decode_step", "gdn_decode_fused", "gdn_gated_rmsnorm", "GDN_F32", "GDN_BF16"]
+           "gdn_decode_step", "gdn_decode_fused", "gdn_decode_verify", "gdn_gated_rmsnorm", "GDN_F32", "GDN_BF16"]

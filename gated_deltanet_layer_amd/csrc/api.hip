@@ -230,35 +230,43 @@ gdn_status gdn_decode_step(const gdn_config *cfg, int32_t n_seqs, const float *q
   return launched(gdn::launch_decode(p, cfg->act_dtype, static_cast<hipStream_t>(stream)));
 }
 
-gdn_status gdn_decode_fused(const gdn_config *cfg, int32_t n_seqs, const void *qkv, const void *beta_logit,
-                            const void *alpha_logit, const void *z, const float *conv_w, const float *dt_bias,
-                            const float *A_log, const float *norm_w, const void *conv_state_in,
-                            void *conv_state_out, const float *S_in, float *S_out, void *y,
-                            gdn_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// gdn_decode_fused (K = 1) and gdn_decode_verify: K tokens per sequence in one
+// launch, the state and conv state after each token to its snapshot plane.
+gdn_status decode_tokens(const gdn_config *cfg, int32_t n_seqs, int32_t K, const void *qkv,
+                         const void *beta_logit, const void *alpha_logit, const void *z, const float *conv_w,
+                         const float *dt_bias, const float *A_log, const float *norm_w,
+                         const void *conv_state_in, void *conv_snap, const float *S_in, float *S_snap,
+                         void *y, gdn_stream_t stream) {
   const gdn_status cs = check_config(cfg);
   if (cs != GDN_OK) return cs;
-  if (n_seqs < 0) return GDN_E_INVALID_ARG;
-  if (n_seqs == 0) return GDN_OK;
+  if (n_seqs < 0 || K < 0) return GDN_E_INVALID_ARG;
+  if (n_seqs == 0 || K == 0) return GDN_OK;
   if (!qkv || !beta_logit || !alpha_logit || !z || !conv_w || !dt_bias || !A_log || !norm_w ||
-      !conv_state_in || !conv_state_out || !S_in || !S_out || !y)
+      !conv_state_in || !conv_snap || !S_in || !S_snap || !y)
     return GDN_E_INVALID_ARG;
   const int Hqk = cfg->n_qk_heads, Hv = cfg->n_v_heads;
   if (static_cast<int64_t>(n_seqs) * Hv > kMaxGrid) return GDN_E_UNSUPPORTED;
-  const size_t N = static_cast<size_t>(n_seqs), as = act_size(cfg);
+  const size_t N = static_cast<size_t>(n_seqs), NK = N * static_cast<size_t>(K), as = act_size(cfg);
   const size_t C = static_cast<size_t>(kHeadDim) * (2 * Hqk + Hv);
-  const size_t sb = N * Hv * kHeadDim * kHeadDim * 4;
-  const size_t st = N * (gdn::kConvK - 1) * C * as;
-  const Range outs[] = {{y, N * Hv * kHeadDim * as}, {conv_state_out, st}};
-  const Range ins[] = {{qkv, N * C * as}, {beta_logit, N * Hv * as}, {alpha_logit, N * Hv * as},
-                       {z, N * Hv * kHeadDim * as}, {conv_w, C * 4 * 4}, {dt_bias, Hv * 4u},
-                       {A_log, Hv * 4u}, {norm_w, kHeadDim * 4u}, {conv_state_in, st}, {S_in, sb}, {S_out, sb}};
+  const size_t sb = N * Hv * kHeadDim * kHeadDim * 4, snap = NK * Hv * kHeadDim * kHeadDim * 4;
+  const size_t st = N * (gdn::kConvK - 1) * C * as, cst = NK * (gdn::kConvK - 1) * C * as;
+  const Range outs[] = {{y, NK * Hv * kHeadDim * as}, {conv_snap, cst}};
+  const Range ins[] = {{qkv, NK * C * as}, {beta_logit, NK * Hv * as}, {alpha_logit, NK * Hv * as},
+                       {z, NK * Hv * kHeadDim * as}, {conv_w, C * 4 * 4}, {dt_bias, Hv * 4u},
+                       {A_log, Hv * 4u}, {norm_w, kHeadDim * 4u}, {conv_state_in, st}, {S_in, sb}, {S_snap, snap}};
   if (any_overlap(outs, ins)) return GDN_E_INVALID_ARG;
-  if (S_in != S_out && overlap(S_in, sb, S_out, sb)) return GDN_E_INVALID_ARG;
+  // A single step may update S in place; K > 1 needs the snapshot planes apart from S_in.
+  if (overlap(S_in, sb, S_snap, snap) && !(K == 1 && S_in == S_snap)) return GDN_E_INVALID_ARG;
   for (size_t i = 0; i < 9; ++i)
-    if (overlap(ins[i].p, ins[i].n, S_out, sb)) return GDN_E_INVALID_ARG;
+    if (overlap(ins[i].p, ins[i].n, S_snap, snap)) return GDN_E_INVALID_ARG;
 
   gdn::FusedDecodeParams p;
   p.n_seqs = n_seqs;
+  p.n_tok = K;
   p.n_qk = Hqk;
   p.n_v = Hv;
   p.qkv = qkv;
@@ -270,14 +278,36 @@ gdn_status gdn_decode_fused(const gdn_config *cfg, int32_t n_seqs, const void *q
   p.A_log = A_log;
   p.norm_w = norm_w;
   p.st_in = conv_state_in;
-  p.st_out = conv_state_out;
+  p.st_out = conv_snap;
   p.S_in = S_in;
-  p.S_out = S_out;
+  p.S_out = S_snap;
   p.y = y;
   p.l2_eps = cfg->l2_eps;
   p.l2_mode = cfg->l2_mode;
   p.norm_eps = cfg->norm_eps;
   return launched(gdn::launch_decode_fused(p, cfg->act_dtype, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_decode_fused(const gdn_config *cfg, int32_t n_seqs, const void *qkv, const void *beta_logit,
+                            const void *alpha_logit, const void *z, const float *conv_w, const float *dt_bias,
+                            const float *A_log, const float *norm_w, const void *conv_state_in,
+                            void *conv_state_out, const float *S_in, float *S_out, void *y,
+                            gdn_stream_t stream) {
+  return decode_tokens(cfg, n_seqs, 1, qkv, beta_logit, alpha_logit, z, conv_w, dt_bias, A_log, norm_w,
+                       conv_state_in, conv_state_out, S_in, S_out, y, stream);
+}
+
+gdn_status gdn_decode_verify(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens, const void *qkv,
+                             const void *beta_logit, const void *alpha_logit, const void *z,
+                             const float *conv_w, const float *dt_bias, const float *A_log,
+                             const float *norm_w, const void *conv_state_in, void *conv_snap,
+                             const float *S_in, float *S_snap, void *y, gdn_stream_t stream) {
+  return decode_tokens(cfg, n_seqs, n_tokens, qkv, beta_logit, alpha_logit, z, conv_w, dt_bias, A_log, norm_w,
+                       conv_state_in, conv_snap, S_in, S_snap, y, stream);
 }
 
 gdn_status gdn_gated_rmsnorm(const gdn_config *cfg, int64_t n_rows, const void *o, const void *z,

@@ -40,8 +40,11 @@ constexpr int kFusedWaves = kFusedThreads / kWave;
 constexpr int kRowsPerThread = 8;
 constexpr int kColQuads = kHeadDim / 4;   // 32 lanes span a row
 
-template <typename TA>
-__global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedDecodeParams p) {
+// kOne: a single token per sequence (gdn_decode_fused), with K = 1 known at
+// compile time so that the step keeps the register budget of six waves per
+// SIMD.
+template <typename TA, bool kOne>
+__global__ __launch_bounds__(kFusedThreads) void decode_tokens_kernel(FusedDecodeParams p) {
   __shared__ __attribute__((aligned(16))) float qs[kHeadDim];
   __shared__ __attribute__((aligned(16))) float ks[kHeadDim];
   __shared__ __attribute__((aligned(16))) float vs[kHeadDim];
@@ -55,138 +58,151 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedDecode
   const int j = blockIdx.x % p.n_v;
   const int n = blockIdx.x / p.n_v;
   const int hk = j % p.n_qk;
+  const int K = kOne ? 1 : p.n_tok;
   const int cq = tid % kColQuads;
   const int row0 = kRowsPerThread * (tid / kColQuads);
   const int col0 = 4 * cq;
-
-  // 1. The state rows of this thread (in flight during the token's prep).
-  const size_t sbase = (static_cast<size_t>(n) * p.n_v + j) * kHeadDim * kHeadDim;
-  float4 S[kRowsPerThread];
-#pragma unroll
-  for (int r = 0; r < kRowsPerThread; ++r)
-    S[r] = *reinterpret_cast<const float4 *>(p.S_in + sbase + (row0 + r) * kHeadDim + col0);
-
-  const size_t e = static_cast<size_t>(n) * p.n_v + j;
-  float4 zv = make_float4(0.f, 0.f, 0.f, 0.f), wv = zv;
-  if (wave == 0) {
-    zv = Act<TA>::load4(static_cast<const TA *>(p.z), e * kHeadDim + col0);
-    wv = *reinterpret_cast<const float4 *>(p.norm_w + col0);
-  }
-
-  // 2. The token's q (wave 0), k (wave 1), v (wave 2); gates (wave 3).
+  const size_t hd2 = static_cast<size_t>(kHeadDim) * kHeadDim;
   const int C = kHeadDim * (2 * p.n_qk + p.n_v);
-  if (wave < 3) {
-    const int hb = wave == 0 ? hk : (wave == 1 ? p.n_qk + hk : 2 * p.n_qk + j);
-    const int c = hb * kHeadDim + 2 * lane;
-    const TA *st = static_cast<const TA *>(p.st_in) + static_cast<size_t>(n) * (kConvK - 1) * C;
-    const TA *x = static_cast<const TA *>(p.qkv) + static_cast<size_t>(n) * C;
-    const float2 x0 = Act<TA>::load2(st, c);
-    const float2 x1 = Act<TA>::load2(st, c + C);
-    const float2 x2 = Act<TA>::load2(st, c + 2 * C);
-    const float2 x3 = Act<TA>::load2(x, c);
-    const float4 w0 = reinterpret_cast<const float4 *>(p.conv_w)[c];
-    const float4 w1 = reinterpret_cast<const float4 *>(p.conv_w)[c + 1];
-    float y0 = w0.x * x0.x + w0.y * x1.x + w0.z * x2.x + w0.w * x3.x;
-    float y1 = w1.x * x0.y + w1.y * x1.y + w1.z * x2.y + w1.w * x3.y;
-    y0 = siluf_(y0);
-    y1 = siluf_(y1);
-    if (wave < 2) {
-      const float ss = wave_sum(y0 * y0 + y1 * y1);
-      const float inv = l2_inv(ss, p.l2_eps, p.l2_mode == GDN_L2_RSQRT);
-      y0 *= inv;
-      y1 *= inv;
+
+  // 1. The state rows of this thread (in flight during the first token's prep).
+  float4 S[kRowsPerThread];
+  {
+    const float *Sin = p.S_in + (static_cast<size_t>(n) * p.n_v + j) * hd2;
+#pragma unroll
+    for (int r = 0; r < kRowsPerThread; ++r)
+      S[r] = *reinterpret_cast<const float4 *>(Sin + (row0 + r) * kHeadDim + col0);
+  }
+
+  for (int tau = 0; tau < K; ++tau) {
+    const size_t tok = static_cast<size_t>(n) * K + tau;      // row of qkv, z, y, logits
+    const size_t e = tok * p.n_v + j;
+    const int plane = K - 1 - tau;                             // snapshot plane (most recent first)
+    if (tau > 0) __syncthreads();                              // the last token's LDS reads are done
+    float4 zv = make_float4(0.f, 0.f, 0.f, 0.f), wv = zv;
+    if (wave == 0) {
+      zv = Act<TA>::load4(static_cast<const TA *>(p.z), e * kHeadDim + col0);
+      wv = *reinterpret_cast<const float4 *>(p.norm_w + col0);
     }
-    float *dst = wave == 0 ? qs : (wave == 1 ? ks : vs);
-    *reinterpret_cast<float2 *>(dst + 2 * lane) = make_float2(y0, y1);
-    // New conv state: old rows 1, 2 and the token.
-    if (wave == 2 || j == hk) {
-      TA *so = static_cast<TA *>(p.st_out) + static_cast<size_t>(n) * (kConvK - 1) * C;
-      Act<TA>::store2(so, c, x1);
-      Act<TA>::store2(so, c + C, x2);
-      Act<TA>::store2(so, c + 2 * C, x3);
+
+    // 2. The token's q (wave 0), k (wave 1), v (wave 2); gates (wave 3).
+    if (wave < 3) {
+      const int hb = wave == 0 ? hk : (wave == 1 ? p.n_qk + hk : 2 * p.n_qk + j);
+      const int c = hb * kHeadDim + 2 * lane;
+      // Rows tau-3 .. tau of [conv state; the sequence's tokens].
+      const TA *st = static_cast<const TA *>(p.st_in) + static_cast<size_t>(n) * (kConvK - 1) * C;
+      const TA *xq = static_cast<const TA *>(p.qkv) + static_cast<size_t>(n) * K * C;
+      float2 xr[kConvK];
+#pragma unroll
+      for (int i = 0; i < kConvK; ++i) {
+        const int r = tau - (kConvK - 1) + i;
+        xr[i] = r < 0 ? Act<TA>::load2(st, static_cast<size_t>(kConvK - 1 + r) * C + c)
+                      : Act<TA>::load2(xq, static_cast<size_t>(r) * C + c);
+      }
+      const float4 w0 = reinterpret_cast<const float4 *>(p.conv_w)[c];
+      const float4 w1 = reinterpret_cast<const float4 *>(p.conv_w)[c + 1];
+      float y0 = w0.x * xr[0].x + w0.y * xr[1].x + w0.z * xr[2].x + w0.w * xr[3].x;
+      float y1 = w1.x * xr[0].y + w1.y * xr[1].y + w1.z * xr[2].y + w1.w * xr[3].y;
+      y0 = siluf_(y0);
+      y1 = siluf_(y1);
+      if (wave < 2) {
+        const float ss = wave_sum(y0 * y0 + y1 * y1);
+        const float inv = l2_inv(ss, p.l2_eps, p.l2_mode == GDN_L2_RSQRT);
+        y0 *= inv;
+        y1 *= inv;
+      }
+      float *dst = wave == 0 ? qs : (wave == 1 ? ks : vs);
+      *reinterpret_cast<float2 *>(dst + 2 * lane) = make_float2(y0, y1);
+      // Conv state after this token: rows tau-2, tau-1, tau.
+      if (wave == 2 || j == hk) {
+        TA *so = static_cast<TA *>(p.st_out) + (static_cast<size_t>(n) * K + plane) * (kConvK - 1) * C;
+        Act<TA>::store2(so, c, xr[1]);
+        Act<TA>::store2(so, c + C, xr[2]);
+        Act<TA>::store2(so, c + 2 * C, xr[3]);
+      }
+    } else if (tid == 3 * kWave) {
+      gate[0] = sigmoidf_(Act<TA>::load(static_cast<const TA *>(p.b), e));
+      gate[1] = -expf(p.A_log[j]) * softplusf_(Act<TA>::load(static_cast<const TA *>(p.a), e) + p.dt_bias[j]);
     }
-  } else if (tid == 3 * kWave) {
-    gate[0] = sigmoidf_(Act<TA>::load(static_cast<const TA *>(p.b), e));
-    gate[1] = -expf(p.A_log[j]) * softplusf_(Act<TA>::load(static_cast<const TA *>(p.a), e) + p.dt_bias[j]);
-  }
-  __syncthreads();
+    __syncthreads();
 
-  // 3. Column sums S^T k, S^T q over this thread's rows, and k.q.
-  float kr[kRowsPerThread], qr[kRowsPerThread];
+    // 3. Column sums S^T k, S^T q over this thread's rows, and k.q.
+    float kr[kRowsPerThread], qr[kRowsPerThread];
 #pragma unroll
-  for (int h = 0; h < kRowsPerThread / 4; ++h) {
-    const float4 k4 = *reinterpret_cast<const float4 *>(ks + row0 + 4 * h);
-    const float4 q4 = *reinterpret_cast<const float4 *>(qs + row0 + 4 * h);
-    kr[4 * h] = k4.x; kr[4 * h + 1] = k4.y; kr[4 * h + 2] = k4.z; kr[4 * h + 3] = k4.w;
-    qr[4 * h] = q4.x; qr[4 * h + 1] = q4.y; qr[4 * h + 2] = q4.z; qr[4 * h + 3] = q4.w;
-  }
-  float part[9];
+    for (int h = 0; h < kRowsPerThread / 4; ++h) {
+      const float4 k4 = *reinterpret_cast<const float4 *>(ks + row0 + 4 * h);
+      const float4 q4 = *reinterpret_cast<const float4 *>(qs + row0 + 4 * h);
+      kr[4 * h] = k4.x; kr[4 * h + 1] = k4.y; kr[4 * h + 2] = k4.z; kr[4 * h + 3] = k4.w;
+      qr[4 * h] = q4.x; qr[4 * h + 1] = q4.y; qr[4 * h + 2] = q4.z; qr[4 * h + 3] = q4.w;
+    }
+    float part[9];
 #pragma unroll
-  for (int i = 0; i < 9; ++i) part[i] = 0.0f;
+    for (int i = 0; i < 9; ++i) part[i] = 0.0f;
 #pragma unroll
-  for (int r = 0; r < kRowsPerThread; ++r) {
-    part[0] += S[r].x * kr[r]; part[1] += S[r].y * kr[r];
-    part[2] += S[r].z * kr[r]; part[3] += S[r].w * kr[r];
-    part[4] += S[r].x * qr[r]; part[5] += S[r].y * qr[r];
-    part[6] += S[r].z * qr[r]; part[7] += S[r].w * qr[r];
-    part[8] += kr[r] * qr[r];
-  }
-  // The two row groups of a wave (lanes l and l + 32 share columns), then
-  // the waves through LDS.
+    for (int r = 0; r < kRowsPerThread; ++r) {
+      part[0] += S[r].x * kr[r]; part[1] += S[r].y * kr[r];
+      part[2] += S[r].z * kr[r]; part[3] += S[r].w * kr[r];
+      part[4] += S[r].x * qr[r]; part[5] += S[r].y * qr[r];
+      part[6] += S[r].z * qr[r]; part[7] += S[r].w * qr[r];
+      part[8] += kr[r] * qr[r];
+    }
+    // The two row groups of a wave (lanes l and l + 32 share columns), then
+    // the waves through LDS.
 #pragma unroll
-  for (int i = 0; i < 9; ++i) part[i] += __shfl_xor(part[i], 32, kWave);
-  if (lane < kColQuads) {
-#pragma unroll
-    for (int i = 0; i < 9; ++i) red[wave][i][cq] = part[i];
-  }
-  __syncthreads();
-  if (tid < 9 * kColQuads) {
-    const int i = tid / kColQuads, c = tid % kColQuads;
-    float s = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kFusedWaves; ++w) s += red[w][i][c];
-    tot[i][c] = s;
-  }
-  __syncthreads();
-
-  // 4. Delta, readout, state update.
-  const float bt = gate[0];
-  const float eg = expf(gate[1]);
-  const float kq = tot[8][cq];
-  const float4 v4 = *reinterpret_cast<const float4 *>(vs + col0);
-  const float vc[4] = {v4.x, v4.y, v4.z, v4.w};
-  const float scale = 0.08838834764831845f;  // 1/sqrt(128)
-  float d[4], o[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    d[c] = bt * (vc[c] - eg * tot[c][cq]);
-    o[c] = scale * (eg * tot[4 + c][cq] + kq * d[c]);
-  }
-  float *Sout = p.S_out + sbase;
-#pragma unroll
-  for (int r = 0; r < kRowsPerThread; ++r) {
-    float4 w;
-    w.x = eg * S[r].x + kr[r] * d[0];
-    w.y = eg * S[r].y + kr[r] * d[1];
-    w.z = eg * S[r].z + kr[r] * d[2];
-    w.w = eg * S[r].w + kr[r] * d[3];
-    *reinterpret_cast<float4 *>(Sout + (row0 + r) * kHeadDim + col0) = w;
-  }
-
-  // 5. Gated RMSNorm of the 128 readout values: each 32-lane half of wave 0
-  // holds all of them (4 per lane).
-  if (wave == 0) {
-    float ss = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
-    ss = row16_sum(ss);
-    ss += __shfl_xor(ss, 16, kWave);
-    const float inv = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + p.norm_eps);
+    for (int i = 0; i < 9; ++i) part[i] += __shfl_xor(part[i], 32, kWave);
     if (lane < kColQuads) {
-      float4 y;
-      y.x = o[0] * inv * wv.x * siluf_(zv.x);
-      y.y = o[1] * inv * wv.y * siluf_(zv.y);
-      y.z = o[2] * inv * wv.z * siluf_(zv.z);
-      y.w = o[3] * inv * wv.w * siluf_(zv.w);
-      Act<TA>::store4(static_cast<TA *>(p.y), e * kHeadDim + col0, y);
+#pragma unroll
+      for (int i = 0; i < 9; ++i) red[wave][i][cq] = part[i];
+    }
+    __syncthreads();
+    if (tid < 9 * kColQuads) {
+      const int i = tid / kColQuads, c = tid % kColQuads;
+      float s = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kFusedWaves; ++w) s += red[w][i][c];
+      tot[i][c] = s;
+    }
+    __syncthreads();
+
+    // 4. Delta, readout, state update; the updated state is this token's
+    // snapshot plane.
+    const float bt = gate[0];
+    const float eg = expf(gate[1]);
+    const float kq = tot[8][cq];
+    const float4 v4 = *reinterpret_cast<const float4 *>(vs + col0);
+    const float vc[4] = {v4.x, v4.y, v4.z, v4.w};
+    const float scale = 0.08838834764831845f;  // 1/sqrt(128)
+    float d[4], o[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      d[c] = bt * (vc[c] - eg * tot[c][cq]);
+      o[c] = scale * (eg * tot[4 + c][cq] + kq * d[c]);
+    }
+    float *Sout = p.S_out + ((static_cast<size_t>(n) * K + plane) * p.n_v + j) * hd2;
+#pragma unroll
+    for (int r = 0; r < kRowsPerThread; ++r) {
+      S[r].x = eg * S[r].x + kr[r] * d[0];
+      S[r].y = eg * S[r].y + kr[r] * d[1];
+      S[r].z = eg * S[r].z + kr[r] * d[2];
+      S[r].w = eg * S[r].w + kr[r] * d[3];
+      *reinterpret_cast<float4 *>(Sout + (row0 + r) * kHeadDim + col0) = S[r];
+    }
+
+    // 5. Gated RMSNorm of the 128 readout values: each 32-lane half of wave 0
+    // holds all of them (4 per lane).
+    if (wave == 0) {
+      float ss = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
+      ss = row16_sum(ss);
+      ss += __shfl_xor(ss, 16, kWave);
+      const float inv = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + p.norm_eps);
+      if (lane < kColQuads) {
+        float4 y;
+        y.x = o[0] * inv * wv.x * siluf_(zv.x);
+        y.y = o[1] * inv * wv.y * siluf_(zv.y);
+        y.z = o[2] * inv * wv.z * siluf_(zv.z);
+        y.w = o[3] * inv * wv.w * siluf_(zv.w);
+        Act<TA>::store4(static_cast<TA *>(p.y), e * kHeadDim + col0, y);
+      }
     }
   }
 }
@@ -195,10 +211,18 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedDecode
 
 hipError_t launch_decode_fused(const FusedDecodeParams &p, gdn_dtype act, hipStream_t s) {
   const int64_t blocks = static_cast<int64_t>(p.n_seqs) * p.n_v;
-  if (act == GDN_BF16)
-    hipLaunchKernelGGL(decode_fused_kernel<bf16_t>, dim3(static_cast<unsigned>(blocks)), dim3(kFusedThreads), 0, s, p);
-  else
-    hipLaunchKernelGGL(decode_fused_kernel<float>, dim3(static_cast<unsigned>(blocks)), dim3(kFusedThreads), 0, s, p);
+  const dim3 grid(static_cast<unsigned>(blocks)), block(kFusedThreads);
+  if (act == GDN_BF16) {
+    if (p.n_tok == 1)
+      hipLaunchKernelGGL((decode_tokens_kernel<bf16_t, true>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((decode_tokens_kernel<bf16_t, false>), grid, block, 0, s, p);
+  } else {
+    if (p.n_tok == 1)
+      hipLaunchKernelGGL((decode_tokens_kernel<float, true>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((decode_tokens_kernel<float, false>), grid, block, 0, s, p);
+  }
   return hipGetLastError();
 }
 

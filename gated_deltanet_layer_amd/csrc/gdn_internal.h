@@ -41,8 +41,11 @@ struct DecodeParams {
 };
 hipError_t launch_decode(const DecodeParams &p, gdn_dtype act, hipStream_t s);
 
+// n_tok tokens per sequence ([N][n_tok] rows of qkv, z, y, logits); the
+// state and conv state after token t go to plane n_tok - 1 - t of S_out and
+// st_out (most recent first; n_tok = 1 is a plain decode step).
 struct FusedDecodeParams {
-  int n_seqs, n_qk, n_v;
+  int n_seqs, n_tok, n_qk, n_v;
   const void *qkv, *b, *a, *z;
   const float *conv_w, *dt_bias, *A_log, *norm_w;
   const void *st_in;

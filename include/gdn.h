@@ -180,6 +180,30 @@ GDN_API gdn_status gdn_decode_fused(const gdn_config *cfg, int32_t n_seqs, const
                             const float *S_in, float *S_out, void *y, gdn_stream_t stream);
 
 /*
+ * gdn_decode_verify -- K = n_tokens consecutive tokens for each of n_seqs
+ * sequences in one launch (a draft block under speculative decoding), with
+ * the recurrent state and the conv state after EVERY token kept as snapshot
+ * planes, most recent first, so that a caller that accepts only the first a
+ * tokens resumes from plane K - a without recomputing (plane 0 is the state
+ * after all K tokens). The arithmetic per token is that of gdn_decode_fused
+ * (the page's section "Architecture cheat sheet", gated DeltaNet paragraph;
+ * the page's speculative-decoding notes keep per-token state planes in this
+ * most-recent-first order for the verify walk's rollback).
+ *   qkv [N][K][C], beta_logit, alpha_logit [N][K][Hv], z, y [N][K][Hv][d]
+ *   conv_state_in [N][3][C]           the state before the first token
+ *   conv_snap [N][K][3][C]            plane p = conv state after token K-1-p
+ *   S_in [N][Hv][d][d]                the state before the first token
+ *   S_snap [N][K][Hv][d][d]           plane p = S after token K-1-p
+ * conv_snap must not overlap conv_state_in; S_snap must not overlap S_in
+ * (K = 1 may update S in place). n_seqs or n_tokens may be 0.
+ */
+GDN_API gdn_status gdn_decode_verify(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens, const void *qkv,
+                             const void *beta_logit, const void *alpha_logit, const void *z,
+                             const float *conv_w, const float *dt_bias, const float *A_log,
+                             const float *norm_w, const void *conv_state_in, void *conv_snap,
+                             const float *S_in, float *S_snap, void *y, gdn_stream_t stream);
+
+/*
  * gdn_gated_rmsnorm -- per row of d values (n_rows = T * Hv):
  *   y = o / sqrt(mean(o^2) + norm_eps) * norm_w * silu(z)
  * with norm_w [d] fp32 shared by all heads and used as stored (no +1).

@@ -167,3 +167,21 @@ def test_l2_mode_validation(lib):
     assert lib.gdn_decode_step(ctypes.byref(bad), 1, *p, None) == B.GDN_E_INVALID_ARG
     with pytest.raises(ValueError):
         B.make_config(2, 4, l2_mode="hf")
+
+
+def test_decode_verify_validation(lib):
+    cfg = B.make_config(2, 4)
+    p = FAKE[:13]   # qkv, b, a, z, conv_w, dt_bias, A_log, norm_w, conv_in, conv_snap, S_in, S_snap, y
+    call = lambda n, k, ptrs: lib.gdn_decode_verify(ctypes.byref(cfg), n, k, *ptrs, None)
+    assert call(0, 4, p) == B.GDN_OK
+    assert call(2, 0, p) == B.GDN_OK
+    assert call(2, -1, p) == B.GDN_E_INVALID_ARG
+    q = p[:]
+    q[11] = q[10]               # snapshot planes on top of S_in with K > 1
+    assert call(1, 2, q) == B.GDN_E_INVALID_ARG
+    q = p[:]
+    q[9] = q[8]                 # conv snapshots on top of the old conv state
+    assert call(1, 3, q) == B.GDN_E_INVALID_ARG
+    q = p[:]
+    q[3] = None
+    assert call(1, 3, q) == B.GDN_E_INVALID_ARG
