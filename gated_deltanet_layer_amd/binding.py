@@ -30,7 +30,8 @@ CONV_K = 4
 # Every entry point include/gdn.h declares.
 EXPORTS = ("gdn_default_config", "gdn_conv_gate_prep", "gdn_prefill_chunked",
            "gdn_prefill_workspace_bytes", "gdn_decode_step", "gdn_decode_fused", "gdn_decode_verify",
-           "gdn_gated_rmsnorm", "gdn_status_string", "gdn_version")
+           "gdn_gated_rmsnorm", "gdn_prefill_chunked_ckpt", "gdn_conv_state_ckpt", "gdn_state_check",
+           "gdn_status_string", "gdn_version")
 
 
 class GdnError(RuntimeError):
@@ -70,6 +71,14 @@ def load(path: Optional[str] = None):
     lib.gdn_conv_gate_prep.restype = ctypes.c_int
     lib.gdn_prefill_chunked.argtypes = [cfgp, ctypes.c_int32, ctypes.c_int32] + [_P] * 10 + [ctypes.c_size_t, _P]
     lib.gdn_prefill_chunked.restype = ctypes.c_int
+    lib.gdn_prefill_chunked_ckpt.argtypes = ([cfgp, ctypes.c_int32, ctypes.c_int32] + [_P] * 9
+                                             + [ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_size_t, _P])
+    lib.gdn_prefill_chunked_ckpt.restype = ctypes.c_int
+    lib.gdn_conv_state_ckpt.argtypes = [cfgp, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, ctypes.c_int32,
+                                        ctypes.c_int32, _P, _P]
+    lib.gdn_conv_state_ckpt.restype = ctypes.c_int
+    lib.gdn_state_check.argtypes = [_P, ctypes.c_int64, _P, _P]
+    lib.gdn_state_check.restype = ctypes.c_int
     lib.gdn_prefill_workspace_bytes.argtypes = [cfgp, ctypes.c_int32, ctypes.c_int32]
     lib.gdn_prefill_workspace_bytes.restype = ctypes.c_size_t
     lib.gdn_decode_step.argtypes = [cfgp, ctypes.c_int32] + [_P] * 8 + [_P]
@@ -172,6 +181,41 @@ def gdn_prefill_chunked(cfg: gdn_config, n_seqs: int, n_tokens: int, cu_seqlens,
     _check("gdn_prefill_chunked", s)
 
 
+def gdn_prefill_chunked_ckpt(cfg: gdn_config, n_seqs: int, n_tokens: int, cu_seqlens, q, k, v, beta, g,
+                             S_in, S_out, o, ckpt_every: int, ckpt_cap: int, S_ckpt, workspace, stream=None):
+    Hqk, Hv, d = cfg.n_qk_heads, cfg.n_v_heads, cfg.head_dim
+    T, N = n_tokens, n_seqs
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    s = load().gdn_prefill_chunked_ckpt(
+        ctypes.byref(cfg), N, T, _ptr(cu_seqlens, "cu_seqlens", torch.int32, N + 1),
+        _ptr(q, "q", torch.float32, T * Hqk * d), _ptr(k, "k", torch.float32, T * Hqk * d),
+        _ptr(v, "v", torch.float32, T * Hv * d), _ptr(beta, "beta", torch.float32, T * Hv),
+        _ptr(g, "g", torch.float32, T * Hv), _ptr(S_in, "S_in", torch.float32, N * Hv * d * d),
+        _ptr(S_out, "S_out", torch.float32, N * Hv * d * d), _ptr(o, "o", _act_dtype(cfg), T * Hv * d),
+        ckpt_every, ckpt_cap, _ptr(S_ckpt, "S_ckpt", torch.float32, N * ckpt_cap * Hv * d * d),
+        _ptr(workspace, "workspace"), ws_bytes, _stream(stream))
+    _check("gdn_prefill_chunked_ckpt", s)
+
+
+def gdn_conv_state_ckpt(cfg: gdn_config, n_seqs: int, n_tokens: int, cu_seqlens, qkv, conv_state_in,
+                        ckpt_every: int, ckpt_cap: int, conv_ckpt, stream=None):
+    Hqk, Hv, d = cfg.n_qk_heads, cfg.n_v_heads, cfg.head_dim
+    C, ad, N, T = d * (2 * Hqk + Hv), _act_dtype(cfg), n_seqs, n_tokens
+    s = load().gdn_conv_state_ckpt(
+        ctypes.byref(cfg), N, T, _ptr(cu_seqlens, "cu_seqlens", torch.int32, N + 1), _ptr(qkv, "qkv", ad, T * C),
+        _ptr(conv_state_in, "conv_state_in", ad, N * (CONV_K - 1) * C), ckpt_every, ckpt_cap,
+        _ptr(conv_ckpt, "conv_ckpt", ad, N * ckpt_cap * (CONV_K - 1) * C), _stream(stream))
+    _check("gdn_conv_state_ckpt", s)
+
+
+def gdn_state_check(S, stats, stream=None):
+    """Non-finite guard: stats (int32[2] on the GPU) <- [count of NaN/Inf in S,
+    bits of max |x| over the finite values]."""
+    s = load().gdn_state_check(_ptr(S, "S", torch.float32), S.numel(), _ptr(stats, "stats", torch.int32, 2),
+                               _stream(stream))
+    _check("gdn_state_check", s)
+
+
 def gdn_decode_step(cfg: gdn_config, n_seqs: int, q, k, v, beta, g, S_in, S_out, o, stream=None):
     Hqk, Hv, d, N = cfg.n_qk_heads, cfg.n_v_heads, cfg.head_dim, n_seqs
     s = load().gdn_decode_step(
@@ -225,4 +269,5 @@ def gdn_gated_rmsnorm(cfg: gdn_config, n_rows: int, o, z, norm_w, y, stream=None
 
 __all__ = ["load", "make_config", "gdn_config", "GdnError", "status_string", "EXPORTS",
            "gdn_conv_gate_prep", "gdn_prefill_chunked", "gdn_prefill_workspace_bytes",
-           "gdn_decode_step", "gdn_decode_fused", "gdn_decode_verify", "gdn_gated_rmsnorm", "GDN_F32", "GDN_BF16"]
+           "gdn_decode_step", "gdn_decode_fused", "gdn_decode_verify", "gdn_gated_rmsnorm",
+           "gdn_prefill_chunked_ckpt", "gdn_conv_state_ckpt", "gdn_state_check", "GDN_F32", "GDN_BF16"]

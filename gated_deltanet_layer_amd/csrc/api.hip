@@ -148,16 +148,20 @@ size_t gdn_prefill_workspace_bytes(const gdn_config *cfg, int32_t n_seqs, int32_
   return gdn::prefill_workspace_bytes(n_seqs, n_tokens, cfg->n_qk_heads, cfg->n_v_heads);
 }
 
-gdn_status gdn_prefill_chunked(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens,
-                               const int32_t *cu_seqlens, const float *q, const float *k, const float *v,
-                               const float *beta, const float *g, const float *S_in, float *S_out, void *o,
-                               void *workspace, size_t workspace_bytes, gdn_stream_t stream) {
+gdn_status gdn_prefill_chunked_ckpt(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens,
+                                    const int32_t *cu_seqlens, const float *q, const float *k, const float *v,
+                                    const float *beta, const float *g, const float *S_in, float *S_out, void *o,
+                                    int32_t ckpt_every, int32_t ckpt_cap, float *S_ckpt,
+                                    void *workspace, size_t workspace_bytes, gdn_stream_t stream) {
   const gdn_status cs = check_config(cfg);
   if (cs != GDN_OK) return cs;
   if (n_seqs < 0 || n_tokens < 0) return GDN_E_INVALID_ARG;
   if (n_seqs == 0) return n_tokens == 0 ? GDN_OK : GDN_E_INVALID_ARG;
   if (!cu_seqlens || !S_in || !S_out) return GDN_E_INVALID_ARG;
   if (n_tokens > 0 && (!q || !k || !v || !beta || !g || !o)) return GDN_E_INVALID_ARG;
+  if (ckpt_every < 0 || ckpt_cap < 0 || ckpt_every % gdn::kChunk != 0) return GDN_E_INVALID_ARG;
+  const bool ckpt = ckpt_every > 0 && ckpt_cap > 0;
+  if (ckpt && !S_ckpt) return GDN_E_INVALID_ARG;
   const int Hqk = cfg->n_qk_heads, Hv = cfg->n_v_heads;
   const size_t need = gdn_prefill_workspace_bytes(cfg, n_seqs, n_tokens);
   if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_E_WORKSPACE;
@@ -175,6 +179,13 @@ gdn_status gdn_prefill_chunked(const gdn_config *cfg, int32_t n_seqs, int32_t n_
   if (S_in != S_out && overlap(S_in, sb, S_out, sb)) return GDN_E_INVALID_ARG;
   for (size_t i = 0; i < 6; ++i)
     if (overlap(ins[i].p, ins[i].n, S_out, sb)) return GDN_E_INVALID_ARG;
+  if (ckpt) {
+    const size_t cb = static_cast<size_t>(n_seqs) * ckpt_cap * Hv * kHeadDim * kHeadDim * 4;
+    for (const Range &r : ins)
+      if (overlap(r.p, r.n, S_ckpt, cb)) return GDN_E_INVALID_ARG;
+    if (overlap(o, T * Hv * kHeadDim * act_size(cfg), S_ckpt, cb) || overlap(workspace, need, S_ckpt, cb))
+      return GDN_E_INVALID_ARG;
+  }
 
   gdn::PrefillParams p;
   p.cu = cu_seqlens;
@@ -192,7 +203,56 @@ gdn_status gdn_prefill_chunked(const gdn_config *cfg, int32_t n_seqs, int32_t n_
   p.o = o;
   p.ws = workspace;
   p.ws_bytes = workspace_bytes;
+  p.S_ckpt = ckpt ? S_ckpt : nullptr;
+  p.ckpt_chunks = ckpt ? ckpt_every / gdn::kChunk : 0;
+  p.ckpt_cap = ckpt ? ckpt_cap : 0;
   return launched(gdn::launch_prefill(p, cfg->act_dtype, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_prefill_chunked(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens,
+                               const int32_t *cu_seqlens, const float *q, const float *k, const float *v,
+                               const float *beta, const float *g, const float *S_in, float *S_out, void *o,
+                               void *workspace, size_t workspace_bytes, gdn_stream_t stream) {
+  return gdn_prefill_chunked_ckpt(cfg, n_seqs, n_tokens, cu_seqlens, q, k, v, beta, g, S_in, S_out, o, 0, 0,
+                                  nullptr, workspace, workspace_bytes, stream);
+}
+
+gdn_status gdn_conv_state_ckpt(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens, const int32_t *cu_seqlens,
+                               const void *qkv, const void *conv_state_in, int32_t ckpt_every, int32_t ckpt_cap,
+                               void *conv_ckpt, gdn_stream_t stream) {
+  const gdn_status cs = check_config(cfg);
+  if (cs != GDN_OK) return cs;
+  if (n_seqs < 0 || n_tokens < 0 || ckpt_every < 1 || ckpt_cap < 0) return GDN_E_INVALID_ARG;
+  if (n_seqs == 0 || ckpt_cap == 0) return GDN_OK;
+  if (!cu_seqlens || !conv_state_in || !conv_ckpt || (n_tokens > 0 && !qkv)) return GDN_E_INVALID_ARG;
+  if (static_cast<int64_t>(n_seqs) * ckpt_cap > kMaxGrid) return GDN_E_UNSUPPORTED;
+  const int Hqk = cfg->n_qk_heads, Hv = cfg->n_v_heads;
+  const size_t as = act_size(cfg), C = static_cast<size_t>(kHeadDim) * (2 * Hqk + Hv);
+  const size_t st = static_cast<size_t>(n_seqs) * (gdn::kConvK - 1) * C * as;
+  const Range outs[] = {{conv_ckpt, static_cast<size_t>(n_seqs) * ckpt_cap * (gdn::kConvK - 1) * C * as}};
+  const Range ins[] = {{qkv, static_cast<size_t>(n_tokens) * C * as}, {conv_state_in, st},
+                       {cu_seqlens, (n_seqs + 1u) * 4u}};
+  if (any_overlap(outs, ins)) return GDN_E_INVALID_ARG;
+  gdn::ConvCkptParams p;
+  p.cu = cu_seqlens;
+  p.n_seqs = n_seqs;
+  p.n_tokens = n_tokens;
+  p.n_qk = Hqk;
+  p.n_v = Hv;
+  p.every = ckpt_every;
+  p.cap = ckpt_cap;
+  p.qkv = qkv;
+  p.st_in = conv_state_in;
+  p.ckpt = conv_ckpt;
+  return launched(gdn::launch_conv_ckpt(p, cfg->act_dtype, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_state_check(const float *S, int64_t n_values, int32_t *stats, gdn_stream_t stream) {
+  if (n_values < 0 || !stats || (n_values > 0 && !S)) return GDN_E_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(S) % 16 != 0 || reinterpret_cast<uintptr_t>(stats) % 4 != 0)
+    return GDN_E_INVALID_ARG;
+  if (overlap(S, static_cast<size_t>(n_values) * 4, stats, 8)) return GDN_E_INVALID_ARG;
+  return launched(gdn::launch_state_check(S, n_values, stats, static_cast<hipStream_t>(stream)));
 }
 
 gdn_status gdn_decode_step(const gdn_config *cfg, int32_t n_seqs, const float *q, const float *k,

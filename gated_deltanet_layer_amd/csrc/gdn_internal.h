@@ -67,6 +67,21 @@ struct NormParams {
 };
 hipError_t launch_norm(const NormParams &p, gdn_dtype act, hipStream_t s);
 
+// Conv-state checkpoints: conv_ckpt[n][c] = the 3 raw rows before token
+// (c + 1) * every of sequence n (rows of [conv_state_in; qkv]), c < cap,
+// for every such token inside the sequence or at its end.
+struct ConvCkptParams {
+  const int32_t *cu;
+  int n_seqs, n_tokens, n_qk, n_v, every, cap;
+  const void *qkv, *st_in;
+  void *ckpt;
+};
+hipError_t launch_conv_ckpt(const ConvCkptParams &p, gdn_dtype act, hipStream_t s);
+
+// Non-finite guard over n_values fp32 state values: stats[0] = number of
+// non-finite values, stats[1] = bit pattern of max |x| over the finite ones.
+hipError_t launch_state_check(const float *S, int64_t n_values, int32_t *stats, hipStream_t s);
+
 struct PrefillParams {
   const int32_t *cu;
   int n_seqs, n_tokens, n_qk, n_v;
@@ -76,6 +91,11 @@ struct PrefillParams {
   void *o;
   void *ws;
   size_t ws_bytes;
+  // State checkpoints: plane c of sequence n (S_ckpt[n][c], c < ckpt_cap)
+  // holds S after token (c + 1) * 64 * ckpt_chunks of the sequence, for
+  // every such token inside it; ckpt_chunks = 0 writes none.
+  float *S_ckpt;
+  int ckpt_chunks, ckpt_cap;
 };
 // Upper bound on the number of chunks over all sequences.
 inline int64_t max_chunks(int n_seqs, int n_tokens) {

@@ -665,6 +665,18 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
 #pragma unroll
     for (int ks = 0; ks < kChunk / 32; ++ks)
       Op<P>::mma2(S[0], S[1], KtLds<P>::get(Ktb, wave, ks), lds_frag<P>(Dsb, ks), lds_frag<P>(Dsb, 2 + ks));
+    // Checkpoint: the state after token (ci + 1) * 64 of the sequence.
+    if (p.ckpt_chunks > 0 && (ci + 1) % p.ckpt_chunks == 0 && (ci + 1) * kChunk <= L) {
+      const int c = (ci + 1) / p.ckpt_chunks - 1;
+      if (c < p.ckpt_cap) {
+        float *dst = p.S_ckpt + ((static_cast<size_t>(n) * p.ckpt_cap + c) * p.n_v + j) * kHeadDim * kHeadDim;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            dst[static_cast<size_t>(16 * wave + acc_row(r)) * kHeadDim + col_base + 16 * ct + acc_col()] = S[ct][r];
+      }
+    }
     block_sync_lds();                        // every LDS read of chunk ci is done
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) lds_put4<P>(Stb, 4, 16 * wave + lr, 16 * ct + lc, S[ct]);

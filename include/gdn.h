@@ -141,6 +141,43 @@ GDN_API gdn_status gdn_prefill_chunked(const gdn_config *cfg, int32_t n_seqs, in
                                const float *S_in, float *S_out, void *o,
                                void *workspace, size_t workspace_bytes, gdn_stream_t stream);
 
+/*
+ * gdn_prefill_chunked_ckpt -- gdn_prefill_chunked that also keeps the delta
+ * state at block boundaries, for re-seeding later calls from a cached prefix:
+ * S_ckpt [N][ckpt_cap][Hv][d][d] fp32, plane c of sequence n = S after its
+ * first (c + 1) * ckpt_every tokens, written for every such boundary inside
+ * the sequence (or at its end) with c < ckpt_cap; other planes are left
+ * untouched. ckpt_every must be a multiple of the chunk length 64 (0, or
+ * ckpt_cap = 0, writes no checkpoint). o and S_out are the same as without
+ * checkpoints. S_ckpt must not overlap any other buffer.
+ */
+GDN_API gdn_status gdn_prefill_chunked_ckpt(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens,
+                               const int32_t *cu_seqlens, const float *q, const float *k, const float *v,
+                               const float *beta, const float *g, const float *S_in, float *S_out, void *o,
+                               int32_t ckpt_every, int32_t ckpt_cap, float *S_ckpt,
+                               void *workspace, size_t workspace_bytes, gdn_stream_t stream);
+
+/*
+ * gdn_conv_state_ckpt -- the conv states at the same boundaries: conv_ckpt
+ * [N][ckpt_cap][3][C] act dtype, plane c of sequence n = the 3 raw rows of
+ * [conv_state_in[n]; its qkv rows] before token (c + 1) * ckpt_every, copied
+ * bit for bit (the conv state a call resuming there needs), for every such
+ * token inside the sequence or at its end, c < ckpt_cap. ckpt_every >= 1.
+ */
+GDN_API gdn_status gdn_conv_state_ckpt(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens,
+                               const int32_t *cu_seqlens, const void *qkv, const void *conv_state_in,
+                               int32_t ckpt_every, int32_t ckpt_cap, void *conv_ckpt, gdn_stream_t stream);
+
+/*
+ * gdn_state_check -- a non-finite guard over n_values fp32 state values S
+ * (16-byte aligned): writes stats[0] = number of NaN/Inf values and
+ * stats[1] = the bit pattern of max |x| over the finite ones (a float, 0 when
+ * there are none) to the device int32 array stats[2]. Nothing is returned to
+ * the host: the caller reads stats after synchronising. Two kernels (one
+ * clears stats), no memset, so the call can be captured in a HIP graph.
+ */
+GDN_API gdn_status gdn_state_check(const float *S, int64_t n_values, int32_t *stats, gdn_stream_t stream);
+
 /* Workspace size gdn_prefill_chunked needs for these sizes (0 for a bad cfg). */
 GDN_API size_t gdn_prefill_workspace_bytes(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens);
 

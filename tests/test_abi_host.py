@@ -185,3 +185,19 @@ def test_decode_verify_validation(lib):
     q = p[:]
     q[3] = None
     assert call(1, 3, q) == B.GDN_E_INVALID_ARG
+
+
+def test_checkpoint_and_guard_validation(lib):
+    cfg = B.make_config(2, 4)
+    need = B.gdn_prefill_workspace_bytes(cfg, 1, 200)
+    args = lambda every, cap, sck: (ctypes.byref(cfg), 1, 200, *FAKE[:9], every, cap, sck, FAKE[12], need, None)
+    assert lib.gdn_prefill_chunked_ckpt(*args(100, 2, FAKE[11])) == B.GDN_E_INVALID_ARG   # not a multiple of 64
+    assert lib.gdn_prefill_chunked_ckpt(*args(-64, 2, FAKE[11])) == B.GDN_E_INVALID_ARG
+    assert lib.gdn_prefill_chunked_ckpt(*args(64, 2, None)) == B.GDN_E_INVALID_ARG
+    c = (ctypes.byref(cfg), 1, 200, FAKE[0], FAKE[1], FAKE[2])
+    assert lib.gdn_conv_state_ckpt(*c, 0, 2, FAKE[3], None) == B.GDN_E_INVALID_ARG     # every >= 1
+    assert lib.gdn_conv_state_ckpt(*c, 5, 0, FAKE[3], None) == B.GDN_OK               # nothing to write
+    assert lib.gdn_conv_state_ckpt(*c, 5, 2, FAKE[1] + 8, None) == B.GDN_E_INVALID_ARG  # overlaps qkv
+    assert lib.gdn_state_check(FAKE[0], 16, None, None) == B.GDN_E_INVALID_ARG
+    assert lib.gdn_state_check(FAKE[0] + 4, 16, FAKE[1], None) == B.GDN_E_INVALID_ARG  # S not 16-byte aligned
+    assert lib.gdn_state_check(FAKE[0], -1, FAKE[1], None) == B.GDN_E_INVALID_ARG

@@ -1,0 +1,111 @@
+"""State checkpoints at block boundaries during prefill, and the non-finite
+guard.
+
+Delta-state checkpoint plane c of a sequence must equal the oracle's final
+state over the sequence's first (c + 1) * B tokens (same bar as S_out);
+conv-state checkpoints must equal the oracle's conv state over the same
+prefix bit for bit. Checkpointing must not change o or S_out. The guard
+must count planted NaN/Inf values exactly and report max |x| of the rest."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from gated_deltanet_layer_amd import binding as B
+from gated_deltanet_layer_amd import layer as Lyr
+from gated_deltanet_layer_amd import workloads as wl
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _prefix(x, m):
+    """The packed inputs of the first m[n] tokens of every sequence n."""
+    cu = x["cu_seqlens"]
+    idx = np.concatenate([np.arange(cu[n], cu[n] + m[n]) for n in range(len(cu) - 1)])
+    out = dict(x)
+    for k in ("qkv", "z", "b", "a"):
+        out[k] = np.ascontiguousarray(x[k][idx])
+    out["cu_seqlens"] = np.concatenate([[0], np.cumsum(m)]).astype(np.int32)
+    return out
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_prefill_state_and_conv_checkpoints(act):
+    lengths = [200, 140, 64]
+    w = wl.custom("prefill", 3, 2, 4, act, seed=340, lengths=lengths, s0_std=0.02, conv0_std=1.0)
+    x = wl.generate(w)
+    cfg = B.make_config(2, 4, act)
+    N, T, Hv, d = 3, sum(lengths), 4, 128
+    t = {k: P.dev(v) for k, v in x.items()}
+    run = Lyr.Prefill(cfg, N, T)
+    conv_out = torch.empty_like(t["conv0"])
+    run.prep(t["cu_seqlens"], t["qkv"], t["b"], t["a"], t["conv_w"], t["dt_bias"], t["A_log"], t["conv0"], conv_out)
+    S_plain = torch.empty_like(t["S0"])
+    run.core(t["cu_seqlens"], t["S0"], S_plain)
+    o_plain = run.o.clone()
+    every, cap = 64, 3
+    S_out = torch.empty_like(t["S0"])
+    S_ckpt = torch.full((N, cap, Hv, d, d), float("nan"), device="cuda")
+    B.gdn_prefill_chunked_ckpt(cfg, N, T, t["cu_seqlens"], run.q, run.k, run.v, run.beta, run.g, t["S0"], S_out,
+                               run.o, every, cap, S_ckpt, run.ws)
+    conv_every = 2                                          # boundaries inside the incoming conv state too
+    conv_cap = 4
+    conv_ckpt = torch.zeros((N, conv_cap) + tuple(t["conv0"].shape[1:]), dtype=t["conv0"].dtype, device="cuda")
+    B.gdn_conv_state_ckpt(cfg, N, T, t["cu_seqlens"], t["qkv"], t["conv0"], conv_every, conv_cap, conv_ckpt)
+    conv_ckpt64 = torch.zeros_like(conv_ckpt[:, :cap])
+    B.gdn_conv_state_ckpt(cfg, N, T, t["cu_seqlens"], t["qkv"], t["conv0"], every, cap, conv_ckpt64)
+    torch.cuda.synchronize()
+    assert np.array_equal(P.bits(S_out), P.bits(S_plain)), "checkpointing changed S_out"
+    assert np.array_equal(P.bits(run.o), P.bits(o_plain)), "checkpointing changed o"
+    for c in range(cap):
+        m = [min(L, (c + 1) * every) for L in lengths]
+        xm = _prefix(x, m)
+        ref = P.oracle_layer(w, P.inputs_f64(xm, act), xm["cu_seqlens"])
+        ref_conv = ref["conv_out"].astype(np.float32)
+        exp_bits = wl.bf16_bits(ref_conv) if act == "bf16" else ref_conv.view(np.uint32)
+        for n, L in enumerate(lengths):
+            if (c + 1) * every > L:
+                assert torch.isnan(S_ckpt[n, c]).all(), f"plane {c} of sequence {n} written past its end"
+                continue
+            say(f"  plane {c} of sequence {n} (token {(c + 1) * every})")
+            P.check(f"S_ckpt[{n},{c}]", P.host(S_ckpt[n, c]), ref["S_out"][n], act)
+            assert np.array_equal(P.bits(conv_ckpt64[n, c]), exp_bits[n]), f"conv plane {c} of sequence {n}"
+    for c in range(conv_cap):
+        m = [min(L, (c + 1) * conv_every) for L in lengths]
+        xm = _prefix(x, m)
+        ref = P.oracle_layer(w, P.inputs_f64(xm, act), xm["cu_seqlens"])
+        ref_conv = ref["conv_out"].astype(np.float32)
+        exp_bits = wl.bf16_bits(ref_conv) if act == "bf16" else ref_conv.view(np.uint32)
+        assert np.array_equal(P.bits(conv_ckpt[:, c]), exp_bits), f"conv plane {c} (every {conv_every})"
+
+
+@pytest.mark.parametrize("n", [0, 7, 1 << 20])
+def test_state_check_counts_and_max(n):
+    g = torch.Generator(device="cpu").manual_seed(341)
+    S = torch.randn(n, generator=g).cuda() if n else torch.empty(0, device="cuda")
+    planted = 0
+    if n >= 7:
+        S[3] = float("nan")
+        S[n - 1] = float("inf")
+        planted = 2
+    if n > 1000:
+        S[500] = float("-inf")
+        S[123457] = float("nan")
+        S[70000] = 1e6                       # the largest finite value
+        planted += 2
+    stats = torch.full((2,), -1, dtype=torch.int32, device="cuda")
+    B.gdn_state_check(S, stats)
+    torch.cuda.synchronize()
+    st = stats.cpu().numpy()
+    finite = S[torch.isfinite(S)].abs()
+    exp_max = float(finite.max()) if finite.numel() else 0.0
+    say(f"case state check n={n}: {st[0]} non-finite, max {np.int32(st[1]).view(np.float32)}")
+    assert st[0] == planted
+    assert np.int32(st[1]).view(np.float32) == np.float32(exp_max)
