@@ -33,7 +33,12 @@ CONV_K = 4
 _STREAM = {
     "lengths": 1, "conv_w": 2, "norm_w": 3, "dt_bias": 4, "A_log": 5,
     "S0": 6, "conv0": 7, "qkv": 8, "z": 9, "b": 10, "a": 11,
+    "x": 12, "w_qkv": 13, "w_gate": 14, "w_beta": 15, "w_alpha": 16, "w_out": 17,
 }
+
+# Hidden sizes of the two models' layer input (the page's section
+# "Architecture cheat sheet": 5120 on the 27B, 2048 on the 35B-A3B).
+HIDDEN = {48: 5120, 32: 2048}
 
 
 @dataclass(frozen=True)
@@ -164,6 +169,35 @@ def generate(w: Workload, max_tokens: Optional[int] = None,
     return out
 
 
+def generate_block(w: Workload, hidden: int, max_tokens: Optional[int] = None,
+                   max_steps: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Inputs of the whole token-mixer block: ``generate(w)``'s parameters,
+    states and cu_seqlens, plus the layer input and the projection weights
+    (Linear layout, one row per output), all bf16 bit patterns:
+      x [T, hidden] (decode: [S, N, hidden]) ~ N(0, 1)
+      w_qkv [C, hidden], w_gate [Hv*d, hidden], w_beta, w_alpha [Hv, hidden]
+        ~ N(0, 1/hidden), so that the projected streams are ~ N(0, 1) like
+        the mixer's own synthetic inputs
+      w_out [hidden, Hv*d] ~ N(0, 1/(Hv*d))
+    The mixer streams qkv, z, b, a of ``generate`` are dropped: the block
+    computes them from x."""
+    if w.act != "bf16":
+        raise ValueError("the projections take bf16 operands")
+    out = generate(w, max_tokens=max_tokens, max_steps=max_steps)
+    lead = out.pop("qkv").shape[:-1]
+    for k in ("z", "b", "a"):
+        out.pop(k)
+    Hv, d, C, seed = w.n_v_heads, w.head_dim, w.conv_width, w.seed
+    out["x"] = bf16_bits(_normal(seed, "x", lead + (hidden,)))
+    s_in = 1.0 / np.sqrt(hidden)
+    out["w_qkv"] = bf16_bits(_normal(seed, "w_qkv", (C, hidden), 0.0, s_in))
+    out["w_gate"] = bf16_bits(_normal(seed, "w_gate", (Hv * d, hidden), 0.0, s_in))
+    out["w_beta"] = bf16_bits(_normal(seed, "w_beta", (Hv, hidden), 0.0, s_in))
+    out["w_alpha"] = bf16_bits(_normal(seed, "w_alpha", (Hv, hidden), 0.0, s_in))
+    out["w_out"] = bf16_bits(_normal(seed, "w_out", (hidden, Hv * d), 0.0, 1.0 / np.sqrt(Hv * d)))
+    return out
+
+
 # The five synthetic workloads (shapes of the Qwen 3.6 27B / 35B-A3B GDN layers).
 WORKLOADS = {
     1: Workload("tiny single-chunk prefill T=64 Hqk=2 Hv=4 f32", "prefill", 1, 2, 4, "f32",
@@ -187,5 +221,5 @@ def custom(kind: str, n_seqs: int, n_qk_heads: int, n_v_heads: int, act: str, se
                     steps=steps, s0_std=s0_std, conv0_std=conv0_std, head_dim=head_dim)
 
 
-__all__ = ["Workload", "WORKLOADS", "generate", "custom", "bf16_bits", "bf16_to_f32", "as_f32",
+__all__ = ["Workload", "WORKLOADS", "generate", "generate_block", "HIDDEN", "custom", "bf16_bits", "bf16_to_f32", "as_f32",
            "HEAD_DIM", "CONV_K", "replace"]

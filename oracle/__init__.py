@@ -7,7 +7,8 @@ with the HIP library and imports nothing from it; it takes plain numpy arrays.
 The arithmetic lives in ``gdn_oracle.c`` (fp64, libm only). This wrapper only
 converts arrays to contiguous fp64, allocates outputs and calls the C entry
 points; ``layer`` chains the three steps in the order the xwen CLAUDE.md page
-lists them (section "Architecture cheat sheet", gated DeltaNet paragraph).
+lists them (section "Architecture cheat sheet", gated DeltaNet paragraph), and
+``block`` adds the projections before and after it.
 """
 from __future__ import annotations
 
@@ -59,6 +60,11 @@ def load(path: Optional[str] = None):
     lib.gdno_delta_rule.restype = None
     lib.gdno_gated_rmsnorm.argtypes = [ctypes.c_long, ctypes.c_int, _D, _D, _D, ctypes.c_double, _D]
     lib.gdno_gated_rmsnorm.restype = None
+    lib.gdno_linear.argtypes = [ctypes.c_long, ctypes.c_int, ctypes.c_int, _D, _D, _D]
+    lib.gdno_linear.restype = None
+    lib.gdno_in_proj.argtypes = [ctypes.c_long, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                 _D, _D, _D, _D, _D, _D, _D, _D, _D]
+    lib.gdno_in_proj.restype = None
     for f in ("gdno_sigmoid", "gdno_softplus", "gdno_silu"):
         getattr(lib, f).argtypes = [ctypes.c_double]
         getattr(lib, f).restype = ctypes.c_double
@@ -77,6 +83,15 @@ def _p(x: np.ndarray):
 
 def _cu(cu) -> np.ndarray:
     return np.ascontiguousarray(cu, dtype=np.int32)
+
+
+def round_bf16(x) -> np.ndarray:
+    """Round fp64 values to bfloat16 precision (8 significant bits), to nearest
+    with ties to even, returned as fp64. Finite inputs in bf16's normal range;
+    this is how a value is stored in a bf16 tensor."""
+    x = _f64(x)
+    m, e = np.frexp(x)                      # x = m * 2^e, 0.5 <= |m| < 1
+    return np.ldexp(np.rint(m * 256.0), e - 8)
 
 
 class Oracle:
@@ -171,6 +186,53 @@ class Oracle:
         return r
 
 
+    def linear(self, x, W):
+        """y = x W^T for x [..., n_in], W [n_out, n_in] (a Linear without bias)."""
+        W = _f64(W)
+        n_out, n_in = W.shape
+        x = _f64(x)
+        lead = x.shape[:-1]
+        xx = x.reshape(-1, n_in)
+        y = np.empty((xx.shape[0], n_out))
+        self.lib.gdno_linear(xx.shape[0], n_in, n_out, _p(xx), _p(W), _p(y))
+        return y.reshape(lead + (n_out,))
+
+    def in_proj(self, n_qk_heads: int, n_v_heads: int, head_dim: int, x, w_qkv, w_gate, w_beta, w_alpha):
+        """The four input projections of x [T, hidden]: dict of fp64 qkv [T, C],
+        z [T, Hv, d], b [T, Hv], a [T, Hv]."""
+        x = _f64(x)
+        T, hidden = x.shape
+        Hqk, Hv, d = n_qk_heads, n_v_heads, head_dim
+        C = d * (2 * Hqk + Hv)
+        ws = [_f64(w_qkv).reshape(C, hidden), _f64(w_gate).reshape(Hv * d, hidden),
+              _f64(w_beta).reshape(Hv, hidden), _f64(w_alpha).reshape(Hv, hidden)]
+        out = dict(qkv=np.empty((T, C)), z=np.empty((T, Hv, d)), b=np.empty((T, Hv)), a=np.empty((T, Hv)))
+        self.lib.gdno_in_proj(T, hidden, Hqk, Hv, d, _p(x), *[_p(w) for w in ws],
+                              _p(out["qkv"]), _p(out["z"]), _p(out["b"]), _p(out["a"]))
+        return out
+
+    def block(self, cu, n_qk_heads: int, n_v_heads: int, head_dim: int, x, w_qkv, w_gate, w_beta,
+              w_alpha, w_out, conv_w, dt_bias, A_log, norm_w, conv_in, S_in, round_act: bool = True,
+              l2_eps: float = L2_EPS, norm_eps: float = NORM_EPS, l2_mode: int = L2_CLAMP):
+        """The token-mixer block from the layer input x [T, hidden]: the input
+        projections, the mixer (``layer``), then ssm_out (the page's gated
+        DeltaNet paragraph, in its order). With ``round_act`` the tensors at
+        the mixer's boundary (qkv, z, the logits in; y out) are rounded to
+        bf16, the dtype they are stored in. Returns the ``layer`` dict plus
+        ``proj`` (the in-projections, rounded as the mixer saw them) and
+        ``out`` [T, hidden]."""
+        rnd = round_bf16 if round_act else _f64
+        pr = {k: rnd(v) for k, v in self.in_proj(n_qk_heads, n_v_heads, head_dim, x, w_qkv, w_gate,
+                                                   w_beta, w_alpha).items()}
+        r = self.layer(cu, n_qk_heads, n_v_heads, head_dim, pr["qkv"], pr["z"], pr["b"], pr["a"],
+                       conv_w, dt_bias, A_log, norm_w, conv_in, S_in, l2_eps=l2_eps, norm_eps=norm_eps,
+                       l2_mode=l2_mode)
+        T = pr["qkv"].shape[0]
+        y = rnd(r["y"]).reshape(T, n_v_heads * head_dim)
+        r.update(proj=pr, out=self.linear(y, w_out))
+        return r
+
+
 _default: Optional[Oracle] = None
 
 
@@ -181,4 +243,4 @@ def default() -> Oracle:
     return _default
 
 
-__all__ = ["Oracle", "default", "build", "load", "CONV_K", "L2_EPS", "NORM_EPS"]
+__all__ = ["Oracle", "default", "build", "load", "round_bf16", "CONV_K", "L2_EPS", "NORM_EPS"]

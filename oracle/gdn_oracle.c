@@ -217,6 +217,47 @@ void gdno_gated_rmsnorm(long n_rows, int d, const double *o, const double *z,
     }
 }
 
+/*
+ * A linear layer without bias, weight in the Linear layout (one row per
+ * output): y[t][o] = sum_i W[o][i] * x[t][i], for T rows of x [T][n_in],
+ * W [n_out][n_in], y [T][n_out]. The page applies every projection of the
+ * layer this way to its input ("W @ x" per token: attn_qkv, attn_gate,
+ * ssm_beta, ssm_alpha before the mixer, ssm_out after it).
+ */
+void gdno_linear(long T, int n_in, int n_out, const double *x, const double *W, double *y)
+{
+    for (long t = 0; t < T; ++t) {
+        const double *xr = x + (size_t)t * n_in;
+        for (int o = 0; o < n_out; ++o) {
+            const double *wr = W + (size_t)o * n_in;
+            double acc = 0.0;
+            for (int i = 0; i < n_in; ++i) acc += wr[i] * xr[i];
+            y[(size_t)t * n_out + o] = acc;
+        }
+    }
+}
+
+/*
+ * The four input projections of the layer input x [T][hidden] (the page's
+ * gated DeltaNet paragraph, with the tensor names of its section "GGUF facts
+ * that differ from the HF checkpoint"):
+ *   qkv = attn_qkv @ x   [T][C]      the fused stream the conv runs over
+ *   z   = attn_gate @ x  [T][Hv*d]   the gate of the RMSNorm
+ *   b   = ssm_beta @ x   [T][Hv]     beta logits
+ *   a   = ssm_alpha @ x  [T][Hv]     alpha logits
+ * with w_qkv [C][hidden], w_gate [Hv*d][hidden], w_beta, w_alpha [Hv][hidden].
+ */
+void gdno_in_proj(long T, int hidden, int Hqk, int Hv, int d, const double *x,
+                  const double *w_qkv, const double *w_gate, const double *w_beta,
+                  const double *w_alpha, double *qkv, double *z, double *b, double *a)
+{
+    const int C = d * (2 * Hqk + Hv);
+    gdno_linear(T, hidden, C, x, w_qkv, qkv);
+    gdno_linear(T, hidden, Hv * d, x, w_gate, z);
+    gdno_linear(T, hidden, Hv, x, w_beta, b);
+    gdno_linear(T, hidden, Hv, x, w_alpha, a);
+}
+
 /* Scalar functions, exposed so tests can pin them on their own. */
 double gdno_sigmoid(double x) { return sigmoid(x); }
 double gdno_softplus(double x) { return softplus(x); }

@@ -416,4 +416,86 @@ def pin_head_subset(orc):
     assert np.array_equal(sub["S_out"][:, [1, 4]], full["S_out"][:, [1, 4]])
 
 
+# ------------------------------------------------------------ projections
+def pin_linear_hand_worked(orc):
+    """y = x W^T on integers, worked by hand: row (1, 2) against weight rows
+    (3, 4), (5, 6), (7, 8) gives 11, 17, 23; row (3, -1) gives 5, 9, 13."""
+    x = np.array([[1.0, 2.0], [3.0, -1.0]])
+    W = np.array([[3.0, 4.0], [5.0, 6.0], [7.0, 8.0]])
+    y = orc.linear(x, W)
+    assert np.array_equal(y, np.array([[11.0, 17.0, 23.0], [5.0, 9.0, 13.0]])), y
+
+
+def pin_linear_library(orc):
+    """A non-square product against numpy's matmul of x and W^T."""
+    rng = np.random.default_rng(171)
+    x = rng.standard_normal((7, 13))
+    W = rng.standard_normal((5, 13))
+    _close(orc.linear(x, W), x @ W.T, 1e-13, "linear")
+
+
+def pin_in_proj_routing(orc):
+    """Each of the four projections takes its own weight: with identity
+    blocks as weights, qkv, z, b and a are the matching slices of x; with
+    random weights each equals numpy's product with its weight."""
+    Hqk, Hv, d = 1, 2, 4
+    C = d * (2 * Hqk + Hv)
+    widths = [C, Hv * d, Hv, Hv]
+    hidden = sum(widths)
+    rng = np.random.default_rng(172)
+    x = rng.standard_normal((5, hidden))
+    eye = np.eye(hidden)
+    cuts = np.cumsum([0] + widths)
+    ws = [eye[cuts[i]:cuts[i + 1]] for i in range(4)]
+    r = orc.in_proj(Hqk, Hv, d, x, *ws)
+    for i, name in enumerate(("qkv", "z", "b", "a")):
+        assert np.array_equal(r[name].reshape(5, -1), x[:, cuts[i]:cuts[i + 1]]), name
+    ws = [rng.standard_normal((w, hidden)) for w in widths]
+    r = orc.in_proj(Hqk, Hv, d, x, *ws)
+    for i, name in enumerate(("qkv", "z", "b", "a")):
+        _close(r[name].reshape(5, -1), x @ ws[i].T, 1e-13, name)
+
+
+def pin_round_bf16(orc):
+    """bf16 rounding: hand-worked ties to even at 8 significant bits, and
+    agreement with the integer bit-pattern rounding of fp32 values."""
+    import oracle
+    u = 2.0 ** -8
+    cases = {1.0 + u: 1.0, 1.0 + 3 * u: 1.0 + 4 * u, 1.0 + u + 2.0 ** -20: 1.0 + 2 * u,
+             -(1.0 + u): -1.0, 0.0: 0.0, 3.0: 3.0, 255.5: 256.0, 2.0 ** -100 * 1.5: 2.0 ** -100 * 1.5}
+    for x, want in cases.items():
+        got = float(oracle.round_bf16(np.array([x]))[0])
+        assert got == want, (x, got, want)
+    rng = np.random.default_rng(173)
+    v = (rng.standard_normal(4096) * np.exp(rng.uniform(-20, 20, 4096))).astype(np.float32)
+    ref = wl.bf16_to_f32(wl.bf16_bits(v)).astype(np.float64)
+    assert np.array_equal(oracle.round_bf16(v.astype(np.float64)), ref)
+
+
+def pin_block_composition(orc):
+    """The block with identity-block weights is the mixer on slices of x: the
+    in-projections feed the mixer unchanged and ssm_out passes y through."""
+    Hqk, Hv, d = 1, 2, 8
+    C = d * (2 * Hqk + Hv)
+    widths = [C, Hv * d, Hv, Hv]
+    hidden = sum(widths)
+    cuts = np.cumsum([0] + widths)
+    lx = _layer_inputs(174, [9, 70], Hqk, Hv, d)
+    T = int(lx["cu_seqlens"][-1])
+    x = np.concatenate([lx["qkv"].reshape(T, -1), lx["z"].reshape(T, -1), lx["b"], lx["a"]], axis=1)
+    eye = np.eye(hidden)
+    ws = [eye[cuts[i]:cuts[i + 1]] for i in range(4)]
+    w_out = np.eye(hidden)[:, :Hv * d]                   # out[:, :Hv*d] = y, the rest 0
+    for rnd in (False, True):
+        r = orc.block(lx["cu_seqlens"], Hqk, Hv, d, x, *ws, w_out, lx["conv_w"], lx["dt_bias"],
+                      lx["A_log"], lx["norm_w"], lx["conv0"], lx["S0"], round_act=rnd)
+        import oracle
+        f = oracle.round_bf16 if rnd else (lambda a: a)
+        ref = orc.layer(lx["cu_seqlens"], Hqk, Hv, d, f(lx["qkv"]), f(lx["z"]), f(lx["b"]), f(lx["a"]),
+                        lx["conv_w"], lx["dt_bias"], lx["A_log"], lx["norm_w"], lx["conv0"], lx["S0"])
+        assert np.array_equal(r["out"][:, :Hv * d], f(ref["y"]).reshape(T, -1)), rnd
+        assert np.array_equal(r["out"][:, Hv * d:], np.zeros((T, hidden - Hv * d))), rnd
+        assert np.array_equal(r["S_out"], ref["S_out"]), rnd
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -56,6 +56,12 @@ MUTANTS = [
      "const int c0 = part * d + h * 2 * d;", False),
     ("v_offset", "const int c0 = 2 * d * Hqk + jh * d;", "const int c0 = d * Hqk + jh * d;", False),
     ("sigmoid_wrong", "return 1.0 / (1.0 + exp(-x));", "return 1.0 / (1.0 + exp(x));", False),
+    ("linear_transposed", "acc += wr[i] * xr[i];", "acc += W[(size_t)i * n_out + o] * xr[i];", False),
+    ("linear_dropped_term", "for (int i = 0; i < n_in; ++i) acc", "for (int i = 1; i < n_in; ++i) acc", False),
+    ("in_proj_beta_alpha_swapped", "gdno_linear(T, hidden, Hv, x, w_beta, b);",
+     "gdno_linear(T, hidden, Hv, x, w_alpha, b);", False),
+    ("in_proj_gate_weight", "gdno_linear(T, hidden, Hv * d, x, w_gate, z);",
+     "gdno_linear(T, hidden, Hv * d, x, w_qkv, z);", False),
 ]
 
 
