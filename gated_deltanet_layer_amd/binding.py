@@ -31,7 +31,7 @@ CONV_K = 4
 EXPORTS = ("gdn_default_config", "gdn_conv_gate_prep", "gdn_prefill_chunked",
            "gdn_prefill_workspace_bytes", "gdn_decode_step", "gdn_decode_fused", "gdn_decode_verify",
            "gdn_gated_rmsnorm", "gdn_prefill_chunked_ckpt", "gdn_conv_state_ckpt", "gdn_state_check",
-           "gdn_status_string", "gdn_version")
+           "gdn_in_proj", "gdn_out_proj", "gdn_status_string", "gdn_version")
 
 
 class GdnError(RuntimeError):
@@ -87,6 +87,10 @@ def load(path: Optional[str] = None):
     lib.gdn_decode_fused.restype = ctypes.c_int
     lib.gdn_decode_verify.argtypes = [cfgp, ctypes.c_int32, ctypes.c_int32] + [_P] * 13 + [_P]
     lib.gdn_decode_verify.restype = ctypes.c_int
+    lib.gdn_in_proj.argtypes = [cfgp, ctypes.c_int32, ctypes.c_int32] + [_P] * 9 + [_P]
+    lib.gdn_in_proj.restype = ctypes.c_int
+    lib.gdn_out_proj.argtypes = [cfgp, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P]
+    lib.gdn_out_proj.restype = ctypes.c_int
     lib.gdn_gated_rmsnorm.argtypes = [cfgp, ctypes.c_int64, _P, _P, _P, _P, _P]
     lib.gdn_gated_rmsnorm.restype = ctypes.c_int
     if path is None:
@@ -267,7 +271,28 @@ def gdn_gated_rmsnorm(cfg: gdn_config, n_rows: int, o, z, norm_w, y, stream=None
     _check("gdn_gated_rmsnorm", s)
 
 
+def gdn_in_proj(cfg: gdn_config, n_tokens: int, hidden: int, x, w_qkv, w_gate, w_beta, w_alpha, qkv, z,
+                beta_logit, alpha_logit, stream=None):
+    Hqk, Hv, d, T, bf = cfg.n_qk_heads, cfg.n_v_heads, cfg.head_dim, n_tokens, torch.bfloat16
+    C = d * (2 * Hqk + Hv)
+    s = load().gdn_in_proj(
+        ctypes.byref(cfg), T, hidden, _ptr(x, "x", bf, T * hidden), _ptr(w_qkv, "w_qkv", bf, C * hidden),
+        _ptr(w_gate, "w_gate", bf, Hv * d * hidden), _ptr(w_beta, "w_beta", bf, Hv * hidden),
+        _ptr(w_alpha, "w_alpha", bf, Hv * hidden), _ptr(qkv, "qkv", bf, T * C), _ptr(z, "z", bf, T * Hv * d),
+        _ptr(beta_logit, "beta_logit", bf, T * Hv), _ptr(alpha_logit, "alpha_logit", bf, T * Hv), _stream(stream))
+    _check("gdn_in_proj", s)
+
+
+def gdn_out_proj(cfg: gdn_config, n_tokens: int, hidden: int, y, w_out, out, stream=None):
+    Hv, d, T, bf = cfg.n_v_heads, cfg.head_dim, n_tokens, torch.bfloat16
+    s = load().gdn_out_proj(
+        ctypes.byref(cfg), T, hidden, _ptr(y, "y", bf, T * Hv * d), _ptr(w_out, "w_out", bf, hidden * Hv * d),
+        _ptr(out, "out", bf, T * hidden), _stream(stream))
+    _check("gdn_out_proj", s)
+
+
 __all__ = ["load", "make_config", "gdn_config", "GdnError", "status_string", "EXPORTS",
            "gdn_conv_gate_prep", "gdn_prefill_chunked", "gdn_prefill_workspace_bytes",
            "gdn_decode_step", "gdn_decode_fused", "gdn_decode_verify", "gdn_gated_rmsnorm",
-           "gdn_prefill_chunked_ckpt", "gdn_conv_state_ckpt", "gdn_state_check", "GDN_F32", "GDN_BF16"]
+           "gdn_prefill_chunked_ckpt", "gdn_conv_state_ckpt", "gdn_state_check", "gdn_in_proj",
+           "gdn_out_proj", "GDN_F32", "GDN_BF16"]

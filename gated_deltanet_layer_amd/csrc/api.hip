@@ -294,6 +294,103 @@ gdn_status gdn_decode_step(const gdn_config *cfg, int32_t n_seqs, const float *q
 
 namespace {
 
+bool aligned(const void *p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+// Shared checks of the two projections: bf16 only, K (the contraction length)
+// a positive multiple of 64, operands 16-byte aligned.
+gdn_status check_proj(const gdn_config *cfg, int32_t n_tokens, int32_t hidden) {
+  const gdn_status cs = check_config(cfg);
+  if (cs != GDN_OK) return cs;
+  if (n_tokens < 0 || hidden < 1) return GDN_E_INVALID_ARG;
+  if (cfg->act_dtype != GDN_BF16 || hidden % 64 != 0) return GDN_E_UNSUPPORTED;
+  return GDN_OK;
+}
+
+gdn_status launch_proj(const gdn::GemmParams &p, gdn_stream_t stream) {
+  // Tiles of 256 rows by at least 128 columns; the grid is far below its limit
+  // for any int32 sizes, but the row index arithmetic needs M * K in int64.
+  return launched(gdn::launch_gemm(p, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_in_proj(const gdn_config *cfg, int32_t n_tokens, int32_t hidden, const void *x, const void *w_qkv,
+                       const void *w_gate, const void *w_beta, const void *w_alpha, void *qkv, void *z,
+                       void *beta_logit, void *alpha_logit, gdn_stream_t stream) {
+  const gdn_status cs = check_proj(cfg, n_tokens, hidden);
+  if (cs != GDN_OK) return cs;
+  if (n_tokens == 0) return GDN_OK;
+  if (!x || !w_qkv || !w_gate || !w_beta || !w_alpha || !qkv || !z || !beta_logit || !alpha_logit)
+    return GDN_E_INVALID_ARG;
+  const void *ops[] = {x, w_qkv, w_gate, w_beta, w_alpha};
+  for (const void *o : ops)
+    if (!aligned(o, 16)) return GDN_E_INVALID_ARG;
+  const void *res[] = {qkv, z, beta_logit, alpha_logit};
+  for (const void *o : res)
+    if (!aligned(o, 2)) return GDN_E_INVALID_ARG;
+  const int Hqk = cfg->n_qk_heads, Hv = cfg->n_v_heads;
+  const int64_t C = static_cast<int64_t>(kHeadDim) * (2 * Hqk + Hv), Z = static_cast<int64_t>(Hv) * kHeadDim;
+  const int64_t N = C + Z + 2 * Hv;
+  if (N > kMaxGrid) return GDN_E_UNSUPPORTED;
+  const size_t T = static_cast<size_t>(n_tokens), H = static_cast<size_t>(hidden);
+  const Range outs[] = {{qkv, T * C * 2}, {z, T * Z * 2}, {beta_logit, T * Hv * 2}, {alpha_logit, T * Hv * 2}};
+  const Range ins[] = {{x, T * H * 2}, {w_qkv, C * H * 2}, {w_gate, Z * H * 2}, {w_beta, Hv * H * 2},
+                       {w_alpha, Hv * H * 2}};
+  if (any_overlap(outs, ins)) return GDN_E_INVALID_ARG;
+
+  gdn::GemmParams p;
+  p.M = n_tokens;
+  p.N = static_cast<int>(N);
+  p.K = hidden;
+  p.x = static_cast<const uint16_t *>(x);
+  p.n_seg = 4;
+  const int64_t start[4] = {0, C, C + Z, C + Z + Hv};
+  const void *w[4] = {w_qkv, w_gate, w_beta, w_alpha};
+  void *out[4] = {qkv, z, beta_logit, alpha_logit};
+  const int64_t ld[4] = {C, Z, Hv, Hv};
+  for (int s = 0; s < 4; ++s) {
+    p.start[s] = static_cast<int>(start[s]);
+    p.w[s] = static_cast<const uint16_t *>(w[s]);
+    p.out[s] = static_cast<uint16_t *>(out[s]);
+    p.ld[s] = ld[s];
+  }
+  return launch_proj(p, stream);
+}
+
+gdn_status gdn_out_proj(const gdn_config *cfg, int32_t n_tokens, int32_t hidden, const void *y, const void *w_out,
+                        void *out, gdn_stream_t stream) {
+  const gdn_status cs = check_config(cfg);
+  if (cs != GDN_OK) return cs;
+  if (n_tokens < 0 || hidden < 1) return GDN_E_INVALID_ARG;
+  if (cfg->act_dtype != GDN_BF16) return GDN_E_UNSUPPORTED;
+  if (n_tokens == 0) return GDN_OK;
+  if (!y || !w_out || !out) return GDN_E_INVALID_ARG;
+  if (!aligned(y, 16) || !aligned(w_out, 16) || !aligned(out, 2)) return GDN_E_INVALID_ARG;
+  const int64_t Kd = static_cast<int64_t>(cfg->n_v_heads) * kHeadDim;
+  if (Kd > kMaxGrid) return GDN_E_UNSUPPORTED;
+  const size_t T = static_cast<size_t>(n_tokens), H = static_cast<size_t>(hidden);
+  const Range outs[] = {{out, T * H * 2}};
+  const Range ins[] = {{y, T * Kd * 2}, {w_out, H * Kd * 2}};
+  if (any_overlap(outs, ins)) return GDN_E_INVALID_ARG;
+
+  gdn::GemmParams p = {};
+  p.M = n_tokens;
+  p.N = hidden;
+  p.K = static_cast<int>(Kd);
+  p.x = static_cast<const uint16_t *>(y);
+  p.n_seg = 1;
+  p.w[0] = static_cast<const uint16_t *>(w_out);
+  p.out[0] = static_cast<uint16_t *>(out);
+  p.ld[0] = hidden;
+  return launch_proj(p, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
 // gdn_decode_fused (K = 1) and gdn_decode_verify: K tokens per sequence in one
 // launch, the state and conv state after each token to its snapshot plane.
 gdn_status decode_tokens(const gdn_config *cfg, int32_t n_seqs, int32_t K, const void *qkv,

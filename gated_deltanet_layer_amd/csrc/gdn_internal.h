@@ -82,6 +82,23 @@ hipError_t launch_conv_ckpt(const ConvCkptParams &p, gdn_dtype act, hipStream_t 
 // non-finite values, stats[1] = bit pattern of max |x| over the finite ones.
 hipError_t launch_state_check(const float *S, int64_t n_values, int32_t *stats, hipStream_t s);
 
+// bf16 product out[m][n] = sum_k x[m][k] w[n][k] (fp32 accumulation, bf16
+// out). Columns [start[s], start[s+1]) (start[n_seg] = N) form segment s: its
+// weight rows come from w[s] (row n - start[s], K values each) and its outputs
+// go to out[s][m * ld[s] + n - start[s]]. K is a multiple of 64; x and every
+// w[s] are 16-byte aligned.
+constexpr int kMaxSeg = 4;
+struct GemmParams {
+  int M, N, K;
+  const uint16_t *x;
+  int n_seg;
+  int start[kMaxSeg];
+  const uint16_t *w[kMaxSeg];
+  uint16_t *out[kMaxSeg];
+  int64_t ld[kMaxSeg];
+};
+hipError_t launch_gemm(const GemmParams &p, hipStream_t s);
+
 struct PrefillParams {
   const int32_t *cu;
   int n_seqs, n_tokens, n_qk, n_v;

@@ -3,7 +3,9 @@
 ``Prefill`` runs gdn_conv_gate_prep -> gdn_prefill_chunked -> gdn_gated_rmsnorm
 over packed sequences; ``Decode`` runs gdn_conv_gate_prep -> gdn_decode_step ->
 gdn_gated_rmsnorm for one token per sequence; ``DecodeFused`` runs the same
-step as the single launch gdn_decode_fused. Each allocates its intermediates
+step as the single launch gdn_decode_fused. ``Block`` and ``DecodeBlock`` put
+gdn_in_proj before and gdn_out_proj after ``Prefill`` and ``DecodeFused``
+(the whole token-mixer block from the layer input). Each allocates its intermediates
 (q, k, v, beta, g, o, y, workspace, the second conv-state buffer) once with
 torch and then only calls the library, so a timed loop allocates nothing.
 """
@@ -99,3 +101,59 @@ class DecodeFused:
                            stream)
         self.cur = 1 - self.cur
         return y
+
+
+class _Proj:
+    """Buffers of the projected streams and of the block output (bf16)."""
+
+    def __init__(self, cfg: B.gdn_config, n_tokens: int, hidden: int, device):
+        Hqk, Hv, d = cfg.n_qk_heads, cfg.n_v_heads, cfg.head_dim
+        bf = dict(dtype=torch.bfloat16, device=device)
+        self.hidden = hidden
+        self.qkv = torch.empty(n_tokens, d * (2 * Hqk + Hv), **bf)
+        self.z = torch.empty(n_tokens, Hv, d, **bf)
+        self.b = torch.empty(n_tokens, Hv, **bf)
+        self.a = torch.empty(n_tokens, Hv, **bf)
+        self.out = torch.empty(n_tokens, hidden, **bf)
+
+    def project_in(self, cfg, T, x, w_qkv, w_gate, w_beta, w_alpha, stream):
+        B.gdn_in_proj(cfg, T, self.hidden, x, w_qkv, w_gate, w_beta, w_alpha, self.qkv, self.z, self.b, self.a,
+                      stream)
+
+    def project_out(self, cfg, T, y, w_out, stream):
+        B.gdn_out_proj(cfg, T, self.hidden, y, w_out, self.out, stream)
+        return self.out
+
+
+class Block:
+    """The block over packed sequences: gdn_in_proj -> Prefill -> gdn_out_proj."""
+
+    def __init__(self, cfg: B.gdn_config, n_seqs: int, n_tokens: int, hidden: int, device="cuda"):
+        self.cfg, self.T = cfg, n_tokens
+        self.mixer = Prefill(cfg, n_seqs, n_tokens, device)
+        self.proj = _Proj(cfg, n_tokens, hidden, device)
+
+    def __call__(self, cu, x, w_qkv, w_gate, w_beta, w_alpha, w_out, conv_w, dt_bias, A_log, norm_w, conv_in,
+                 conv_out, S_in, S_out, stream=None):
+        P = self.proj
+        P.project_in(self.cfg, self.T, x, w_qkv, w_gate, w_beta, w_alpha, stream)
+        y = self.mixer(cu, P.qkv, P.z, P.b, P.a, conv_w, dt_bias, A_log, norm_w, conv_in, conv_out, S_in, S_out,
+                       stream)
+        return P.project_out(self.cfg, self.T, y, w_out, stream)
+
+
+class DecodeBlock:
+    """One token per sequence through the block: gdn_in_proj -> gdn_decode_fused
+    -> gdn_out_proj (conv state handled as in ``DecodeFused``)."""
+
+    def __init__(self, cfg: B.gdn_config, n_seqs: int, hidden: int, conv_state: torch.Tensor):
+        self.cfg, self.N = cfg, n_seqs
+        self.mixer = DecodeFused(cfg, n_seqs, conv_state)
+        self.proj = _Proj(cfg, n_seqs, hidden, conv_state.device)
+        self.y = torch.empty_like(self.proj.z)
+
+    def __call__(self, x, w_qkv, w_gate, w_beta, w_alpha, w_out, conv_w, dt_bias, A_log, norm_w, S, stream=None):
+        P = self.proj
+        P.project_in(self.cfg, self.N, x, w_qkv, w_gate, w_beta, w_alpha, stream)
+        self.mixer(P.qkv, P.z, P.b, P.a, conv_w, dt_bias, A_log, norm_w, S, self.y, stream)
+        return P.project_out(self.cfg, self.N, self.y, w_out, stream)

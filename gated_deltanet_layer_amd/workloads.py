@@ -33,7 +33,7 @@ CONV_K = 4
 _STREAM = {
     "lengths": 1, "conv_w": 2, "norm_w": 3, "dt_bias": 4, "A_log": 5,
     "S0": 6, "conv0": 7, "qkv": 8, "z": 9, "b": 10, "a": 11,
-    "x": 12, "w_qkv": 13, "w_gate": 14, "w_beta": 15, "w_alpha": 16, "w_out": 17,
+    "x": 12, "w_qkv": 13, "w_gate": 14, "w_beta": 15, "w_alpha": 16, "w_out": 17, "y": 18,
 }
 
 # Hidden sizes of the two models' layer input (the page's section
@@ -179,6 +179,7 @@ def generate_block(w: Workload, hidden: int, max_tokens: Optional[int] = None,
         ~ N(0, 1/hidden), so that the projected streams are ~ N(0, 1) like
         the mixer's own synthetic inputs
       w_out [hidden, Hv*d] ~ N(0, 1/(Hv*d))
+      y [T, Hv*d] ~ N(0, 1)   (ssm_out's input, for testing it on its own)
     The mixer streams qkv, z, b, a of ``generate`` are dropped: the block
     computes them from x."""
     if w.act != "bf16":
@@ -195,6 +196,8 @@ def generate_block(w: Workload, hidden: int, max_tokens: Optional[int] = None,
     out["w_beta"] = bf16_bits(_normal(seed, "w_beta", (Hv, hidden), 0.0, s_in))
     out["w_alpha"] = bf16_bits(_normal(seed, "w_alpha", (Hv, hidden), 0.0, s_in))
     out["w_out"] = bf16_bits(_normal(seed, "w_out", (hidden, Hv * d), 0.0, 1.0 / np.sqrt(Hv * d)))
+    # A stand-in for the mixer's output, to drive ssm_out on its own.
+    out["y"] = bf16_bits(_normal(seed, "y", lead + (Hv * d,)))
     return out
 
 

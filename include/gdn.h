@@ -4,8 +4,10 @@
  *
  * The mixer is the one the xwen CLAUDE.md page specifies for the Qwen 3.6
  * hybrid layers (section "Architecture cheat sheet", gated DeltaNet
- * paragraph). It starts from the already projected fused qkv stream and ends
- * after the gated RMSNorm; the projections around it are not part of it.
+ * paragraph). Its core starts from the already projected fused qkv stream and
+ * ends after the gated RMSNorm; gdn_in_proj and gdn_out_proj add the bf16
+ * projections before and after it (the layer input x -> qkv, z and the gate
+ * logits; y -> the layer output).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -248,6 +250,38 @@ GDN_API gdn_status gdn_decode_verify(const gdn_config *cfg, int32_t n_seqs, int3
  */
 GDN_API gdn_status gdn_gated_rmsnorm(const gdn_config *cfg, int64_t n_rows, const void *o, const void *z,
                              const float *norm_w, void *y, gdn_stream_t stream);
+
+/*
+ * gdn_in_proj -- the four input projections of the layer input (the page's
+ * gated DeltaNet paragraph: attn_qkv, attn_gate, ssm_beta, ssm_alpha, each a
+ * Linear without bias applied to x), as one bf16 product on the matrix cores:
+ *   qkv = x W_qkv^T, z = x W_gate^T, beta_logit = x W_beta^T, alpha_logit = x W_alpha^T
+ *   x            [T][hidden]      bf16, 16-byte aligned
+ *   w_qkv        [C][hidden]      bf16, 16-byte aligned (one row per output)
+ *   w_gate       [Hv*d][hidden]   bf16, 16-byte aligned
+ *   w_beta,
+ *   w_alpha      [Hv][hidden]     bf16, 16-byte aligned
+ *   qkv [T][C], z [T][Hv][d], beta_logit, alpha_logit [T][Hv]: bf16
+ * fp32 accumulation; each output rounded once to bf16 (nearest even). The
+ * act dtype of cfg must be GDN_BF16 and hidden a multiple of 64 (else
+ * GDN_E_UNSUPPORTED). Outputs must not overlap each other or the inputs.
+ * n_tokens may be 0.
+ */
+GDN_API gdn_status gdn_in_proj(const gdn_config *cfg, int32_t n_tokens, int32_t hidden, const void *x,
+                               const void *w_qkv, const void *w_gate, const void *w_beta, const void *w_alpha,
+                               void *qkv, void *z, void *beta_logit, void *alpha_logit, gdn_stream_t stream);
+
+/*
+ * gdn_out_proj -- ssm_out, the projection after the gated RMSNorm (the page's
+ * gated DeltaNet paragraph): out = y W_out^T.
+ *   y      [T][Hv*d]       bf16, 16-byte aligned
+ *   w_out  [hidden][Hv*d]  bf16, 16-byte aligned (one row per output)
+ *   out    [T][hidden]     bf16
+ * fp32 accumulation, each output rounded once to bf16. The act dtype of cfg
+ * must be GDN_BF16. out must not overlap y or w_out. n_tokens may be 0.
+ */
+GDN_API gdn_status gdn_out_proj(const gdn_config *cfg, int32_t n_tokens, int32_t hidden, const void *y,
+                                const void *w_out, void *out, gdn_stream_t stream);
 
 /* A static, NUL-terminated description of a status code. */
 GDN_API const char *gdn_status_string(gdn_status status);

@@ -213,23 +213,28 @@ class Oracle:
 
     def block(self, cu, n_qk_heads: int, n_v_heads: int, head_dim: int, x, w_qkv, w_gate, w_beta,
               w_alpha, w_out, conv_w, dt_bias, A_log, norm_w, conv_in, S_in, round_act: bool = True,
-              l2_eps: float = L2_EPS, norm_eps: float = NORM_EPS, l2_mode: int = L2_CLAMP):
+              round_o: bool = False, l2_eps: float = L2_EPS, norm_eps: float = NORM_EPS,
+              l2_mode: int = L2_CLAMP):
         """The token-mixer block from the layer input x [T, hidden]: the input
-        projections, the mixer (``layer``), then ssm_out (the page's gated
-        DeltaNet paragraph, in its order). With ``round_act`` the tensors at
-        the mixer's boundary (qkv, z, the logits in; y out) are rounded to
-        bf16, the dtype they are stored in. Returns the ``layer`` dict plus
-        ``proj`` (the in-projections, rounded as the mixer saw them) and
-        ``out`` [T, hidden]."""
+        projections, the mixer's steps (conv/gates, delta rule, gated RMSNorm),
+        then ssm_out (the page's gated DeltaNet paragraph, in its order).
+
+        With ``round_act`` the tensors that cross the mixer's boundary (qkv,
+        z, the logits in; y out) are rounded to bf16, the dtype they are
+        stored in; with ``round_o`` also the readout o between the delta rule
+        and the norm (a path that stores o in bf16 there). Returns the step
+        outputs (as ``layer``) plus ``proj`` (the in-projections as the mixer
+        saw them) and ``out`` [T, hidden]."""
         rnd = round_bf16 if round_act else _f64
-        pr = {k: rnd(v) for k, v in self.in_proj(n_qk_heads, n_v_heads, head_dim, x, w_qkv, w_gate,
-                                                   w_beta, w_alpha).items()}
-        r = self.layer(cu, n_qk_heads, n_v_heads, head_dim, pr["qkv"], pr["z"], pr["b"], pr["a"],
-                       conv_w, dt_bias, A_log, norm_w, conv_in, S_in, l2_eps=l2_eps, norm_eps=norm_eps,
-                       l2_mode=l2_mode)
+        Hqk, Hv, d = n_qk_heads, n_v_heads, head_dim
+        pr = {k: rnd(v) for k, v in self.in_proj(Hqk, Hv, d, x, w_qkv, w_gate, w_beta, w_alpha).items()}
+        r = self.conv_gate_prep(cu, Hqk, Hv, d, pr["qkv"], pr["b"], pr["a"], conv_w, dt_bias, A_log, conv_in,
+                                l2_eps, l2_mode)
+        o, S_out = self.delta_rule(cu, Hqk, Hv, d, r["q"], r["k"], r["v"], r["beta"], r["g"], S_in)
+        o_n = round_bf16(o) if (round_act and round_o) else o
+        y = self.gated_rmsnorm(o_n, pr["z"], norm_w, norm_eps)
         T = pr["qkv"].shape[0]
-        y = rnd(r["y"]).reshape(T, n_v_heads * head_dim)
-        r.update(proj=pr, out=self.linear(y, w_out))
+        r.update(proj=pr, o=o, S_out=S_out, y=y, out=self.linear(rnd(y).reshape(T, Hv * d), w_out))
         return r
 
 

@@ -486,16 +486,20 @@ def pin_block_composition(orc):
     eye = np.eye(hidden)
     ws = [eye[cuts[i]:cuts[i + 1]] for i in range(4)]
     w_out = np.eye(hidden)[:, :Hv * d]                   # out[:, :Hv*d] = y, the rest 0
-    for rnd in (False, True):
+    import oracle
+    for rnd, rnd_o in ((False, False), (True, False), (True, True)):
         r = orc.block(lx["cu_seqlens"], Hqk, Hv, d, x, *ws, w_out, lx["conv_w"], lx["dt_bias"],
-                      lx["A_log"], lx["norm_w"], lx["conv0"], lx["S0"], round_act=rnd)
-        import oracle
+                      lx["A_log"], lx["norm_w"], lx["conv0"], lx["S0"], round_act=rnd, round_o=rnd_o)
         f = oracle.round_bf16 if rnd else (lambda a: a)
         ref = orc.layer(lx["cu_seqlens"], Hqk, Hv, d, f(lx["qkv"]), f(lx["z"]), f(lx["b"]), f(lx["a"]),
                         lx["conv_w"], lx["dt_bias"], lx["A_log"], lx["norm_w"], lx["conv0"], lx["S0"])
-        assert np.array_equal(r["out"][:, :Hv * d], f(ref["y"]).reshape(T, -1)), rnd
-        assert np.array_equal(r["out"][:, Hv * d:], np.zeros((T, hidden - Hv * d))), rnd
-        assert np.array_equal(r["S_out"], ref["S_out"]), rnd
+        y = ref["y"]
+        if rnd_o:   # the norm reads the readout after its bf16 rounding
+            y = orc.gated_rmsnorm(oracle.round_bf16(ref["o"]), f(lx["z"]), lx["norm_w"])
+        assert np.array_equal(r["out"][:, :Hv * d], f(y).reshape(T, -1)), (rnd, rnd_o)
+        assert np.array_equal(r["out"][:, Hv * d:], np.zeros((T, hidden - Hv * d))), (rnd, rnd_o)
+        assert np.array_equal(r["S_out"], ref["S_out"]), (rnd, rnd_o)
+        assert not rnd_o or not np.array_equal(y, ref["y"]), "rounding o must change y"
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

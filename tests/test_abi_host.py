@@ -201,3 +201,35 @@ def test_checkpoint_and_guard_validation(lib):
     assert lib.gdn_state_check(FAKE[0], 16, None, None) == B.GDN_E_INVALID_ARG
     assert lib.gdn_state_check(FAKE[0] + 4, 16, FAKE[1], None) == B.GDN_E_INVALID_ARG  # S not 16-byte aligned
     assert lib.gdn_state_check(FAKE[0], -1, FAKE[1], None) == B.GDN_E_INVALID_ARG
+
+
+def test_projection_validation(lib):
+    cfg = B.make_config(2, 4, "bf16")
+    p = FAKE[:9]   # x, w_qkv, w_gate, w_beta, w_alpha, qkv, z, beta_logit, alpha_logit
+    call = lambda t, h, ptrs, c=cfg: lib.gdn_in_proj(ctypes.byref(c), t, h, *ptrs, None)
+    assert call(0, 64, p) == B.GDN_OK
+    assert call(-1, 64, p) == B.GDN_E_INVALID_ARG
+    assert call(4, 0, p) == B.GDN_E_INVALID_ARG
+    assert call(4, 96, p) == B.GDN_E_UNSUPPORTED          # hidden not a multiple of 64
+    assert call(4, 64, p, B.make_config(2, 4, "f32")) == B.GDN_E_UNSUPPORTED
+    for i, bad in ((0, FAKE[0] + 8), (1, FAKE[1] + 8), (6, FAKE[6] + 1)):   # misaligned operands
+        q = p[:]
+        q[i] = bad
+        assert call(4, 64, q) == B.GDN_E_INVALID_ARG, i
+    q = p[:]
+    q[6] = q[5] + 2                                       # z overlaps qkv
+    assert call(4, 64, q) == B.GDN_E_INVALID_ARG
+    q = p[:]
+    q[5] = q[0]                                           # qkv on top of x
+    assert call(4, 64, q) == B.GDN_E_INVALID_ARG
+    q = p[:]
+    q[3] = None
+    assert call(4, 64, q) == B.GDN_E_INVALID_ARG
+
+    out = lambda t, h, y, w, o, c=cfg: lib.gdn_out_proj(ctypes.byref(c), t, h, y, w, o, None)
+    assert out(0, 80, *FAKE[:3]) == B.GDN_OK
+    assert out(2, 0, *FAKE[:3]) == B.GDN_E_INVALID_ARG
+    assert out(2, 80, *FAKE[:3], c=B.make_config(2, 4, "f32")) == B.GDN_E_UNSUPPORTED
+    assert out(2, 80, FAKE[0], FAKE[1], FAKE[0] + 64) == B.GDN_E_INVALID_ARG   # out overlaps y
+    assert out(2, 80, FAKE[0] + 2, FAKE[1], FAKE[2]) == B.GDN_E_INVALID_ARG    # y misaligned
+    assert out(2, 80, FAKE[0], None, FAKE[2]) == B.GDN_E_INVALID_ARG
