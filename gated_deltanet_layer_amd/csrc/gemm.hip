@@ -40,28 +40,83 @@ constexpr int kRowBytes = kBK * 2;
 constexpr int kGemmThreads = 256;
 constexpr int kGroupM = 4;        // row tiles per group in the tile walk
 constexpr int kGemmXcds = 8;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// Per-lane source addresses of the 8 loads of a k-tile. A vector value, not
+// an array: the compiler may move a private array into LDS or scratch.
+typedef uint64_t u64x8 __attribute__((ext_vector_type(8)));
 
-__device__ __forceinline__ int seg_of(const GemmParams &p, int n) {
-  int s = 0;
-#pragma unroll
-  for (int i = 1; i < kMaxSeg; ++i)
-    if (i < p.n_seg && n >= p.start[i]) s = i;
-  return s;
-}
-
-// Element s of a kernel-argument array, selected with constant indices (a
-// dynamic index would copy the array to private memory).
 template <typename T>
-__device__ __forceinline__ T pick(const T (&a)[kMaxSeg], int s) {
-  T r = a[0];
-#pragma unroll
-  for (int i = 1; i < kMaxSeg; ++i)
-    if (s == i) r = a[i];
-  return r;
+__device__ __forceinline__ T sel4(int s, T a0, T a1, T a2, T a3) {
+  return s == 0 ? a0 : s == 1 ? a1 : s == 2 ? a2 : a3;
 }
+
+// The segment table, read once into scalars. Indexing the kernel argument's
+// arrays with a runtime segment number would make the compiler copy the whole
+// argument to private memory (or LDS) first.
+struct Segs {
+  int n_seg, N, s1, s2, s3;
+  const uint16_t *w0, *w1, *w2, *w3;
+  uint16_t *o0, *o1, *o2, *o3;
+  int64_t l0, l1, l2, l3;
+
+  __device__ __forceinline__ explicit Segs(const GemmParams &p)
+      : n_seg(p.n_seg), N(p.N), s1(p.start[1]), s2(p.start[2]), s3(p.start[3]),
+        w0(p.w[0]), w1(p.w[1]), w2(p.w[2]), w3(p.w[3]), o0(p.out[0]), o1(p.out[1]), o2(p.out[2]),
+        o3(p.out[3]), l0(p.ld[0]), l1(p.ld[1]), l2(p.ld[2]), l3(p.ld[3]) {}
+  // Segment of column n.
+  __device__ __forceinline__ int seg(int n) const {
+    return (n_seg > 1 && n >= s1) + (n_seg > 2 && n >= s2) + (n_seg > 3 && n >= s3);
+  }
+  __device__ __forceinline__ int start(int s) const { return sel4(s, 0, s1, s2, s3); }
+  __device__ __forceinline__ int end(int s) const { return s + 1 < n_seg ? sel4(s, s1, s2, s3, N) : N; }
+  __device__ __forceinline__ const uint16_t *w(int s) const { return sel4(s, w0, w1, w2, w3); }
+  __device__ __forceinline__ uint16_t *out(int s) const { return sel4(s, o0, o1, o2, o3); }
+  __device__ __forceinline__ int64_t ld(int s) const { return sel4(s, l0, l1, l2, l3); }
+};
 
 // Byte offset of chunk c of LDS row r.
 __device__ __forceinline__ int lds_off(int r, int c) { return r * kRowBytes + ((c ^ (r & 7)) << 4); }
+
+// Epilogue: acc[i][j] of this lane holds out[mrow + 16 i][ncol + 16 j + e],
+// e = 0..3 (4 consecutive columns: one 8-byte store when they stay in one
+// segment and are aligned, else one 2-byte store each).
+// Four columns n .. n+3 of row m that cross a segment end, the last column or
+// an 8-byte boundary: one 2-byte store each. Kept out of line so that the
+// epilogue loop stays small enough to unroll (the accumulators then stay in
+// registers).
+__device__ __noinline__ void store4_split(Segs g, int m, int n, uint32_t lo, uint32_t hi) {
+  for (int e = 0; e < 4; ++e) {
+    const int ne = n + e;
+    if (ne < g.N) {
+      const int se = g.seg(ne);
+      const uint16_t h = static_cast<uint16_t>(((e < 2 ? lo : hi) >> (16 * (e & 1))) & 0xffff);
+      g.out(se)[static_cast<int64_t>(m) * g.ld(se) + (ne - g.start(se))] = h;
+    }
+  }
+}
+
+template <int WN>
+__device__ __forceinline__ void gemm_epilogue(const Segs &g, int M, const f32x4 (&acc)[8][WN], int mrow, int ncol) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+      const int m = mrow + 16 * i, n = ncol + 16 * j;
+      const uint32_t lo = static_cast<uint32_t>(f32_to_bf16(acc[i][j][0])) |
+                          (static_cast<uint32_t>(f32_to_bf16(acc[i][j][1])) << 16);
+      const uint32_t hi = static_cast<uint32_t>(f32_to_bf16(acc[i][j][2])) |
+                          (static_cast<uint32_t>(f32_to_bf16(acc[i][j][3])) << 16);
+      if (m < M && n < g.N) {
+        const int s = g.seg(n);
+        uint16_t *dst = g.out(s) + static_cast<int64_t>(m) * g.ld(s) + (n - g.start(s));
+        if (n + 4 <= g.end(s) && (reinterpret_cast<uintptr_t>(dst) & 7) == 0)
+          *reinterpret_cast<uint2 *>(dst) = make_uint2(lo, hi);
+        else
+          store4_split(g, m, n, lo, hi);
+      }
+    }
+  }
+}
 
 template <int WN>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmParams p, int tiles_m, int tiles_n, int per_xcd) {
@@ -85,39 +140,48 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmParams p, int ti
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int wr = wave >> 1, wc = wave & 1;
   const int K = p.K;
+  const Segs g(p);
 
   // Global sources of this thread's chunks: row (tid >> 3) + 32 i, chunk tid & 7.
   const int lrow = tid >> 3, lchunk = tid & 7;
-  const uint16_t *asrc[kAChunks];
-  const uint16_t *bsrc[kBChunks];
+  u64x8 asrc, bsrc = {};
 #pragma unroll
   for (int i = 0; i < kAChunks; ++i) {
     const int m = min(m0 + lrow + 32 * i, p.M - 1);
-    asrc[i] = p.x + static_cast<int64_t>(m) * K + 8 * lchunk;
+    asrc[i] = reinterpret_cast<uint64_t>(p.x + static_cast<int64_t>(m) * K + 8 * lchunk);
   }
 #pragma unroll
   for (int i = 0; i < kBChunks; ++i) {
     const int n = min(n0 + lrow + 32 * i, p.N - 1);
-    const int s = seg_of(p, n);
-    bsrc[i] = pick(p.w, s) + static_cast<int64_t>(n - pick(p.start, s)) * K + 8 * lchunk;
+    const int s = g.seg(n);
+    bsrc[i] = reinterpret_cast<uint64_t>(g.w(s) + static_cast<int64_t>(n - g.start(s)) * K + 8 * lchunk);
   }
   const int st_off = lds_off(lrow, lchunk);   // + 32 i rows (same slot: 32 i is a multiple of 8)
 
-  uint4 ra[kAChunks], rb[kBChunks];
-  auto load = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < kAChunks; ++i) ra[i] = *reinterpret_cast<const uint4 *>(asrc[i] + kt * kBK);
-#pragma unroll
-    for (int i = 0; i < kBChunks; ++i) rb[i] = *reinterpret_cast<const uint4 *>(bsrc[i] + kt * kBK);
-  };
-  auto store = [&](int buf) {
-    uint8_t *a = smem + buf * (kABytes + kBBytes);
-    uint8_t *b = a + kABytes;
-#pragma unroll
-    for (int i = 0; i < kAChunks; ++i) *reinterpret_cast<uint4 *>(a + st_off + 32 * i * kRowBytes) = ra[i];
-#pragma unroll
-    for (int i = 0; i < kBChunks; ++i) *reinterpret_cast<uint4 *>(b + st_off + 32 * i * kRowBytes) = rb[i];
-  };
+  // Staging registers of the next k-tile: native 4 x u32 vectors (HIP's
+  // union-based uint4 is kept in memory, which here meant LDS or scratch and
+  // serialised every load against its store), indexed with literal constants.
+  static_assert(kAChunks == 8 && kBChunks <= 8, "staging is written out for at most 8 chunks");
+  u32x4 ra[8], rb[8];
+#define GDN_REP8(M) M(0) M(1) M(2) M(3) M(4) M(5) M(6) M(7)
+#define GDN_LD(i)                                                                            \
+  ra[i] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(asrc[i]) + koff); \
+  if constexpr (i < kBChunks)                                                                \
+    rb[i] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(bsrc[i]) + koff);
+#define GDN_ST(i)                                                                            \
+  *reinterpret_cast<u32x4 *>(sa_ + st_off + 32 * (i) * kRowBytes) = ra[i];                   \
+  if constexpr (i < kBChunks) *reinterpret_cast<u32x4 *>(sb_ + st_off + 32 * (i) * kRowBytes) = rb[i];
+#define GDN_GEMM_LOAD(kt)                                                                    \
+  do {                                                                                       \
+    const int koff = (kt) * kBK;                                                             \
+    GDN_REP8(GDN_LD)                                                                         \
+  } while (0)
+#define GDN_GEMM_STORE(buf)                                                                  \
+  do {                                                                                       \
+    uint8_t *sa_ = smem + (buf) * (kABytes + kBBytes);                                       \
+    uint8_t *sb_ = sa_ + kABytes;                                                            \
+    GDN_REP8(GDN_ST)                                                                         \
+  } while (0)
 
   f32x4 acc[8][WN];
 #pragma unroll
@@ -130,12 +194,16 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmParams p, int ti
   const int a_row0 = 128 * wr + fr, b_row0 = 16 * WN * wc + fr;
 
   const int KT = K / kBK;
-  load(0);
-  store(0);
+  GDN_GEMM_LOAD(0);
+  GDN_GEMM_STORE(0);
   __syncthreads();
   for (int kt = 0; kt < KT; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < KT) load(kt + 1);
+    if (kt + 1 < KT) GDN_GEMM_LOAD(kt + 1);
+    // Keep the next k-tile's loads in flight across the MFMAs: without these
+    // fences the compiler sinks each load next to its LDS store and waits
+    // for it there, one at a time.
+    asm volatile("" ::: "memory");
     const uint8_t *a = smem + cur * (kABytes + kBBytes);
     const uint8_t *b = a + kABytes;
 #pragma unroll
@@ -153,43 +221,138 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmParams p, int ti
         for (int j = 0; j < WN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < KT) store(cur ^ 1);
+    asm volatile("" ::: "memory");
+    if (kt + 1 < KT) GDN_GEMM_STORE(cur ^ 1);
     __syncthreads();
   }
 
-  // Epilogue: lane holds out[m][n .. n+3], m = row 16 i + (lane & 15), n = col 16 j + 4 (lane >> 4).
+#undef GDN_GEMM_LOAD
+#undef GDN_GEMM_STORE
+#undef GDN_LD
+#undef GDN_ST
+#undef GDN_REP8
+
+  gemm_epilogue<WN>(g, p.M, acc, m0 + 128 * wr + fr, n0 + 16 * WN * wc + 4 * fq);
+}
+
+// The same product with the operand tiles brought into LDS by the load
+// instructions themselves (16 bytes per lane, written at the wave's LDS
+// address + 16 * lane), in a ring of kStages k-tiles: the loads of k-tile
+// kt + 2 are issued as soon as every wave has finished k-tile kt - 1, so two
+// k-tiles of memory latency hide behind the MFMAs, and no registers stage the
+// data. Each lane loads the chunk that belongs in its slot of the swizzled
+// row: chunk (lane & 7) ^ (row & 7).
+constexpr int kStages = 3;
+constexpr int kMaxDmaWn = 5;      // kStages k-tiles of 256 + 32 WN rows fit the 160 KB of LDS
+constexpr bool kUseDma = true;
+
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  // This wave's loads except the newest N have landed in LDS, its LDS reads
+  // are done; then the workgroup barrier (which waits for nothing else, so
+  // the newest k-tile stays in flight).
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+template <int WN>
+__global__ __launch_bounds__(kGemmThreads) void gemm_dma_kernel(GemmParams p, int tiles_m, int tiles_n, int per_xcd) {
+  constexpr int BN = 32 * WN;
+  constexpr int kBChunks = BN * 8 / kGemmThreads;
+  constexpr int kLoads = 8 + kBChunks;            // loads per thread and k-tile
+  constexpr int kABytes = kBM * kRowBytes, kBBytes = BN * kRowBytes, kStage = kABytes + kBBytes;
+  static_assert(kBChunks <= 8, "at most 8 weight chunks per thread");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStage];
+
+  const int logical = (blockIdx.x % kGemmXcds) * per_xcd + blockIdx.x / kGemmXcds;
+  if (logical >= tiles_m * tiles_n) return;
+  const int group = logical / (kGroupM * tiles_n);
+  const int gm0 = group * kGroupM;
+  const int gsize = min(kGroupM, tiles_m - gm0);
+  const int in_group = logical - group * kGroupM * tiles_n;
+  const int tm = gm0 + in_group % gsize;
+  const int tn = in_group / gsize;
+  const int m0 = tm * kBM, n0 = tn * BN;
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int K = p.K;
+  const Segs g(p);
+
+  // Load i of this lane: row lrow + 32 i of the tile, the chunk for slot lane & 7.
+  const int lrow = tid >> 3;
+  const int gchunk = (lane & 7) ^ (lrow & 7);
+  u64x8 asrc, bsrc = {};
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int m = m0 + 128 * wr + 16 * i + fr;
-    if (m >= p.M) continue;
-#pragma unroll
-    for (int j = 0; j < WN; ++j) {
-      const int n = n0 + 16 * WN * wc + 16 * j + 4 * fq;
-      if (n >= p.N) continue;
-      const int s = seg_of(p, n);
-      const int e0 = n - pick(p.start, s);
-      const int end = s + 1 < p.n_seg ? pick(p.start, s + 1) : p.N;
-      uint16_t *dst = pick(p.out, s) + static_cast<int64_t>(m) * pick(p.ld, s) + e0;
-      const uint16_t h0 = f32_to_bf16(acc[i][j][0]), h1 = f32_to_bf16(acc[i][j][1]);
-      const uint16_t h2 = f32_to_bf16(acc[i][j][2]), h3 = f32_to_bf16(acc[i][j][3]);
-      if (n + 4 <= end && (reinterpret_cast<uintptr_t>(dst) & 7) == 0) {
-        uint2 v;
-        v.x = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
-        v.y = static_cast<uint32_t>(h2) | (static_cast<uint32_t>(h3) << 16);
-        *reinterpret_cast<uint2 *>(dst) = v;
-      } else {
-        const uint16_t h[4] = {h0, h1, h2, h3};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int ne = n + e;
-          if (ne < p.N) {
-            const int se = seg_of(p, ne);
-            pick(p.out, se)[static_cast<int64_t>(m) * pick(p.ld, se) + (ne - pick(p.start, se))] = h[e];
-          }
-        }
-      }
-    }
+    const int m = min(m0 + lrow + 32 * i, p.M - 1);
+    asrc[i] = reinterpret_cast<uint64_t>(p.x + static_cast<int64_t>(m) * K + 8 * gchunk);
   }
+#pragma unroll
+  for (int i = 0; i < kBChunks; ++i) {
+    const int n = min(n0 + lrow + 32 * i, p.N - 1);
+    const int s = g.seg(n);
+    bsrc[i] = reinterpret_cast<uint64_t>(g.w(s) + static_cast<int64_t>(n - g.start(s)) * K + 8 * gchunk);
+  }
+  const int wdst = 8 * wave * kRowBytes;          // this wave's 8 rows of load i: + 32 i rows
+
+#define GDN_REP8(M) M(0) M(1) M(2) M(3) M(4) M(5) M(6) M(7)
+#define GDN_DMA(i)                                                                                \
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint16_t *>(asrc[i]) + koff,           \
+                                   sa_ + wdst + 32 * (i) * kRowBytes, 16, 0, 0);                  \
+  if constexpr (i < kBChunks)                                                                     \
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint16_t *>(bsrc[i]) + koff,         \
+                                     sb_ + wdst + 32 * (i) * kRowBytes, 16, 0, 0);
+#define GDN_ISSUE(kt, stage)                                                                      \
+  do {                                                                                            \
+    uint8_t *sa_ = smem + (stage) * kStage;                                                       \
+    uint8_t *sb_ = sa_ + kABytes;                                                                 \
+    const int koff = (kt) * kBK;                                                                  \
+    GDN_REP8(GDN_DMA)                                                                             \
+  } while (0)
+
+  f32x4 acc[8][WN];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int fr = lane & 15, fq = lane >> 4;
+  const int a_row0 = 128 * wr + fr, b_row0 = 16 * WN * wc + fr;
+
+  const int KT = K / kBK;
+  GDN_ISSUE(0, 0);
+  if (KT > 1) GDN_ISSUE(1, 1);
+  int stage = 0;
+  for (int kt = 0; kt < KT; ++kt) {
+    if (kt + 1 < KT)
+      wait_vm_barrier<kLoads>();
+    else
+      wait_vm_barrier<0>();
+    if (kt + 2 < KT) GDN_ISSUE(kt + 2, stage == 0 ? 2 : stage - 1);
+    const uint8_t *a = smem + stage * kStage;
+    const uint8_t *b = a + kABytes;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 fa[8], fb[WN];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        fa[i] = *reinterpret_cast<const bf16x8 *>(a + lds_off(a_row0 + 16 * i, 4 * ks + fq));
+#pragma unroll
+      for (int j = 0; j < WN; ++j)
+        fb[j] = *reinterpret_cast<const bf16x8 *>(b + lds_off(b_row0 + 16 * j, 4 * ks + fq));
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+    }
+    stage = stage == kStages - 1 ? 0 : stage + 1;
+  }
+#undef GDN_ISSUE
+#undef GDN_DMA
+#undef GDN_REP8
+
+  gemm_epilogue<WN>(g, p.M, acc, m0 + 128 * wr + fr, n0 + 16 * WN * wc + 4 * fq);
 }
 
 template <int WN>
@@ -198,8 +361,12 @@ hipError_t launch_wn(const GemmParams &p, hipStream_t s) {
   const int tiles_m = (p.M + kBM - 1) / kBM, tiles_n = (p.N + BN - 1) / BN;
   const int tiles = tiles_m * tiles_n;
   const int per_xcd = (tiles + kGemmXcds - 1) / kGemmXcds;
-  hipLaunchKernelGGL(gemm_kernel<WN>, dim3(per_xcd * kGemmXcds), dim3(kGemmThreads), 0, s, p, tiles_m, tiles_n,
-                     per_xcd);
+  if constexpr (kUseDma && WN <= kMaxDmaWn)
+    hipLaunchKernelGGL(gemm_dma_kernel<WN>, dim3(per_xcd * kGemmXcds), dim3(kGemmThreads), 0, s, p, tiles_m,
+                       tiles_n, per_xcd);
+  else
+    hipLaunchKernelGGL(gemm_kernel<WN>, dim3(per_xcd * kGemmXcds), dim3(kGemmThreads), 0, s, p, tiles_m, tiles_n,
+                       per_xcd);
   return hipGetLastError();
 }
 
@@ -207,13 +374,13 @@ hipError_t launch_wn(const GemmParams &p, hipStream_t s) {
 
 // The column-tile width is chosen per call so that the number of rounds of
 // 256 concurrent tiles, times the tile width, is smallest (the last round of
-// a launch is often partly idle). Wider tiles than 5 fragments per wave do
-// not fit the registers next to the staging of the next k-tile.
+// a launch is often partly idle). Eight fragments per wave would spill.
+constexpr int kMaxWn = kUseDma ? kMaxDmaWn : 7;
 static int gemm_tile_wn(int M, int N) {
   const int tiles_m = (M + kBM - 1) / kBM;
-  int best = 5;
+  int best = kMaxWn;
   int64_t best_cost = -1;
-  for (int wn = 5; wn >= 4; --wn) {
+  for (int wn = kMaxWn; wn >= 4; --wn) {
     const int64_t tiles = static_cast<int64_t>(tiles_m) * ((N + 32 * wn - 1) / (32 * wn));
     const int64_t rounds = (tiles + 255) / 256;
     const int64_t cost = rounds * (32 * wn + 16);   // + a fixed per-tile cost
@@ -224,8 +391,12 @@ static int gemm_tile_wn(int M, int N) {
 
 hipError_t launch_gemm(const GemmParams &p, hipStream_t s) {
   if (p.M == 0 || p.N == 0) return hipSuccess;
-  if (gemm_tile_wn(p.M, p.N) == 4) return launch_wn<4>(p, s);
-  return launch_wn<5>(p, s);
+  switch (gemm_tile_wn(p.M, p.N)) {
+    case 4: return launch_wn<4>(p, s);
+    case 5: return launch_wn<5>(p, s);
+    case 6: return launch_wn<6>(p, s);
+    default: return launch_wn<7>(p, s);
+  }
 }
 
 }  // namespace gdn
