@@ -355,6 +355,118 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_dma_kernel(GemmParams p, in
   gemm_epilogue<WN>(g, p.M, acc, m0 + 128 * wr + fr, n0 + 16 * WN * wc + 4 * fq);
 }
 
+// Few rows (decode: M <= 64): the product is bound by streaming the weights
+// from HBM once, and there are too few row tiles to fill the chip. A block
+// owns 16 * NF output columns and all M rows (MF fragments of 16); its 8
+// waves split the contraction into contiguous ranges of 32-wide steps and
+// read both operands straight into MFMA fragments (16 bytes per lane: the
+// weights from HBM, the few activation rows from L2), kSkU steps of loads in
+// flight before their MFMAs; the 8 partial sums meet in LDS.
+constexpr int kSkWaves = 8;
+constexpr int kSkU = 4;
+
+template <int MF, int NF>
+__global__ __launch_bounds__(kSkWaves * kWave) void gemm_skinny_kernel(GemmParams p) {
+  const Segs g(p);
+  const int K = p.K, M = p.M;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int fr = lane & 15, fq = lane >> 4;
+  const int n0 = blockIdx.x * 16 * NF;
+
+  // Row pointers at this lane's 8 contraction indices of a step (8 fq ..).
+  u64x8 arow = {}, brow = {};
+#pragma unroll
+  for (int i = 0; i < MF; ++i)
+    arow[i] = reinterpret_cast<uint64_t>(p.x + static_cast<int64_t>(min(16 * i + fr, M - 1)) * K + 8 * fq);
+#pragma unroll
+  for (int j = 0; j < NF; ++j) {
+    const int n = min(n0 + 16 * j + fr, p.N - 1);
+    const int s = g.seg(n);
+    brow[j] = reinterpret_cast<uint64_t>(g.w(s) + static_cast<int64_t>(n - g.start(s)) * K + 8 * fq);
+  }
+
+  f32x4 acc[MF][NF];
+#pragma unroll
+  for (int i = 0; i < MF; ++i)
+#pragma unroll
+    for (int j = 0; j < NF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int steps = K / 32;
+  const int s_lo = wave * steps / kSkWaves, s_hi = (wave + 1) * steps / kSkWaves;
+  auto step = [&](int st, bf16x8 (&fa)[MF], bf16x8 (&fb)[NF]) {
+#pragma unroll
+    for (int i = 0; i < MF; ++i)
+      fa[i] = *reinterpret_cast<const bf16x8 *>(reinterpret_cast<const uint16_t *>(arow[i]) + 32 * st);
+#pragma unroll
+    for (int j = 0; j < NF; ++j)
+      fb[j] = *reinterpret_cast<const bf16x8 *>(reinterpret_cast<const uint16_t *>(brow[j]) + 32 * st);
+  };
+  int s0 = s_lo;
+  for (; s0 + kSkU <= s_hi; s0 += kSkU) {
+    bf16x8 fa[kSkU][MF], fb[kSkU][NF];
+#pragma unroll
+    for (int u = 0; u < kSkU; ++u) step(s0 + u, fa[u], fb[u]);
+    // Every load of the group goes out before the first MFMA waits on one.
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kSkU; ++u)
+#pragma unroll
+      for (int i = 0; i < MF; ++i)
+#pragma unroll
+        for (int j = 0; j < NF; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[u][j], fa[u][i], acc[i][j], 0, 0, 0);
+  }
+  for (; s0 < s_hi; ++s0) {
+    bf16x8 fa[MF], fb[NF];
+    step(s0, fa, fb);
+#pragma unroll
+    for (int i = 0; i < MF; ++i)
+#pragma unroll
+      for (int j = 0; j < NF; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+  }
+
+  // Partial sums of the 8 waves through LDS; wave w then finishes fragments
+  // f = w, w + 8, ... of the MF x NF and stores them.
+  __shared__ f32x4 part[kSkWaves][MF * NF][kWave];
+#pragma unroll
+  for (int i = 0; i < MF; ++i)
+#pragma unroll
+    for (int j = 0; j < NF; ++j) part[wave][i * NF + j][lane] = acc[i][j];
+  __syncthreads();
+  for (int f = wave; f < MF * NF; f += kSkWaves) {
+    f32x4 sum = part[0][f][lane];
+#pragma unroll
+    for (int w = 1; w < kSkWaves; ++w) sum += part[w][f][lane];
+    const int i = f / NF, j = f % NF;
+    const int m = 16 * i + fr, n = n0 + 16 * j + 4 * fq;
+    const uint32_t lo = static_cast<uint32_t>(f32_to_bf16(sum[0])) | (static_cast<uint32_t>(f32_to_bf16(sum[1])) << 16);
+    const uint32_t hi = static_cast<uint32_t>(f32_to_bf16(sum[2])) | (static_cast<uint32_t>(f32_to_bf16(sum[3])) << 16);
+    if (m < M && n < g.N) {
+      const int sg = g.seg(n);
+      uint16_t *dst = g.out(sg) + static_cast<int64_t>(m) * g.ld(sg) + (n - g.start(sg));
+      if (n + 4 <= g.end(sg) && (reinterpret_cast<uintptr_t>(dst) & 7) == 0)
+        *reinterpret_cast<uint2 *>(dst) = make_uint2(lo, hi);
+      else
+        store4_split(g, m, n, lo, hi);
+    }
+  }
+}
+
+template <int MF, int NF>
+hipError_t launch_skinny(const GemmParams &p, hipStream_t s) {
+  const int blocks = (p.N + 16 * NF - 1) / (16 * NF);
+  hipLaunchKernelGGL((gemm_skinny_kernel<MF, NF>), dim3(blocks), dim3(kSkWaves * kWave), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int MF>
+hipError_t launch_skinny_m(const GemmParams &p, hipStream_t s) {
+  // Two fragments of columns per block when that still gives a block per CU.
+  if ((p.N + 31) / 32 >= 256) return launch_skinny<MF, 2>(p, s);
+  return launch_skinny<MF, 1>(p, s);
+}
+
 template <int WN>
 hipError_t launch_wn(const GemmParams &p, hipStream_t s) {
   constexpr int BN = 32 * WN;
@@ -391,6 +503,9 @@ static int gemm_tile_wn(int M, int N) {
 
 hipError_t launch_gemm(const GemmParams &p, hipStream_t s) {
   if (p.M == 0 || p.N == 0) return hipSuccess;
+  if (p.M <= 16) return launch_skinny_m<1>(p, s);
+  if (p.M <= 32) return launch_skinny_m<2>(p, s);
+  if (p.M <= 64) return launch_skinny_m<4>(p, s);
   switch (gemm_tile_wn(p.M, p.N)) {
     case 4: return launch_wn<4>(p, s);
     case 5: return launch_wn<5>(p, s);
