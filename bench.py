@@ -26,6 +26,12 @@ on the stream the kernels run on:
     o written.
 The CPU baseline is the fp64 oracle, single-threaded, over the whole prefill
 workload once.
+
+"block" times the projections around the mixer as well (gdn_in_proj ->
+mixer -> gdn_out_proj) on the 27B prefill layer and the 35B-A3B batch-64
+decode layer, with each projection's roofline: 2 M N K flop against the bf16
+MFMA peak for prefill, and its weights plus activations in and out against
+HBM for decode (the weights are streamed once per token batch).
 """
 from __future__ import annotations
 
@@ -254,6 +260,162 @@ def bench_prefill(steps: int, warmup: int):
                           "flop_per_launch": flops, "avg_launch_us": round(core_ms * 1e3, 2)})
 
 
+def _events(n):
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+
+def _mean_ms(evs):
+    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+
+def bench_block(steps: int, warmup: int):
+    """The whole token-mixer block: gdn_in_proj -> the mixer -> gdn_out_proj.
+
+    Prefill on the 27B layer (T = 4096, hidden 5120, 16 K-heads, 48 V-heads)
+    with the mixer's three calls in between, plain launches and as one graph;
+    decode on the 35B-A3B layer (64 sequences, hidden 2048, 32 V-heads) with
+    gdn_decode_fused in between, 64 steps as one graph. The projections are
+    also timed one by one (HIP events around each launch on its stream)."""
+    out = {}
+    # ---- prefill block
+    w = wl.WORKLOADS[3]
+    hidden = wl.HIDDEN[w.n_v_heads]
+    x = wl.generate_block(w, hidden)
+    t = {k: dev(v) for k, v in x.items() if k != "y"}
+    cfg = B.make_config(w.n_qk_heads, w.n_v_heads, w.act)
+    T = int(x["cu_seqlens"][-1])
+    run = Lyr.Block(cfg, 1, T, hidden)
+    conv_out = torch.empty_like(t["conv0"])
+    S_out = torch.empty_like(t["S0"])
+    P = run.proj
+    wargs = (t["w_qkv"], t["w_gate"], t["w_beta"], t["w_alpha"])
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0][0].record()
+        P.project_in(cfg, T, t["x"], *wargs, None)
+        if evs is not None:
+            evs[0][1].record()
+        run.mixer(t["cu_seqlens"], P.qkv, P.z, P.b, P.a, t["conv_w"], t["dt_bias"], t["A_log"], t["norm_w"],
+                  t["conv0"], conv_out, t["S0"], S_out)
+        if evs is not None:
+            evs[1][0].record()
+        P.project_out(cfg, T, run.mixer.y, t["w_out"], None)
+        if evs is not None:
+            evs[1][1].record()
+
+    for _ in range(warmup):
+        step()
+    ev_in, ev_out = _events(steps), _events(steps)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        step((ev_in[i], ev_out[i]))
+    end.record()
+    torch.cuda.synchronize()
+    plain_ms = start.elapsed_time(end)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    graph_ms = start.elapsed_time(end)
+    del g
+    C, Z, Hv = P.qkv.shape[1], P.z.shape[1] * P.z.shape[2], w.n_v_heads
+    n_in = C + Z + 2 * Hv
+    gemms = {}
+    for name, evs, (M, N, K) in (("in_proj", ev_in, (T, n_in, hidden)), ("out_proj", ev_out, (T, hidden, Z))):
+        ms = _mean_ms(evs)
+        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        gemms[name] = {"M": M, "N": N, "K": K, "avg_launch_us": round(ms * 1e3, 2),
+                       "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS,
+                                    "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4)}}
+    best = min(plain_ms, graph_ms)
+    out["prefill"] = {"workload": f"27B block prefill T={T} hidden={hidden} Hqk=16 Hv=48 bf16",
+                      "tokens_per_s": round(T * steps / (best * 1e-3), 1),
+                      "ms_per_step": round(best / steps, 4),
+                      "modes": {"plain_ms_per_step": round(plain_ms / steps, 4),
+                                "graph_ms_per_step": round(graph_ms / steps, 4)},
+                      "gemms": gemms}
+    del t, run, x
+    torch.cuda.empty_cache()
+
+    # ---- decode block (35B-A3B, 64 sequences)
+    w = wl.WORKLOADS[4]
+    hidden = wl.HIDDEN[w.n_v_heads]
+    dsteps = 64
+    x = wl.generate_block(w, hidden, max_steps=dsteps)
+    t = {k: dev(v) for k, v in x.items() if k != "y"}
+    cfg = B.make_config(w.n_qk_heads, w.n_v_heads, w.act)
+    N = w.n_seqs
+    run = Lyr.DecodeBlock(cfg, N, hidden, t["conv0"].clone())
+    S = t["S0"].clone()
+    P = run.proj
+    wargs = (t["w_qkv"], t["w_gate"], t["w_beta"], t["w_alpha"])
+
+    def dstep(s, evs=None):
+        if evs is not None:
+            evs[0][0].record()
+        P.project_in(cfg, N, t["x"][s], *wargs, None)
+        if evs is not None:
+            evs[0][1].record()
+        run.mixer(P.qkv, P.z, P.b, P.a, t["conv_w"], t["dt_bias"], t["A_log"], t["norm_w"], S, run.y)
+        if evs is not None:
+            evs[1][0].record()
+        P.project_out(cfg, N, run.y, t["w_out"], None)
+        if evs is not None:
+            evs[1][1].record()
+
+    for s in range(min(8, dsteps)):
+        dstep(s)
+    ev_in, ev_out = _events(dsteps), _events(dsteps)
+    torch.cuda.synchronize()
+    start.record()
+    for s in range(dsteps):
+        dstep(s, (ev_in[s], ev_out[s]))
+    end.record()
+    torch.cuda.synchronize()
+    plain_ms = start.elapsed_time(end)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for s in range(dsteps):
+            dstep(s)
+    g.replay()
+    torch.cuda.synchronize()
+    start.record()
+    g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    graph_ms = start.elapsed_time(end)
+    del g
+    C, Z = P.qkv.shape[1], P.z.shape[1] * P.z.shape[2]
+    n_in = C + Z + 2 * w.n_v_heads
+    gemms = {}
+    for name, evs, (M, Nn, K) in (("in_proj", ev_in, (N, n_in, hidden)), ("out_proj", ev_out, (N, hidden, Z))):
+        ms = _mean_ms(evs)
+        byts = 2 * (Nn * K + M * K + M * Nn)        # weights once, activations in and out (bf16)
+        gbs = byts / (ms * 1e-3) / 1e9
+        gemms[name] = {"M": M, "N": Nn, "K": K, "avg_launch_us": round(ms * 1e3, 2),
+                       "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                                    "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": byts}}
+    best = min(plain_ms, graph_ms)
+    out["decode_b64"] = {"workload": f"35B-A3B block decode {N} seqs hidden={hidden} Hqk=16 Hv=32 bf16, "
+                                     f"{dsteps} steps",
+                         "tokens_per_s": round(N * dsteps / (best * 1e-3), 1),
+                         "us_per_step": round(best * 1e3 / dsteps, 2),
+                         "modes": {"plain_us_per_step": round(plain_ms * 1e3 / dsteps, 2),
+                                   "graph_us_per_step": round(graph_ms * 1e3 / dsteps, 2)},
+                         "gemms": gemms}
+    return out
+
+
 def decode_kernel_bytes(w: wl.Workload) -> int:
     """Algorithmic bytes of one gdn_decode_step launch: S read + written, q, k,
     v, beta, g read, o written."""
@@ -447,7 +609,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-decode", action="store_true", help="skip the decode workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the oracle")
-    ap.add_argument("--only", choices=["prefill", "decode-b1", "decode-b64"], default=None,
+    ap.add_argument("--no-block", action="store_true", help="skip the block (projections + mixer)")
+    ap.add_argument("--only", choices=["prefill", "decode-b1", "decode-b64", "block"], default=None,
                     help="run one workload only (for counter collection)")
     ap.add_argument("--summarize-rocprof", metavar="DB", default=None,
                     help="print a per-kernel summary of a rocprofv3 results database and exit")
@@ -485,6 +648,9 @@ def main():
         d = bench_decode(2 if a.only == "decode-b1" else 4, graphs=not a.no_graph)
         print(json.dumps(d), flush=True)
         return
+    if a.only == "block":
+        print(json.dumps(bench_block(a.steps, a.warmup)), flush=True)
+        return
     log("prefill workload: T=4096 Hqk=16 Hv=48 bf16")
     pre = bench_prefill(a.steps, a.warmup)
     log(f"prefill: {pre['ms_per_step']:.3f} ms/step, core {pre['core_ms'] * 1e3:.1f} us")
@@ -495,6 +661,11 @@ def main():
             log(f"decode workload {wid}")
             decode.append(bench_decode(wid, graphs=not a.no_graph))
             log(json.dumps(decode[-1]))
+    block = None
+    if not a.no_block and a.only is None:
+        log("block: projections around the mixer")
+        block = bench_block(a.steps, a.warmup)
+        log(json.dumps(block))
     cpu = None
     if not a.no_cpu_baseline and a.only is None:
         log("cpu baseline (oracle)")
@@ -512,6 +683,7 @@ def main():
         "prefill_modes": pre["modes"],
         "roofline": pre["roofline"],
         "decode": decode,
+        "block": block,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
