@@ -70,14 +70,23 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    """sha256 over the HIP sources (the traffic counters are only valid for this build)."""
-    import glob
+# Source files behind each traffic record (plus the shared headers): a record
+# is only used while these are unchanged.
+TRAFFIC_SOURCES = {
+    "prefill_core": ("prefill.hip",), "prefill_prep": ("prep.hip",), "prefill_norm": ("norm.hip",),
+    "decode_b64": ("decode.hip",), "decode_b1": ("decode.hip",),
+    "decode_fused_b64": ("decode_fused.hip",), "decode_fused_b1": ("decode_fused.hip",),
+}
+
+
+def kernel_source_hash(key: str) -> str:
+    """sha256 over the HIP source of the kernel(s) behind a traffic record and
+    the shared device headers (the counters are only valid for that code)."""
     import hashlib
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h"))):
-        h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
+    for f in sorted(TRAFFIC_SOURCES[key]) + ["gdn_device.h", "gdn_internal.h"]:
+        h.update(f.encode())
+        with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
@@ -91,7 +100,8 @@ def measured_traffic(key: str):
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != kernel_source_hash() or key not in rec.get("kernels", {}):
+    k = rec.get("kernels", {}).get(key)
+    if k is None or k.get("source_sha256") != kernel_source_hash(key):
         return None
     k = rec["kernels"][key]
     return int(k["fetch_bytes"] + k["write_bytes"])
@@ -174,15 +184,15 @@ def write_traffic(dbs):
             ("prefill_prep", "prefill", ("prep_kernel",), "gdn_conv_gate_prep, T=4096 Hv=48 bf16"),
             ("prefill_norm", "prefill", ("norm_kernel",), "gdn_gated_rmsnorm, T=4096 Hv=48 bf16"),
             ("decode_b64", "decode_b64", ("decode_kernel",), "gdn_decode_step, batch 64, Hv=32"),
-            ("decode_fused_b64", "decode_b64", ("decode_fused_kernel",), "gdn_decode_fused, batch 64, Hv=32"),
+            ("decode_fused_b64", "decode_b64", ("decode_tokens_kernel<gdn::bf16_t, true>",), "gdn_decode_fused, batch 64, Hv=32"),
             ("decode_b1", "decode_b1", ("decode_kernel",), "gdn_decode_step, batch 1, Hv=32"),
-            ("decode_fused_b1", "decode_b1", ("decode_fused_kernel",), "gdn_decode_fused, batch 1, Hv=32")):
+            ("decode_fused_b1", "decode_b1", ("decode_tokens_kernel<gdn::bf16_t, true>",), "gdn_decode_fused, batch 1, Hv=32")):
         tot = [pick(run, sub) for sub in subs]
         if any(t is None for t in tot):
             continue
         kernels[key] = {"what": what, "fetch_bytes": int(sum(t[0] for t in tot)),
-                        "write_bytes": int(sum(t[1] for t in tot))}
-    rec = {"source_sha256": kernel_source_hash(),
+                        "write_bytes": int(sum(t[1] for t in tot)), "source_sha256": kernel_source_hash(key)}
+    rec = {
            "note": "HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch, separate "
                    "runs), scaled by what the same counters read for a plain 256 MiB device copy in the same run.",
            "calibration": {k: {"fetch_factor": round(v[2], 4), "write_factor": round(v[3], 4)}

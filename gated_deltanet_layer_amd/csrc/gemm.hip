@@ -14,12 +14,14 @@
 // Tiling for gfx950. A block of 4 waves owns a kBM x BN tile (BN = 32 * WN);
 // wave (wr, wc) owns rows 128 wr .. +127 and columns 16 WN wc .. +16 WN - 1,
 // i.e. 8 x WN accumulator tiles of 16 x 16 (v_mfma_f32_16x16x32_bf16). The
-// contraction runs in k-tiles of 64: both operand tiles are staged in LDS,
-// double-buffered, one barrier per k-tile, with the next k-tile's global loads
-// in flight during the current one's MFMAs. An LDS row is the 128 bytes of one
-// operand row in a k-tile, as 8 chunks of 16 bytes (8 k values); chunk c of
-// row r is stored at slot c ^ (r & 7), which makes both the 16-byte stores
+// contraction runs in k-tiles of 64 staged in a 3-deep LDS ring (see
+// gemm_dma_kernel), one barrier per k-tile. An LDS row is the 128 bytes of
+// one operand row in a k-tile, as 8 chunks of 16 bytes (8 k values); chunk c
+// of row r is stored at slot c ^ (r & 7), which makes both the 16-byte writes
 // and the 16-byte fragment reads free of bank conflicts.
+//
+// Up to 64 rows (decode) take gemm_skinny_kernel instead: the weights are
+// streamed once, and the work is split over the contraction.
 //
 // The weight fragment is the MFMA's first operand and the activation fragment
 // its second, so an accumulator lane holds 4 consecutive output columns of
@@ -40,7 +42,6 @@ constexpr int kRowBytes = kBK * 2;
 constexpr int kGemmThreads = 256;
 constexpr int kGroupM = 4;        // row tiles per group in the tile walk
 constexpr int kGemmXcds = 8;
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // Per-lane source addresses of the 8 loads of a k-tile. A vector value, not
 // an array: the compiler may move a private array into LDS or scratch.
 typedef uint64_t u64x8 __attribute__((ext_vector_type(8)));
@@ -118,133 +119,15 @@ __device__ __forceinline__ void gemm_epilogue(const Segs &g, int M, const f32x4 
   }
 }
 
-template <int WN>
-__global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmParams p, int tiles_m, int tiles_n, int per_xcd) {
-  constexpr int BN = 32 * WN;
-  constexpr int kAChunks = kBM * 8 / kGemmThreads;    // 16-byte chunks per thread and k-tile
-  constexpr int kBChunks = BN * 8 / kGemmThreads;
-  constexpr int kABytes = kBM * kRowBytes, kBBytes = BN * kRowBytes;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (kABytes + kBBytes)];
-
-  // Tile of this block.
-  const int logical = (blockIdx.x % kGemmXcds) * per_xcd + blockIdx.x / kGemmXcds;
-  if (logical >= tiles_m * tiles_n) return;
-  const int group = logical / (kGroupM * tiles_n);
-  const int gm0 = group * kGroupM;
-  const int gsize = min(kGroupM, tiles_m - gm0);
-  const int in_group = logical - group * kGroupM * tiles_n;
-  const int tm = gm0 + in_group % gsize;
-  const int tn = in_group / gsize;
-  const int m0 = tm * kBM, n0 = tn * BN;
-
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int wr = wave >> 1, wc = wave & 1;
-  const int K = p.K;
-  const Segs g(p);
-
-  // Global sources of this thread's chunks: row (tid >> 3) + 32 i, chunk tid & 7.
-  const int lrow = tid >> 3, lchunk = tid & 7;
-  u64x8 asrc, bsrc = {};
-#pragma unroll
-  for (int i = 0; i < kAChunks; ++i) {
-    const int m = min(m0 + lrow + 32 * i, p.M - 1);
-    asrc[i] = reinterpret_cast<uint64_t>(p.x + static_cast<int64_t>(m) * K + 8 * lchunk);
-  }
-#pragma unroll
-  for (int i = 0; i < kBChunks; ++i) {
-    const int n = min(n0 + lrow + 32 * i, p.N - 1);
-    const int s = g.seg(n);
-    bsrc[i] = reinterpret_cast<uint64_t>(g.w(s) + static_cast<int64_t>(n - g.start(s)) * K + 8 * lchunk);
-  }
-  const int st_off = lds_off(lrow, lchunk);   // + 32 i rows (same slot: 32 i is a multiple of 8)
-
-  // Staging registers of the next k-tile: native 4 x u32 vectors (HIP's
-  // union-based uint4 is kept in memory, which here meant LDS or scratch and
-  // serialised every load against its store), indexed with literal constants.
-  static_assert(kAChunks == 8 && kBChunks <= 8, "staging is written out for at most 8 chunks");
-  u32x4 ra[8], rb[8];
-#define GDN_REP8(M) M(0) M(1) M(2) M(3) M(4) M(5) M(6) M(7)
-#define GDN_LD(i)                                                                            \
-  ra[i] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(asrc[i]) + koff); \
-  if constexpr (i < kBChunks)                                                                \
-    rb[i] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(bsrc[i]) + koff);
-#define GDN_ST(i)                                                                            \
-  *reinterpret_cast<u32x4 *>(sa_ + st_off + 32 * (i) * kRowBytes) = ra[i];                   \
-  if constexpr (i < kBChunks) *reinterpret_cast<u32x4 *>(sb_ + st_off + 32 * (i) * kRowBytes) = rb[i];
-#define GDN_GEMM_LOAD(kt)                                                                    \
-  do {                                                                                       \
-    const int koff = (kt) * kBK;                                                             \
-    GDN_REP8(GDN_LD)                                                                         \
-  } while (0)
-#define GDN_GEMM_STORE(buf)                                                                  \
-  do {                                                                                       \
-    uint8_t *sa_ = smem + (buf) * (kABytes + kBBytes);                                       \
-    uint8_t *sb_ = sa_ + kABytes;                                                            \
-    GDN_REP8(GDN_ST)                                                                         \
-  } while (0)
-
-  f32x4 acc[8][WN];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < WN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // Fragment reads: row 16 f + (lane & 15) of the wave's rows, chunk 4 ks + (lane >> 4).
-  const int fr = lane & 15, fq = lane >> 4;
-  const int a_row0 = 128 * wr + fr, b_row0 = 16 * WN * wc + fr;
-
-  const int KT = K / kBK;
-  GDN_GEMM_LOAD(0);
-  GDN_GEMM_STORE(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) GDN_GEMM_LOAD(kt + 1);
-    // Keep the next k-tile's loads in flight across the MFMAs: without these
-    // fences the compiler sinks each load next to its LDS store and waits
-    // for it there, one at a time.
-    asm volatile("" ::: "memory");
-    const uint8_t *a = smem + cur * (kABytes + kBBytes);
-    const uint8_t *b = a + kABytes;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 fa[8], fb[WN];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        fa[i] = *reinterpret_cast<const bf16x8 *>(a + lds_off(a_row0 + 16 * i, 4 * ks + fq));
-#pragma unroll
-      for (int j = 0; j < WN; ++j)
-        fb[j] = *reinterpret_cast<const bf16x8 *>(b + lds_off(b_row0 + 16 * j, 4 * ks + fq));
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < WN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
-    }
-    asm volatile("" ::: "memory");
-    if (kt + 1 < KT) GDN_GEMM_STORE(cur ^ 1);
-    __syncthreads();
-  }
-
-#undef GDN_GEMM_LOAD
-#undef GDN_GEMM_STORE
-#undef GDN_LD
-#undef GDN_ST
-#undef GDN_REP8
-
-  gemm_epilogue<WN>(g, p.M, acc, m0 + 128 * wr + fr, n0 + 16 * WN * wc + 4 * fq);
-}
-
-// The same product with the operand tiles brought into LDS by the load
-// instructions themselves (16 bytes per lane, written at the wave's LDS
-// address + 16 * lane), in a ring of kStages k-tiles: the loads of k-tile
-// kt + 2 are issued as soon as every wave has finished k-tile kt - 1, so two
-// k-tiles of memory latency hide behind the MFMAs, and no registers stage the
-// data. Each lane loads the chunk that belongs in its slot of the swizzled
-// row: chunk (lane & 7) ^ (row & 7).
+// The operand tiles are brought into LDS by the load instructions
+// themselves (16 bytes per lane, written at the wave's LDS address +
+// 16 * lane), in a ring of kStages k-tiles: the loads of k-tile kt + 2 are
+// issued as soon as every wave has finished k-tile kt - 1, so two k-tiles of
+// memory latency hide behind the MFMAs, and no registers stage the data. Each
+// lane loads the chunk that belongs in its slot of the swizzled row: chunk
+// (lane & 7) ^ (row & 7).
 constexpr int kStages = 3;
-constexpr int kMaxDmaWn = 5;      // kStages k-tiles of 256 + 32 WN rows fit the 160 KB of LDS
-constexpr bool kUseDma = true;
+constexpr int kMaxWn = 5;         // kStages k-tiles of 256 + 32 WN rows fit the 160 KB of LDS
 
 template <int N>
 __device__ __forceinline__ void wait_vm_barrier() {
@@ -360,12 +243,11 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_dma_kernel(GemmParams p, in
 // owns 16 * NF output columns and all M rows (MF fragments of 16); its 8
 // waves split the contraction into contiguous ranges of 32-wide steps and
 // read both operands straight into MFMA fragments (16 bytes per lane: the
-// weights from HBM, the few activation rows from L2), kSkU steps of loads in
+// weights from HBM, the few activation rows from L2), U steps of loads in
 // flight before their MFMAs; the 8 partial sums meet in LDS.
 constexpr int kSkWaves = 8;
-constexpr int kSkU = 4;
 
-template <int MF, int NF>
+template <int MF, int NF, int U>
 __global__ __launch_bounds__(kSkWaves * kWave) void gemm_skinny_kernel(GemmParams p) {
   const Segs g(p);
   const int K = p.K, M = p.M;
@@ -402,14 +284,14 @@ __global__ __launch_bounds__(kSkWaves * kWave) void gemm_skinny_kernel(GemmParam
       fb[j] = *reinterpret_cast<const bf16x8 *>(reinterpret_cast<const uint16_t *>(brow[j]) + 32 * st);
   };
   int s0 = s_lo;
-  for (; s0 + kSkU <= s_hi; s0 += kSkU) {
-    bf16x8 fa[kSkU][MF], fb[kSkU][NF];
+  for (; s0 + U <= s_hi; s0 += U) {
+    bf16x8 fa[U][MF], fb[U][NF];
 #pragma unroll
-    for (int u = 0; u < kSkU; ++u) step(s0 + u, fa[u], fb[u]);
+    for (int u = 0; u < U; ++u) step(s0 + u, fa[u], fb[u]);
     // Every load of the group goes out before the first MFMA waits on one.
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < kSkU; ++u)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int i = 0; i < MF; ++i)
 #pragma unroll
@@ -426,8 +308,8 @@ __global__ __launch_bounds__(kSkWaves * kWave) void gemm_skinny_kernel(GemmParam
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
   }
 
-  // Partial sums of the 8 waves through LDS; wave w then finishes fragments
-  // f = w, w + 8, ... of the MF x NF and stores them.
+  // Partial sums of the waves through LDS; wave w then finishes fragments
+  // f = w, w + kSkWaves, ... of the MF x NF and stores them.
   __shared__ f32x4 part[kSkWaves][MF * NF][kWave];
 #pragma unroll
   for (int i = 0; i < MF; ++i)
@@ -455,8 +337,9 @@ __global__ __launch_bounds__(kSkWaves * kWave) void gemm_skinny_kernel(GemmParam
 
 template <int MF, int NF>
 hipError_t launch_skinny(const GemmParams &p, hipStream_t s) {
+  constexpr int U = 4;   // steps of loads in flight per wave
   const int blocks = (p.N + 16 * NF - 1) / (16 * NF);
-  hipLaunchKernelGGL((gemm_skinny_kernel<MF, NF>), dim3(blocks), dim3(kSkWaves * kWave), 0, s, p);
+  hipLaunchKernelGGL((gemm_skinny_kernel<MF, NF, U>), dim3(blocks), dim3(kSkWaves * kWave), 0, s, p);
   return hipGetLastError();
 }
 
@@ -473,12 +356,8 @@ hipError_t launch_wn(const GemmParams &p, hipStream_t s) {
   const int tiles_m = (p.M + kBM - 1) / kBM, tiles_n = (p.N + BN - 1) / BN;
   const int tiles = tiles_m * tiles_n;
   const int per_xcd = (tiles + kGemmXcds - 1) / kGemmXcds;
-  if constexpr (kUseDma && WN <= kMaxDmaWn)
-    hipLaunchKernelGGL(gemm_dma_kernel<WN>, dim3(per_xcd * kGemmXcds), dim3(kGemmThreads), 0, s, p, tiles_m,
-                       tiles_n, per_xcd);
-  else
-    hipLaunchKernelGGL(gemm_kernel<WN>, dim3(per_xcd * kGemmXcds), dim3(kGemmThreads), 0, s, p, tiles_m, tiles_n,
-                       per_xcd);
+  hipLaunchKernelGGL(gemm_dma_kernel<WN>, dim3(per_xcd * kGemmXcds), dim3(kGemmThreads), 0, s, p, tiles_m, tiles_n,
+                     per_xcd);
   return hipGetLastError();
 }
 
@@ -486,8 +365,7 @@ hipError_t launch_wn(const GemmParams &p, hipStream_t s) {
 
 // The column-tile width is chosen per call so that the number of rounds of
 // 256 concurrent tiles, times the tile width, is smallest (the last round of
-// a launch is often partly idle). Eight fragments per wave would spill.
-constexpr int kMaxWn = kUseDma ? kMaxDmaWn : 7;
+// a launch is often partly idle).
 static int gemm_tile_wn(int M, int N) {
   const int tiles_m = (M + kBM - 1) / kBM;
   int best = kMaxWn;
@@ -506,12 +384,8 @@ hipError_t launch_gemm(const GemmParams &p, hipStream_t s) {
   if (p.M <= 16) return launch_skinny_m<1>(p, s);
   if (p.M <= 32) return launch_skinny_m<2>(p, s);
   if (p.M <= 64) return launch_skinny_m<4>(p, s);
-  switch (gemm_tile_wn(p.M, p.N)) {
-    case 4: return launch_wn<4>(p, s);
-    case 5: return launch_wn<5>(p, s);
-    case 6: return launch_wn<6>(p, s);
-    default: return launch_wn<7>(p, s);
-  }
+  if (gemm_tile_wn(p.M, p.N) == 4) return launch_wn<4>(p, s);
+  return launch_wn<5>(p, s);
 }
 
 }  // namespace gdn

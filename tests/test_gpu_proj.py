@@ -108,8 +108,11 @@ def _rows(T, seed):
     return sorted(r for r in base if 0 <= r < T)
 
 
-@pytest.mark.parametrize("T,hidden,heads", [(1, 64, (1, 1)), (77, 128, (2, 6)), (300, 192, (2, 4)),
-                                            (513, 256, (4, 4)), (256, 320, (1, 2))])
+# Row counts up to 64 take the decode kernel (16, 32 or 64 rows per block;
+# 1 to 6 column fragments per block by width), more the tiled one.
+@pytest.mark.parametrize("T,hidden,heads", [(1, 64, (1, 1)), (20, 128, (2, 6)), (40, 192, (2, 4)),
+                                            (5, 64, (16, 64)), (64, 128, (16, 48)), (77, 128, (2, 6)),
+                                            (300, 192, (2, 4)), (513, 256, (4, 4)), (256, 320, (1, 2))])
 def test_in_proj_small(T, hidden, heads):
     hqk, hv = heads
     w = wl.custom("prefill", 1, hqk, hv, "bf16", seed=400 + T, lengths=[T])
@@ -119,7 +122,7 @@ def test_in_proj_small(T, hidden, heads):
     _check_in_proj(w, x, _in_proj_gpu(cfg, x, hidden))
 
 
-@pytest.mark.parametrize("T,hv", [(4096, 48), (64, 32), (1, 32)])
+@pytest.mark.parametrize("T,hv", [(4096, 48), (64, 48), (64, 32), (1, 32)])
 def test_in_proj_full_size_sampled(T, hv):
     hidden = wl.HIDDEN[hv]
     w = wl.custom("prefill", 1, 16, hv, "bf16", seed=410 + hv, lengths=[T])
