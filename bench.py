@@ -80,14 +80,19 @@ TRAFFIC_SOURCES = {
 
 
 def kernel_source_hash(key: str) -> str:
-    """sha256 over the HIP source of the kernel(s) behind a traffic record and
-    the shared device headers (the counters are only valid for that code)."""
+    """sha256 over the code (comments and whitespace removed) of the HIP
+    source behind a traffic record and the shared device headers: the counters
+    are only valid for that code."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in sorted(TRAFFIC_SOURCES[key]) + ["gdn_device.h", "gdn_internal.h"]:
+        with open(os.path.join(CSRC, f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
         h.update(f.encode())
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 

@@ -16,7 +16,7 @@
 //
 // Two kernels:
 //  * chunk_local: one block per (chunk, K-head), fully parallel. Writes the
-//    chunk's K, Q and K^T as ready-to-load MFMA operands, builds K K^T and
+//    chunk's K and Q as ready-to-load MFMA operands, builds K K^T and
 //    Q K^T once for the K-head, then for each V-head that uses it (tiled
 //    repeat: V-heads h, h + Hqk, ...) applies that head's decays and beta,
 //    writes P, and inverts the unit lower-triangular I + A by blocked forward
@@ -27,9 +27,10 @@
 //    walks the sequence's chunks in order with the fp32 state slab held in
 //    MFMA accumulators: [K; Q] S, D = Tm (V - Gam K S), O = s(Gam Q S + P D),
 //    S <- Gam_n S + K^T diag(exp(gam_n - gam)) D. The left operands of these
-//    products (K, Q, Tm, P, K^T) stream from the workspace straight into
+//    products (K, Q, Tm, P) stream from the workspace straight into
 //    registers, each reloaded for the next chunk right after its last use;
-//    only the right operands (S^T, R^T, D^T) and V pass through LDS.
+//    the right operands (S^T, R^T, D^T), V, and the chunk's K rows (from
+//    which every wave gathers its K^T fragments) pass through LDS.
 // Every product runs at fp32-grade precision: fp32 MFMA for fp32
 // activations, three-pass split bf16 MFMA (hi*hi + hi*lo + lo*hi) for bf16
 // activations. Operands are split once, when they are written to LDS (or to
@@ -57,8 +58,7 @@ constexpr int kLdS = kChunk + 1;          // fp32 pitch of the solve's scalar ma
 constexpr int kLdV = kSlab + 4;           // fp32 pitch of the V slab in LDS
 
 // Workspace, all operands in the fragment-major layout:
-//   per (chunk, K-head): K rows (64 x 128, 4 x 4 blocks), Q rows (same) and
-//                        K^T rows (128 x 64, 8 x 2 blocks): 96 KB
+//   per (chunk, K-head): K rows (64 x 128, 4 x 4 blocks) and Q rows (same): 64 KB
 //   per (chunk, V-head): Tm (64 x 64, 4 x 2 blocks) and P (same): 32 KB
 //   per (chunk, V-head): gam, 64 fp64
 constexpr size_t kKBytes = 16 * kFragBlk;
@@ -106,9 +106,9 @@ template <> __device__ __forceinline__ Op<Prec::BF16X3>::Frag make_frag<Prec::BF
 // chunk_local: per (chunk, K-head), 4 waves, ~72 KB of LDS (two blocks per CU).
 //  1. K rows of the chunk into LDS; Q rows into registers as the A fragments
 //     of wave w's row tile, stored to the workspace as they are.
-//  2. K and K^T operand blocks to the workspace, a whole fragment per lane
-//     read out of LDS; wave w computes row tile w of the lower triangles of
-//     K K^T and Q K^T.
+//  2. K operand blocks to the workspace, a whole fragment per lane read out
+//     of LDS; wave w computes row tile w of the lower triangles of K K^T and
+//     Q K^T.
 //  3. For the V-heads that use this K-head (kSolveWaves at a time): decays
 //     and beta; L = I + A into LDS and P to the workspace, one fragment
 //     block per step spread over all waves; L^-1 by blocked forward
