@@ -1,12 +1,14 @@
 """Benchmark of the gated DeltaNet token mixer on one MI355X.
 
 One step = one pass of the whole mixer over the prefill workload
-(T = 4096 tokens, 16 K-heads, 48 V-heads, bf16 activations, one sequence):
-gdn_conv_gate_prep -> gdn_prefill_chunked -> gdn_gated_rmsnorm, inputs
-already resident in HBM. The steps run twice: as plain launches, and as
-the step captured in a HIP graph and replayed; ``value`` is tokens per
-second over exactly ``--steps`` timed steps (after ``--warmup`` untimed
-ones) of the faster of the two, both reported under "prefill_modes".
+(T = 4096 tokens, 16 K-heads, 48 V-heads, bf16 activations, one sequence),
+inputs already resident in HBM, in two forms: the three calls
+gdn_conv_gate_prep -> gdn_prefill_chunked -> gdn_gated_rmsnorm, and the one
+call gdn_prefill_fused (q, k, v, beta, g computed inside the chunked
+kernels). Each runs as plain launches and as the step captured in a HIP
+graph and replayed; ``value`` is tokens per second over exactly ``--steps``
+timed steps (after ``--warmup`` untimed ones) of the fastest of the four,
+all reported under "prefill_modes".
 
 The same run also times the decode path on the batch-1 workload (32 V-heads,
 1024 consecutive steps) and the batch-64 workload (256 steps), and reports
@@ -259,19 +261,53 @@ def bench_prefill(steps: int, warmup: int):
     torch.cuda.synchronize()
     graph_ms = start.elapsed_time(end)
     del g
-    total_ms = min(plain_ms, graph_ms)
+    # The same step as one gdn_prefill_fused call (q, k, v, beta, g computed
+    # inside the chunked kernels), plain and as a graph.
+    fused = Lyr.PrefillFused(cfg, 1, T)
+    conv_f = torch.empty_like(t["conv0"])
+    S_f = torch.empty_like(t["S0"])
+
+    def fstep():
+        fused(t["cu_seqlens"], t["qkv"], t["z"], t["b"], t["a"], t["conv_w"], t["dt_bias"], t["A_log"],
+              t["norm_w"], t["conv0"], conv_f, t["S0"], S_f)
+
+    for _ in range(warmup):
+        fstep()
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        fstep()
+    end.record()
+    torch.cuda.synchronize()
+    fused_ms = start.elapsed_time(end)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fstep()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    fused_graph_ms = start.elapsed_time(end)
+    del g
+    modes_ms = {"plain": plain_ms, "graph": graph_ms, "fused": fused_ms, "fused_graph": fused_graph_ms}
+    best = min(modes_ms, key=modes_ms.get)
+    total_ms = modes_ms[best]
     n_chunk_heads = ((T + CHUNK - 1) // CHUNK) * w.n_v_heads
     flops = FLOP_PER_CHUNK_HEAD * n_chunk_heads
     achieved = flops / (core_ms * 1e-3) / 1e12
-    return dict(total_ms=total_ms, ms_per_step=total_ms / steps, tokens=T, core_ms=core_ms,
-                modes={"plain": {"ms_per_step": round(plain_ms / steps, 4),
-                                 "tokens_per_s": round(T * steps / (plain_ms * 1e-3), 1)},
-                       "graph": {"ms_per_step": round(graph_ms / steps, 4),
-                                 "tokens_per_s": round(T * steps / (graph_ms * 1e-3), 1)}},
+    return dict(total_ms=total_ms, ms_per_step=total_ms / steps, tokens=T, core_ms=core_ms, best=best,
+                modes={k: {"ms_per_step": round(v / steps, 4), "tokens_per_s": round(T * steps / (v * 1e-3), 1)}
+                       for k, v in modes_ms.items()},
                 roofline={"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
                           "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                           "traffic": measured_traffic("prefill_core"),
-                          "kernel": "gdn_prefill_chunked (chunk_local + chunk_state)",
+                          "kernel": "gdn_prefill_chunked (chunk_local + chunk_state), timed in the three-call "
+                                    "step; the fused step runs the same kernels with the conv folded into "
+                                    "their loads",
                           "flop_per_launch": flops, "avg_launch_us": round(core_ms * 1e3, 2)})
 
 
@@ -668,7 +704,7 @@ def main():
         return
     log("prefill workload: T=4096 Hqk=16 Hv=48 bf16")
     pre = bench_prefill(a.steps, a.warmup)
-    log(f"prefill: {pre['ms_per_step']:.3f} ms/step, core {pre['core_ms'] * 1e3:.1f} us")
+    log(f"prefill: {pre['ms_per_step']:.3f} ms/step ({pre['best']}), core {pre['core_ms'] * 1e3:.1f} us; " + json.dumps(pre['modes']))
     decode = None
     if not a.no_decode and a.only is None:
         decode = []
@@ -696,6 +732,7 @@ def main():
         "config": {"workload": "prefill T=4096, 1 sequence, Hqk=16, Hv=48, d=128, chunk 64, bf16, zero states",
                    "global_batch": 1, "seq_len": pre["tokens"], "parallelism": "single GPU"},
         "prefill_modes": pre["modes"],
+        "prefill_best_mode": pre["best"],
         "roofline": pre["roofline"],
         "decode": decode,
         "block": block,

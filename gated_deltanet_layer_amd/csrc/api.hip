@@ -57,6 +57,8 @@ bool any_overlap(const Range (&outs)[NO], const Range (&ins)[NI]) {
 
 gdn_status launched(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_E_HIP; }
 
+bool aligned(const void *p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
 }  // namespace
 
 extern "C" {
@@ -187,7 +189,7 @@ gdn_status gdn_prefill_chunked_ckpt(const gdn_config *cfg, int32_t n_seqs, int32
       return GDN_E_INVALID_ARG;
   }
 
-  gdn::PrefillParams p;
+  gdn::PrefillParams p = {};
   p.cu = cu_seqlens;
   p.n_seqs = n_seqs;
   p.n_tokens = n_tokens;
@@ -215,6 +217,113 @@ gdn_status gdn_prefill_chunked(const gdn_config *cfg, int32_t n_seqs, int32_t n_
                                void *workspace, size_t workspace_bytes, gdn_stream_t stream) {
   return gdn_prefill_chunked_ckpt(cfg, n_seqs, n_tokens, cu_seqlens, q, k, v, beta, g, S_in, S_out, o, 0, 0,
                                   nullptr, workspace, workspace_bytes, stream);
+}
+
+// Workspace of the fused prefill: the chunked form's, then o (act dtype),
+// 256-byte aligned.
+static size_t fused_o_offset(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens) {
+  const size_t base = gdn::prefill_workspace_bytes(n_seqs, n_tokens, cfg->n_qk_heads, cfg->n_v_heads);
+  return (base + 255) / 256 * 256;
+}
+
+size_t gdn_prefill_fused_workspace_bytes(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens) {
+  if (check_config(cfg) != GDN_OK || n_seqs < 0 || n_tokens < 0) return 0;
+  if (n_tokens == 0) return 0;
+  return fused_o_offset(cfg, n_seqs, n_tokens) +
+         static_cast<size_t>(n_tokens) * cfg->n_v_heads * kHeadDim * act_size(cfg);
+}
+
+gdn_status gdn_prefill_fused(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens, const int32_t *cu_seqlens,
+                             const void *qkv, const void *beta_logit, const void *alpha_logit, const void *z,
+                             const float *conv_w, const float *dt_bias, const float *A_log, const float *norm_w,
+                             const void *conv_state_in, void *conv_state_out, const float *S_in, float *S_out,
+                             void *y, void *workspace, size_t workspace_bytes, gdn_stream_t stream) {
+  const gdn_status cs = check_config(cfg);
+  if (cs != GDN_OK) return cs;
+  if (n_seqs < 0 || n_tokens < 0) return GDN_E_INVALID_ARG;
+  if (n_seqs == 0) return n_tokens == 0 ? GDN_OK : GDN_E_INVALID_ARG;
+  if (!cu_seqlens || !conv_w || !dt_bias || !A_log || !norm_w || !conv_state_in || !conv_state_out || !S_in ||
+      !S_out)
+    return GDN_E_INVALID_ARG;
+  if (n_tokens > 0 && (!qkv || !beta_logit || !alpha_logit || !z || !y)) return GDN_E_INVALID_ARG;
+  // The chunk kernels read qkv and the conv state 8 or 16 bytes at a time.
+  if (!aligned(qkv, 16) || !aligned(conv_state_in, 16) || !aligned(conv_state_out, 16) || !aligned(conv_w, 16))
+    return GDN_E_INVALID_ARG;
+  const int Hqk = cfg->n_qk_heads, Hv = cfg->n_v_heads;
+  const size_t need = gdn_prefill_fused_workspace_bytes(cfg, n_seqs, n_tokens);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return GDN_E_WORKSPACE;
+  const int64_t chunks = gdn::max_chunks(n_seqs, n_tokens);
+  const size_t T = static_cast<size_t>(n_tokens), as = act_size(cfg);
+  const size_t C = static_cast<size_t>(kHeadDim) * (2 * Hqk + Hv);
+  if (chunks > kMaxGrid || Hqk > 65535 || static_cast<int64_t>(n_seqs) * Hv * (kHeadDim / 32) > kMaxGrid ||
+      static_cast<int64_t>(n_seqs) * static_cast<int64_t>((C / 2 + 255) / 256) > kMaxGrid)
+    return GDN_E_UNSUPPORTED;
+  const size_t st = static_cast<size_t>(n_seqs) * (gdn::kConvK - 1) * C * as;
+  const size_t sb = static_cast<size_t>(n_seqs) * Hv * kHeadDim * kHeadDim * 4;
+  const size_t yb = T * Hv * kHeadDim * as;
+  const Range outs[] = {{y, yb}, {workspace, need}};
+  const Range ins[] = {{qkv, T * C * as}, {beta_logit, T * Hv * as}, {alpha_logit, T * Hv * as}, {z, yb},
+                       {conv_w, C * 4 * 4}, {dt_bias, Hv * 4u}, {A_log, Hv * 4u}, {norm_w, kHeadDim * 4u},
+                       {cu_seqlens, (n_seqs + 1u) * 4u}, {conv_state_in, st}, {conv_state_out, st},
+                       {S_in, sb}, {S_out, sb}};
+  if (any_overlap(outs, ins)) return GDN_E_INVALID_ARG;
+  // Each state may be updated in place, but must not partly overlap or
+  // overlap anything else.
+  if (conv_state_in != conv_state_out && overlap(conv_state_in, st, conv_state_out, st)) return GDN_E_INVALID_ARG;
+  if (S_in != S_out && overlap(S_in, sb, S_out, sb)) return GDN_E_INVALID_ARG;
+  for (size_t i = 0; i < 9; ++i)
+    if (overlap(ins[i].p, ins[i].n, conv_state_out, st) || overlap(ins[i].p, ins[i].n, S_out, sb))
+      return GDN_E_INVALID_ARG;
+  if (overlap(conv_state_out, st, S_out, sb) || overlap(conv_state_in, st, S_out, sb) ||
+      overlap(conv_state_out, st, S_in, sb))
+    return GDN_E_INVALID_ARG;
+
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  void *o = n_tokens > 0 ? static_cast<uint8_t *>(workspace) + fused_o_offset(cfg, n_seqs, n_tokens) : nullptr;
+  gdn::PrefillParams p = {};
+  p.cu = cu_seqlens;
+  p.n_seqs = n_seqs;
+  p.n_tokens = n_tokens;
+  p.n_qk = Hqk;
+  p.n_v = Hv;
+  p.S_in = S_in;
+  p.S_out = S_out;
+  p.o = o;
+  p.ws = workspace;
+  p.ws_bytes = workspace_bytes;
+  p.qkv = n_tokens > 0 ? qkv : conv_state_in;   // non-null selects the fused kernels
+  p.bl = beta_logit;
+  p.al = alpha_logit;
+  p.st_in = conv_state_in;
+  p.conv_w = conv_w;
+  p.dt_bias = dt_bias;
+  p.A_log = A_log;
+  p.l2_eps = cfg->l2_eps;
+  p.l2_mode = cfg->l2_mode;
+  hipError_t e = gdn::launch_prefill(p, cfg->act_dtype, hs);
+  if (e == hipSuccess && n_tokens > 0) {
+    gdn::NormParams np;
+    np.n_rows = static_cast<int64_t>(n_tokens) * Hv;
+    np.o = o;
+    np.z = z;
+    np.w = norm_w;
+    np.y = y;
+    np.eps = cfg->norm_eps;
+    e = gdn::launch_norm(np, cfg->act_dtype, hs);
+  }
+  if (e == hipSuccess) {
+    // Last: the kernels above read the old conv state (in-place safe).
+    gdn::ConvStateParams cp;
+    cp.cu = cu_seqlens;
+    cp.n_seqs = n_seqs;
+    cp.n_tokens = n_tokens;
+    cp.C = static_cast<int>(C);
+    cp.qkv = qkv;
+    cp.st_in = conv_state_in;
+    cp.st_out = conv_state_out;
+    e = gdn::launch_conv_state(cp, cfg->act_dtype, hs);
+  }
+  return launched(e);
 }
 
 gdn_status gdn_conv_state_ckpt(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens, const int32_t *cu_seqlens,
@@ -293,8 +402,6 @@ gdn_status gdn_decode_step(const gdn_config *cfg, int32_t n_seqs, const float *q
 }  // extern "C"
 
 namespace {
-
-bool aligned(const void *p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
 
 // Shared checks of the two projections: bf16 only, K (the contraction length)
 // a positive multiple of 64, operands 16-byte aligned.

@@ -78,6 +78,17 @@ struct ConvCkptParams {
 };
 hipError_t launch_conv_ckpt(const ConvCkptParams &p, gdn_dtype act, hipStream_t s);
 
+// New conv states after packed sequences: conv_out[n] = the last 3 rows of
+// [st_in[n]; qkv rows of sequence n] (one thread owns a channel's 3 rows, so
+// st_out may equal st_in).
+struct ConvStateParams {
+  const int32_t *cu;
+  int n_seqs, n_tokens, C;
+  const void *qkv, *st_in;
+  void *st_out;
+};
+hipError_t launch_conv_state(const ConvStateParams &p, gdn_dtype act, hipStream_t s);
+
 // Non-finite guard over n_values fp32 state values: stats[0] = number of
 // non-finite values, stats[1] = bit pattern of max |x| over the finite ones.
 hipError_t launch_state_check(const float *S, int64_t n_values, int32_t *stats, hipStream_t s);
@@ -113,6 +124,14 @@ struct PrefillParams {
   // every such token inside it; ckpt_chunks = 0 writes none.
   float *S_ckpt;
   int ckpt_chunks, ckpt_cap;
+  // Fused form (gdn_prefill_fused), when qkv is not null: the chunk kernels
+  // compute q, k (conv, SiLU, L2 norm), v (conv, SiLU), beta and g themselves
+  // from the raw qkv rows (left context: st_in) and the logits, instead of
+  // reading q, k, v, beta, g.
+  const void *qkv, *bl, *al, *st_in;
+  const float *conv_w, *dt_bias, *A_log;
+  float l2_eps;
+  int l2_mode;
 };
 // Upper bound on the number of chunks over all sequences.
 inline int64_t max_chunks(int n_seqs, int n_tokens) {

@@ -40,6 +40,8 @@
 //
 // Decays: exp is only taken of gam_r - gam_m with m <= r (never positive),
 // so nothing overflows; exp(gam) may underflow to 0, which is harmless.
+#include <type_traits>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -115,6 +117,65 @@ template <> __device__ __forceinline__ Op<Prec::BF16X3>::Frag make_frag<Prec::BF
 //     substitution in place, one wave per V-head; Tm = L^-1 diag(beta) to
 //     the workspace over all waves. Blocks of P and Tm above the diagonal
 //     32 x 32 blocks are all zero and are never written or read.
+// Fused form: conv + SiLU of channels c0 .. c0 + 7 (c0 a multiple of 8) for
+// local token tl (0 <= tl < L) of sequence n, from rows tl - 3 .. tl of
+// [st_in[n]; qkv rows of the sequence] (the same arithmetic as the prep
+// kernel: tap 3 meets the current row).
+template <typename TA>
+__device__ __forceinline__ void conv_silu8(const PrefillParams &p, int n, int seq0, int C, int tl, int c0,
+                                           f32x4 &ya, f32x4 &yb) {
+  const TA *qkv = static_cast<const TA *>(p.qkv);
+  const TA *st = static_cast<const TA *>(p.st_in);
+  float4 xa[kConvK], xb[kConvK];
+#pragma unroll
+  for (int r = 0; r < kConvK; ++r) {
+    const int pos = tl - (kConvK - 1) + r;
+    const TA *src = pos < 0 ? st + (static_cast<size_t>(n) * (kConvK - 1) + (pos + kConvK - 1)) * C
+                            : qkv + static_cast<size_t>(seq0 + pos) * C;
+    xa[r] = Act<TA>::load4(src, c0);
+    xb[r] = Act<TA>::load4(src, c0 + 4);
+  }
+  const float4 *w = reinterpret_cast<const float4 *>(p.conv_w) + c0;
+  float y[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float4 we = w[e];
+    const float x0 = e < 4 ? (&xa[0].x)[e] : (&xb[0].x)[e - 4];
+    const float x1 = e < 4 ? (&xa[1].x)[e] : (&xb[1].x)[e - 4];
+    const float x2 = e < 4 ? (&xa[2].x)[e] : (&xb[2].x)[e - 4];
+    const float x3 = e < 4 ? (&xa[3].x)[e] : (&xb[3].x)[e - 4];
+    y[e] = siluf_(we.x * x0 + we.y * x1 + we.z * x2 + we.w * x3);
+  }
+  ya = f32x4{y[0], y[1], y[2], y[3]};
+  yb = f32x4{y[4], y[5], y[6], y[7]};
+}
+
+// Fused form: row tl of q (part 0) or k (part 1) of K-head h, the lane's 32
+// channels 32 ks + 8 (lane / 16) .. +7, conv + SiLU + L2 norm over the
+// row's 128 channels (spread over lanes l, l ^ 16, l ^ 32, l ^ 48).
+template <typename TA>
+__device__ __forceinline__ void qk_row(const PrefillParams &p, int n, int seq0, int L, int tl, bool valid, int part,
+                                       int h, f32x4 (&ya)[kHeadDim / 32], f32x4 (&yb)[kHeadDim / 32]) {
+  const int C = kHeadDim * (2 * p.n_qk + p.n_v);
+  const int cbase = (part * p.n_qk + h) * kHeadDim + 8 * (lane_id() >> 4);
+  const int t = min(tl, L - 1);
+  float ss = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < kHeadDim / 32; ++ks) {
+    conv_silu8<TA>(p, n, seq0, C, t, cbase + 32 * ks, ya[ks], yb[ks]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ss += ya[ks][e] * ya[ks][e] + yb[ks][e] * yb[ks][e];
+  }
+  ss += __shfl_xor(ss, 16);
+  ss += __shfl_xor(ss, 32);
+  const float inv = valid ? l2_inv(ss, p.l2_eps, p.l2_mode == GDN_L2_RSQRT) : 0.f;
+#pragma unroll
+  for (int ks = 0; ks < kHeadDim / 32; ++ks) {
+    ya[ks] *= inv;
+    yb[ks] *= inv;
+  }
+}
+
 constexpr int kSolveWaves = 3;
 constexpr int kTri = kChunk * (kChunk + 1) / 2;   // packed lower triangle incl. diagonal
 
@@ -123,7 +184,7 @@ __device__ __forceinline__ int tri(int r, int m) { return r * (r + 1) / 2 + m; }
 // Orders this wave's earlier LDS accesses before its later ones.
 __device__ __forceinline__ void wave_sync_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-template <Prec P>
+template <Prec P, typename TA, bool kFused>
 __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(PrefillParams p, int64_t max_chunks) {
   using Frag = typename Op<P>::Frag;
   // K as blocked operand rows first; then the solving waves' fp32 matrices
@@ -152,8 +213,8 @@ __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(PrefillParam
   const int cid = blockIdx.x;
   const Workspace ws = carve(p.ws, max_chunks, p.n_qk, p.n_v);
   const size_t qk_stride = static_cast<size_t>(p.n_qk) * kHeadDim;
-  const float *kg = p.k + t0 * qk_stride + h * kHeadDim;
-  const float *qg = p.q + t0 * qk_stride + h * kHeadDim;
+  const float *kg = kFused ? nullptr : p.k + t0 * qk_stride + h * kHeadDim;
+  const float *qg = kFused ? nullptr : p.q + t0 * qk_stride + h * kHeadDim;
   uint8_t *wk = ws.qk + (static_cast<size_t>(cid) * p.n_qk + h) * kQkBytes;   // K rows, Q rows
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
@@ -162,7 +223,25 @@ __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(PrefillParam
   const int rt = wave;
   const int qrow = 16 * rt + (lane & 15);
   Frag fq[kHeadDim / 32];
-  {
+  if constexpr (kFused) {
+    // q and k of row qrow from the raw rows; k goes to LDS (blocked operand
+    // rows, as below), q stays in this lane's A-fragment slots.
+    const bool valid = qrow < len;
+    f32x4 ya[kHeadDim / 32], yb[kHeadDim / 32];
+    qk_row<TA>(p, n, seq0, L, ci * kChunk + qrow, valid, 0, h, ya, yb);
+#pragma unroll
+    for (int ks = 0; ks < kHeadDim / 32; ++ks) {
+      fq[ks] = make_frag<P>(ya[ks], yb[ks]);
+      FragIO<P>::store(wk + kKBytes, kHeadDim / 32, rt, ks, fq[ks]);
+    }
+    qk_row<TA>(p, n, seq0, L, ci * kChunk + qrow, valid, 1, h, ya, yb);
+#pragma unroll
+    for (int ks = 0; ks < kHeadDim / 32; ++ks) {
+      const int c = 32 * ks + 8 * (lane >> 4);
+      Op<P>::put4(Kb + qrow * kPitch128, c, ya[ks]);
+      Op<P>::put4(Kb + qrow * kPitch128, c + 4, yb[ks]);
+    }
+  } else {
     const float *qp = qg + min(qrow, len - 1) * qk_stride + 8 * (lane >> 4);
     f32x4 qa[kHeadDim / 32], qb[kHeadDim / 32];
 #pragma unroll
@@ -177,7 +256,7 @@ __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(PrefillParam
       FragIO<P>::store(wk + kKBytes, kHeadDim / 32, rt, ks, fq[ks]);
     }
   }
-  {  // K rows -> blocked operand rows in LDS; rows >= len are zero.
+  if constexpr (!kFused) {  // K rows -> blocked operand rows in LDS; rows >= len are zero.
     constexpr int kPer = kChunk * (kHeadDim / 4) / kLocalThreads;
     f32x4 kb4[kPer];
 #pragma unroll
@@ -235,8 +314,17 @@ __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(PrefillParam
     if (wave < nu) {
       const int j = h + (u0 + wave) * p.n_qk;
       const size_t e = static_cast<size_t>(t0 + min(lane, len - 1)) * p.n_v + j;
-      const double gr = lane < len ? static_cast<double>(p.g[e]) : 0.0;
-      const float br = lane < len ? p.beta[e] : 0.f;
+      float gv, bv;
+      if constexpr (kFused) {   // the gates, as the prep kernel forms them
+        const TA *bl = static_cast<const TA *>(p.bl), *al = static_cast<const TA *>(p.al);
+        bv = sigmoidf_(Act<TA>::load(bl, e));
+        gv = -expf(p.A_log[j]) * softplusf_(Act<TA>::load(al, e) + p.dt_bias[j]);
+      } else {
+        bv = p.beta[e];
+        gv = p.g[e];
+      }
+      const double gr = lane < len ? static_cast<double>(gv) : 0.0;
+      const float br = lane < len ? bv : 0.f;
       const double gm = wave_inclusive_scan_d(gr);
       gam_s[wave][lane] = gm;
       bet_s[wave][lane] = br;
@@ -453,6 +541,34 @@ template <> struct KtLds<Prec::F32> {
   }
 };
 
+// Fused form: 4 consecutive raw activations as loaded (undecoded, so the load
+// can stay in flight), and their conv + SiLU over rows t - 3 .. t.
+template <typename TA> struct RawAct;
+template <> struct RawAct<float> {
+  using type = float4;
+  static __device__ __forceinline__ float4 f4(float4 x) { return x; }
+};
+template <> struct RawAct<bf16_t> {
+  using type = uint2;
+  static __device__ __forceinline__ float4 f4(uint2 w) {
+    return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                       __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
+  }
+};
+
+template <typename Raw>
+__device__ __forceinline__ f32x4 conv_silu4(const Raw (&raw)[kConvK], const float4 (&w)[4]) {
+  using TA = std::conditional_t<std::is_same<Raw, float4>::value, float, bf16_t>;
+  float4 x[kConvK];
+#pragma unroll
+  for (int r = 0; r < kConvK; ++r) x[r] = RawAct<TA>::f4(raw[r]);
+  f32x4 y;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    y[e] = siluf_(w[e].x * (&x[0].x)[e] + w[e].y * (&x[1].x)[e] + w[e].z * (&x[2].x)[e] + w[e].w * (&x[3].x)[e]);
+  return y;
+}
+
 // ---------------------------------------------------------------------------
 // chunk_state: per (sequence, V-head, 32-column slab). 8 waves; wave w has
 // rt = w % 4. Per chunk:
@@ -468,7 +584,7 @@ template <> struct KtLds<Prec::F32> {
 // the state update are not loaded: the x-waves leave their K fragments in
 // LDS and every wave gathers its K^T fragments from there (the kernel is
 // bound by how many bytes a CU pulls from L2 per chunk).
-template <Prec P, typename TA>
+template <Prec P, typename TA, bool kFused>
 __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParams p, int64_t max_chunks) {
   using Frag = typename Op<P>::Frag;
   __shared__ __attribute__((aligned(16))) uint8_t Stb[8 * kLdsBlk];    // S: B of K S, Q S (2 col x 4 k tiles)
@@ -537,6 +653,19 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
 
   Frag fxy[kHeadDim / 32], fd[kChunk / 32];
   f32x4 pvv;
+  // Fused form: the raw rows t - 3 .. t of this thread's 4 V channels are
+  // loaded with the other operands of the next chunk and turned into
+  // conv + SiLU when committed to LDS; the taps of the 4 channels are loaded
+  // once.
+  using Raw = typename RawAct<TA>::type;
+  Raw vraw[kConvK];
+  float4 vw[4];
+  const int Cq = kHeadDim * (2 * p.n_qk + p.n_v);
+  const int vch = 2 * p.n_qk * kHeadDim + j * kHeadDim + col_base + 4 * v_c4;   // first channel in qkv
+  if constexpr (kFused) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vw[e] = reinterpret_cast<const float4 *>(p.conv_w)[vch + e];
+  }
   double pg = 0.0, pg_end = 0.0;
 
 #define GDN_LOAD_XY(c)                                                                               \
@@ -551,8 +680,19 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
 #define GDN_LOAD_VG(c)                                                                               \
   do {                                                                                               \
     const int t0_ = seq0 + (c) * kChunk, len_ = min(kChunk, L - (c) * kChunk);                       \
-    pvv = *reinterpret_cast<const f32x4 *>(p.v + (t0_ + min(v_row, len_ - 1)) * v_stride +          \
-                                           j * kHeadDim + col_base + 4 * v_c4);                      \
+    if constexpr (kFused) {                                                                          \
+      const int tl_ = (c) * kChunk + min(v_row, len_ - 1);                                           \
+      _Pragma("unroll") for (int r_ = 0; r_ < kConvK; ++r_) {                                        \
+        const int pos_ = tl_ - (kConvK - 1) + r_;                                                    \
+        const TA *src_ = pos_ < 0 ? static_cast<const TA *>(p.st_in) +                               \
+                                        (static_cast<size_t>(n) * (kConvK - 1) + (pos_ + kConvK - 1)) * Cq \
+                                  : static_cast<const TA *>(p.qkv) + static_cast<size_t>(seq0 + pos_) * Cq; \
+        vraw[r_] = *reinterpret_cast<const Raw *>(src_ + vch);                                       \
+      }                                                                                              \
+    } else {                                                                                         \
+      pvv = *reinterpret_cast<const f32x4 *>(p.v + (t0_ + min(v_row, len_ - 1)) * v_stride +        \
+                                             j * kHeadDim + col_base + 4 * v_c4);                    \
+    }                                                                                                \
     if (tid < kChunk) {                                                                              \
       const double *gm = ws.gam + (static_cast<size_t>(cid0 + (c)) * p.n_v + j) * kChunk;            \
       pg = gm[tid];                                                                                  \
@@ -565,6 +705,7 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
   do {                                                                                               \
     const int len_ = min(kChunk, L - (c) * kChunk);                                                  \
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};                                                        \
+    if constexpr (kFused) pvv = conv_silu4(vraw, vw);                                                \
     *reinterpret_cast<f32x4 *>(Vs + v_row * kLdV + 4 * v_c4) = v_row < len_ ? pvv : zero4;          \
     if (tid < kChunk) {                                                                              \
       G_s[tid] = expf(static_cast<float>(pg));                                                       \
@@ -706,15 +847,21 @@ hipError_t launch_prefill(const PrefillParams &p, gdn_dtype act, hipStream_t s) 
   const dim3 grid_local(static_cast<unsigned>(chunks), static_cast<unsigned>(p.n_qk));
   const int64_t pairs = static_cast<int64_t>(p.n_seqs) * p.n_v;
   const dim3 grid_state(static_cast<unsigned>((pairs + kXcds - 1) / kXcds * kXcds * (kHeadDim / kSlab)));
+  const bool fused = p.qkv != nullptr;
+#define GDN_LAUNCH(PR, TA, FU)                                                                                \
+  do {                                                                                                        \
+    if (p.n_tokens > 0)                                                                                       \
+      hipLaunchKernelGGL((chunk_local_kernel<PR, TA, FU>), grid_local, dim3(kLocalThreads), 0, s, p, chunks); \
+    hipLaunchKernelGGL((chunk_state_kernel<PR, TA, FU>), grid_state, dim3(kStateThreads), 0, s, p, chunks);   \
+  } while (0)
   if (act == GDN_BF16) {
-    if (p.n_tokens > 0)
-      hipLaunchKernelGGL(chunk_local_kernel<Prec::BF16X3>, grid_local, dim3(kLocalThreads), 0, s, p, chunks);
-    hipLaunchKernelGGL((chunk_state_kernel<Prec::BF16X3, bf16_t>), grid_state, dim3(kStateThreads), 0, s, p, chunks);
+    if (fused) GDN_LAUNCH(Prec::BF16X3, bf16_t, true);
+    else GDN_LAUNCH(Prec::BF16X3, bf16_t, false);
   } else {
-    if (p.n_tokens > 0)
-      hipLaunchKernelGGL(chunk_local_kernel<Prec::F32>, grid_local, dim3(kLocalThreads), 0, s, p, chunks);
-    hipLaunchKernelGGL((chunk_state_kernel<Prec::F32, float>), grid_state, dim3(kStateThreads), 0, s, p, chunks);
+    if (fused) GDN_LAUNCH(Prec::F32, float, true);
+    else GDN_LAUNCH(Prec::F32, float, false);
   }
+#undef GDN_LAUNCH
   return hipGetLastError();
 }
 

@@ -54,6 +54,24 @@ class Prefill:
         return self.y
 
 
+class PrefillFused:
+    """The whole mixer over packed sequences in one gdn_prefill_fused call
+    (q, k, v, beta and g are never stored); the workspace also holds o."""
+
+    def __init__(self, cfg: B.gdn_config, n_seqs: int, n_tokens: int, device="cuda"):
+        self.cfg, self.N, self.T = cfg, n_seqs, n_tokens
+        Hv, d = cfg.n_v_heads, cfg.head_dim
+        self.y = torch.empty(n_tokens, Hv, d, dtype=_act(cfg), device=device)
+        wsb = B.gdn_prefill_fused_workspace_bytes(cfg, n_seqs, n_tokens)
+        self.ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=device) if wsb else None
+
+    def __call__(self, cu, qkv, z, b, a, conv_w, dt_bias, A_log, norm_w, conv_in, conv_out, S_in, S_out,
+                 stream=None):
+        B.gdn_prefill_fused(self.cfg, self.N, self.T, cu, qkv, b, a, z, conv_w, dt_bias, A_log, norm_w, conv_in,
+                            conv_out, S_in, S_out, self.y, self.ws, stream)
+        return self.y
+
+
 class Decode:
     """One token for each of n_seqs sequences per call; states updated in place."""
 

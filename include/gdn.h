@@ -180,6 +180,32 @@ GDN_API gdn_status gdn_conv_state_ckpt(const gdn_config *cfg, int32_t n_seqs, in
  */
 GDN_API gdn_status gdn_state_check(const float *S, int64_t n_values, int32_t *stats, gdn_stream_t stream);
 
+/*
+ * gdn_prefill_fused -- the whole mixer over packed sequences (the work of
+ * gdn_conv_gate_prep, gdn_prefill_chunked and gdn_gated_rmsnorm, the page's
+ * gated DeltaNet paragraph in its order) without storing q, k, v, beta or g:
+ * the chunked kernels compute them from the raw qkv rows and the logits as
+ * they load them. Same arithmetic as the three calls; o is kept in the
+ * workspace (act dtype) between the delta rule and the norm.
+ *   qkv [T][C], beta_logit, alpha_logit [T][Hv], z, y [T][Hv][d]: act dtype
+ *   conv_w [C][4], dt_bias, A_log [Hv], norm_w [d]: fp32
+ *   conv_state_in, conv_state_out [N][3][C]: act dtype; may be the same
+ *     buffer (the new state is written last)
+ *   S_in, S_out [N][Hv][d][d]: fp32; may be the same buffer
+ * qkv, conv_w and both conv states must be 16-byte aligned; `workspace`
+ * 256-byte aligned, of gdn_prefill_fused_workspace_bytes(cfg, n_seqs,
+ * n_tokens) bytes (may be NULL when that is 0). Four kernels on `stream`.
+ */
+GDN_API gdn_status gdn_prefill_fused(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens,
+                             const int32_t *cu_seqlens, const void *qkv, const void *beta_logit,
+                             const void *alpha_logit, const void *z, const float *conv_w, const float *dt_bias,
+                             const float *A_log, const float *norm_w, const void *conv_state_in,
+                             void *conv_state_out, const float *S_in, float *S_out, void *y,
+                             void *workspace, size_t workspace_bytes, gdn_stream_t stream);
+
+/* Workspace size gdn_prefill_fused needs for these sizes (0 for a bad cfg). */
+GDN_API size_t gdn_prefill_fused_workspace_bytes(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens);
+
 /* Workspace size gdn_prefill_chunked needs for these sizes (0 for a bad cfg). */
 GDN_API size_t gdn_prefill_workspace_bytes(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens);
 

@@ -106,6 +106,22 @@ def gpu_prefill(w: wl.Workload, x: dict, inplace: bool = False, l2_mode: str = "
                 conv_out_bits=bits(conv_out))
 
 
+def gpu_prefill_fused(w: wl.Workload, x: dict, inplace: bool = False, l2_mode: str = "clamp"):
+    """Run the whole mixer as one gdn_prefill_fused call on the GPU; host
+    copies of y and the states."""
+    cfg = B.make_config(w.n_qk_heads, w.n_v_heads, w.act, l2_mode=l2_mode)
+    cu = x["cu_seqlens"]
+    N, T = len(cu) - 1, int(cu[-1])
+    run = Lyr.PrefillFused(cfg, N, T)
+    t = {k: dev(v) for k, v in x.items()}
+    conv_out = t["conv0"] if inplace else torch.empty_like(t["conv0"])
+    S_out = t["S0"] if inplace else torch.empty_like(t["S0"])
+    run(t["cu_seqlens"], t["qkv"], t["z"], t["b"], t["a"], t["conv_w"], t["dt_bias"], t["A_log"],
+        t["norm_w"], t["conv0"], conv_out, t["S0"], S_out)
+    torch.cuda.synchronize()
+    return dict(y=host(run.y), S_out=host(S_out), conv_out=conv_out, conv_out_bits=bits(conv_out))
+
+
 def gpu_decode(w: wl.Workload, x: dict, l2_mode: str = "clamp"):
     """Run the decode loop (prep -> step -> norm per step) on the GPU.
     Returns y, o [steps, N, Hv, d], final S and conv state."""

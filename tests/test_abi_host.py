@@ -233,3 +233,32 @@ def test_projection_validation(lib):
     assert out(2, 80, FAKE[0], FAKE[1], FAKE[0] + 64) == B.GDN_E_INVALID_ARG   # out overlaps y
     assert out(2, 80, FAKE[0] + 2, FAKE[1], FAKE[2]) == B.GDN_E_INVALID_ARG    # y misaligned
     assert out(2, 80, FAKE[0], None, FAKE[2]) == B.GDN_E_INVALID_ARG
+
+
+def test_prefill_fused_validation(lib):
+    cfg = B.make_config(2, 4, "bf16")
+    need = B.gdn_prefill_fused_workspace_bytes(cfg, 2, 100)
+    base = B.gdn_prefill_workspace_bytes(cfg, 2, 100)
+    assert need >= base + 100 * 4 * 128 * 2 and need % 2 == 0
+    # qkv, b, a, z, conv_w, dt_bias, A_log, norm_w, conv_in, conv_out, S_in, S_out, y, ws
+    p = FAKE[:14]
+    call = lambda t, ptrs, ws_bytes=need, n=2: lib.gdn_prefill_fused(ctypes.byref(cfg), n, t, FAKE[15], *ptrs,
+                                                                  ws_bytes, None)
+    assert call(100, p, need - 1) == B.GDN_E_WORKSPACE
+    q = p[:]
+    q[13] = FAKE[13] + 64                  # workspace not 256-byte aligned
+    assert call(100, q) == B.GDN_E_WORKSPACE
+    q = p[:]
+    q[0] = FAKE[0] + 8                     # qkv not 16-byte aligned
+    assert call(100, q) == B.GDN_E_INVALID_ARG
+    q = p[:]
+    q[12] = q[3]                           # y on top of z
+    assert call(100, q) == B.GDN_E_INVALID_ARG
+    q = p[:]
+    q[9] = q[8] + 256                      # conv states partly overlapping
+    assert call(100, q) == B.GDN_E_INVALID_ARG
+    q = p[:]
+    q[3] = None
+    assert call(100, q) == B.GDN_E_INVALID_ARG
+    assert call(5, p, need, n=0) == B.GDN_E_INVALID_ARG     # tokens without sequences
+    assert call(0, p, 0, n=0) == B.GDN_OK
