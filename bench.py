@@ -75,7 +75,8 @@ def log(*a):
 # Source files behind each traffic record (plus the shared headers): a record
 # is only used while these are unchanged.
 TRAFFIC_SOURCES = {
-    "prefill_core": ("prefill.hip",), "prefill_prep": ("prep.hip",), "prefill_norm": ("norm.hip",),
+    "prefill_core": ("prefill.hip",), "prefill_fused_core": ("prefill.hip",),
+    "prefill_prep": ("prep.hip",), "prefill_norm": ("norm.hip",),
     "decode_b64": ("decode.hip",), "decode_b1": ("decode.hip",),
     "decode_fused_b64": ("decode_fused.hip",), "decode_fused_b1": ("decode_fused.hip",),
 }
@@ -114,6 +115,14 @@ def measured_traffic(key: str):
     return int(k["fetch_bytes"] + k["write_bytes"])
 
 
+def _kernel_key(name: str) -> str:
+    """A kernel's name without namespace noise and argument list, with the
+    precision enum spelled out (`chunk_state_kernel<BF16X3, gdn::bf16_t, true>`)."""
+    name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    name = name.replace("(gdn::Prec)1", "BF16X3").replace("(gdn::Prec)0", "F32")
+    return name.split("(")[0]
+
+
 def summarize_rocprof(db_path: str) -> str:
     """Per-kernel summary of a rocprofv3 database: durations from a kernel
     trace, or per-dispatch counter values from a --pmc run."""
@@ -124,9 +133,7 @@ def summarize_rocprof(db_path: str) -> str:
     lines = []
 
     def short(name):
-        name = name.replace("(anonymous namespace)::", "").replace("void ", "")
-        name = name.replace("(gdn::Prec)1", "BF16X3").replace("(gdn::Prec)0", "F32")
-        return name.split("(")[0][:70]
+        return _kernel_key(name)[:70]
     if "counters_collection" in tables and db.execute("select count(*) from counters_collection").fetchone()[0]:
         per = collections.defaultdict(float)
         for k, d, n, v in db.execute("select kernel_name, dispatch_id, counter_name, value from counters_collection"):
@@ -159,7 +166,7 @@ def _pmc_means(db_path: str, counter: str, reduce=None) -> dict:
             per[(k, d)] += v
     agg = collections.defaultdict(list)
     for (k, d), v in per.items():
-        agg[k.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]].append(v)
+        agg[_kernel_key(k)].append(v)
     return {k: (reduce(v) if reduce else sum(v) / len(v)) for k, v in agg.items()}
 
 
@@ -186,8 +193,12 @@ def write_traffic(dbs):
 
     kernels = {}
     for key, run, subs, what in (
-            ("prefill_core", "prefill", ("chunk_local", "chunk_state"),
+            ("prefill_core", "prefill", ("chunk_local_kernel<BF16X3, gdn::bf16_t, false>",
+                                         "chunk_state_kernel<BF16X3, gdn::bf16_t, false>"),
              "gdn_prefill_chunked on the T=4096, Hv=48 bf16 workload (chunk_local + chunk_state)"),
+            ("prefill_fused_core", "prefill", ("chunk_local_kernel<BF16X3, gdn::bf16_t, true>",
+                                               "chunk_state_kernel<BF16X3, gdn::bf16_t, true>"),
+             "the chunked kernels of gdn_prefill_fused, T=4096 Hv=48 bf16 (q, k, v, gates formed inside)"),
             ("prefill_prep", "prefill", ("prep_kernel",), "gdn_conv_gate_prep, T=4096 Hv=48 bf16"),
             ("prefill_norm", "prefill", ("norm_kernel",), "gdn_gated_rmsnorm, T=4096 Hv=48 bf16"),
             ("decode_b64", "decode_b64", ("decode_kernel",), "gdn_decode_step, batch 64, Hv=32"),

@@ -3,9 +3,10 @@
 ``Prefill`` runs gdn_conv_gate_prep -> gdn_prefill_chunked -> gdn_gated_rmsnorm
 over packed sequences; ``Decode`` runs gdn_conv_gate_prep -> gdn_decode_step ->
 gdn_gated_rmsnorm for one token per sequence; ``DecodeFused`` runs the same
-step as the single launch gdn_decode_fused. ``Block`` and ``DecodeBlock`` put
-gdn_in_proj before and gdn_out_proj after ``Prefill`` and ``DecodeFused``
-(the whole token-mixer block from the layer input). Each allocates its intermediates
+step as the single launch gdn_decode_fused. ``PrefillFused`` is the whole prefill
+mixer as one gdn_prefill_fused call. ``Block`` and ``DecodeBlock`` put
+gdn_in_proj before and gdn_out_proj after ``PrefillFused`` and
+``DecodeFused`` (the whole token-mixer block from the layer input). Each allocates its intermediates
 (q, k, v, beta, g, o, y, workspace, the second conv-state buffer) once with
 torch and then only calls the library, so a timed loop allocates nothing.
 """
@@ -144,11 +145,11 @@ class _Proj:
 
 
 class Block:
-    """The block over packed sequences: gdn_in_proj -> Prefill -> gdn_out_proj."""
+    """The block over packed sequences: gdn_in_proj -> gdn_prefill_fused -> gdn_out_proj."""
 
     def __init__(self, cfg: B.gdn_config, n_seqs: int, n_tokens: int, hidden: int, device="cuda"):
         self.cfg, self.T = cfg, n_tokens
-        self.mixer = Prefill(cfg, n_seqs, n_tokens, device)
+        self.mixer = PrefillFused(cfg, n_seqs, n_tokens, device)
         self.proj = _Proj(cfg, n_tokens, hidden, device)
 
     def __call__(self, cu, x, w_qkv, w_gate, w_beta, w_alpha, w_out, conv_w, dt_bias, A_log, norm_w, conv_in,

@@ -194,7 +194,7 @@ def test_block_prefill(lengths, heads, hidden):
     out = run(t["cu_seqlens"], t["x"], t["w_qkv"], t["w_gate"], t["w_beta"], t["w_alpha"], t["w_out"],
               t["conv_w"], t["dt_bias"], t["A_log"], t["norm_w"], t["conv0"], conv_out, t["S0"], S_out)
     torch.cuda.synchronize()
-    ref = _oracle_block(w, x, hidden, round_o=True)     # Prefill stores o in bf16 before the norm
+    ref = _oracle_block(w, x, hidden, round_o=True)     # the prefill stores o in bf16 before the norm
     _check_block_out("block out", P.host(out), ref, x["w_out"])
     P.check("block S_out", P.host(S_out), ref["S_out"], "bf16")
     P.check("block conv_out", P.host(conv_out), ref["conv_out"], "bf16")
