@@ -485,9 +485,25 @@ template <> __device__ __forceinline__ void lds_put4<Prec::BF16X3>(uint8_t *buf,
 
 // K rows of the current chunk in LDS, for the transposed (K^T) fragments of
 // the state update: BF16X3 keeps the hi and lo planes as bf16, F32 one fp32
-// plane. Row pitch kLdKt elements: rows stay 8-byte aligned and the gathers
-// of a wave (lane groups 16 g reading rows 8 g + e) fall on distinct banks.
-constexpr int kLdKt = kHeadDim + 4;
+// plane, row-major (token rows, key index contiguous).
+//
+// BF16X3 reads its K^T fragments with the gfx950 transpose read
+// ds_read_b64_tr_b16: within each group of 16 lanes, output lane j receives
+// element j & 3 of the 4 16-bit values that lanes (j >> 2) + 4 e (e = 0..3)
+// address (checked on the GPU). Lane s of group g pointing at row
+// t0 + (s >> 2), columns i0 + 4 (s & 3) .. +3 therefore yields
+// K[t0 + e][i0 + s] for e = 0..3: four consecutive tokens of one key index,
+// half of an A fragment of K^T. Rows of kLdKt = 144 elements (288 bytes)
+// keep the 16-byte stores aligned and put 4 consecutive rows of a read on
+// disjoint banks.
+constexpr int kLdKt = kHeadDim + 16;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ s16x4 lds_read_tr16(const __bf16 *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4 *)(const_cast<__bf16 *>(p)));
+}
 
 template <Prec P> struct KtLds;
 template <> struct KtLds<Prec::BF16X3> {
@@ -499,43 +515,43 @@ template <> struct KtLds<Prec::BF16X3> {
     __bf16 *hi = reinterpret_cast<__bf16 *>(buf);
     __bf16 *lo = hi + kChunk * kLdKt;
     const int off = (16 * rt + (l & 15)) * kLdKt + 32 * ks + 8 * (l >> 4);
-    *reinterpret_cast<bf16x4 *>(hi + off) = __builtin_shufflevector(f.hi, f.hi, 0, 1, 2, 3);
-    *reinterpret_cast<bf16x4 *>(hi + off + 4) = __builtin_shufflevector(f.hi, f.hi, 4, 5, 6, 7);
-    *reinterpret_cast<bf16x4 *>(lo + off) = __builtin_shufflevector(f.lo, f.lo, 0, 1, 2, 3);
-    *reinterpret_cast<bf16x4 *>(lo + off + 4) = __builtin_shufflevector(f.lo, f.lo, 4, 5, 6, 7);
+    *reinterpret_cast<bf16x8 *>(hi + off) = f.hi;
+    *reinterpret_cast<bf16x8 *>(lo + off) = f.lo;
   }
   // Fragment (it, ks) of K^T: row i = 16 it + l % 16, indices (tokens)
-  // t = 32 ks + 8 (l / 16) .. +7.
+  // t = 32 ks + 8 (l / 16) .. +7, as two transpose reads per plane.
   static __device__ __forceinline__ Op<Prec::BF16X3>::Frag get(const uint8_t *buf, int it, int ks) {
-    const int l = lane_id();
+    const int l = lane_id(), s = l & 15;
     const __bf16 *hi = reinterpret_cast<const __bf16 *>(buf);
     const __bf16 *lo = hi + kChunk * kLdKt;
-    const int off = (32 * ks + 8 * (l >> 4)) * kLdKt + 16 * it + (l & 15);
+    const int off = (32 * ks + 8 * (l >> 4) + (s >> 2)) * kLdKt + 16 * it + 4 * (s & 3);
+    const s16x4 h0 = lds_read_tr16(hi + off), h1 = lds_read_tr16(hi + off + 4 * kLdKt);
+    const s16x4 l0 = lds_read_tr16(lo + off), l1 = lds_read_tr16(lo + off + 4 * kLdKt);
     Op<Prec::BF16X3>::Frag f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      f.hi[e] = hi[off + e * kLdKt];
-      f.lo[e] = lo[off + e * kLdKt];
-    }
+    f.hi = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
+    f.lo = __builtin_bit_cast(bf16x8, __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7));
     return f;
   }
 };
+// F32 gathers its K^T fragments one value at a time; its row pitch of 132
+// floats puts the four lane groups of a gather on two bank halves.
+constexpr int kLdKtF32 = kHeadDim + 4;
 template <> struct KtLds<Prec::F32> {
-  static constexpr int kBytes = kChunk * kLdKt * 4;
+  static constexpr int kBytes = kChunk * kLdKtF32 * 4;
   static __device__ __forceinline__ void put(uint8_t *buf, int rt, int ks, const Op<Prec::F32>::Frag &f) {
     const int l = lane_id();
-    float *k = reinterpret_cast<float *>(buf) + (16 * rt + (l & 15)) * kLdKt + 32 * ks + 8 * (l >> 4);
+    float *k = reinterpret_cast<float *>(buf) + (16 * rt + (l & 15)) * kLdKtF32 + 32 * ks + 8 * (l >> 4);
     *reinterpret_cast<f32x4 *>(k) = f.a;
     *reinterpret_cast<f32x4 *>(k + 4) = f.b;
   }
   static __device__ __forceinline__ Op<Prec::F32>::Frag get(const uint8_t *buf, int it, int ks) {
     const int l = lane_id();
-    const float *k = reinterpret_cast<const float *>(buf) + (32 * ks + 8 * (l >> 4)) * kLdKt + 16 * it + (l & 15);
+    const float *k = reinterpret_cast<const float *>(buf) + (32 * ks + 8 * (l >> 4)) * kLdKtF32 + 16 * it + (l & 15);
     Op<Prec::F32>::Frag f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      f.a[e] = k[e * kLdKt];
-      f.b[e] = k[(e + 4) * kLdKt];
+      f.a[e] = k[e * kLdKtF32];
+      f.b[e] = k[(e + 4) * kLdKtF32];
     }
     return f;
   }
