@@ -586,38 +586,46 @@ __device__ __forceinline__ f32x4 conv_silu4(const Raw (&raw)[kConvK], const floa
 }
 
 // ---------------------------------------------------------------------------
-// chunk_state: per (sequence, V-head, 32-column slab). 8 waves; wave w has
-// rt = w % 4. Per chunk:
-//   X/Y : waves 0-3 X = K S, waves 4-7 Y = Q S (rows 16 rt, both column tiles)
-//   R   : waves 0-3 R = V - diag(Gam) X            -> R in LDS
-//   D   : waves 0-3 D = Tm R (rows 16 rt)          -> D and diag(k~) D
-//         in LDS, k~_r = exp(gam_n - gam_r)
-//   O   : waves 4-7 O = s (diag(Gam) Y + P D)      (rows 16 rt)
-//   S   : all waves S <- Gam_n S + K^T diag(k~) D  (state rows 16 w)
-// Left operands stay in registers: K or Q rows (4 fragments), Tm or P rows
-// (2); each set is reloaded for the next chunk right after its last use in
-// this one, so its loads overlap the rest of the chunk. The K^T fragments of
-// the state update are not loaded: the x-waves leave their K fragments in
-// LDS and every wave gathers its K^T fragments from there (the kernel is
-// bound by how many bytes a CU pulls from L2 per chunk).
-template <Prec P, typename TA, bool kFused>
+// chunk_state: per (sequence, V-head, 32-column slab). 8 waves in two roles
+// of four, row tile rt = w % 4: waves 0-3 (x-waves) hold K and Tm rows,
+// waves 4-7 (y-waves) Q and P rows. Per chunk c:
+//   1. x: X = K S, R = V - diag(Gam) X -> R in LDS      y: Y = Q S
+//   2. x: D = Tm R -> D (one buffer per chunk parity) and diag(k~) D in LDS,
+//         k~_r = exp(gam_n - gam_r)
+//      y: O of chunk c - 1 = s (diag(Gam) Y + P D), from that chunk's D
+//   3. all: S <- Gam_n S + K^T diag(k~) D (state rows 16 w)
+// O trails D by one chunk, so it is formed while the x-waves form D, off the
+// chain S -> X -> D -> S that orders the chunks; the last chunk's O follows
+// the loop.
+// Each role keeps its left operands in registers of its own (K or Q rows: 4
+// fragments; Tm or P rows: 2), reloaded for the next chunk right after their
+// last use so that the loads overlap the rest of the chunk. No register is
+// loaded by both roles, so the compiler's memory-wait counts never make a
+// wave wait for loads only the other role issues. The loads that must land
+// before a chunk ends (V rows, gam) belong to the x-waves, whose memory
+// operations are loads only (checkpoint stores aside), so the y-waves'
+// pending O stores never hold them up. The K^T fragments of the state update
+// are not loaded: the x-waves leave their K fragments in LDS and every wave
+// reads its K^T fragments from there.
+template <Prec P, typename TA, bool kFused, bool kCkpt>
 __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParams p, int64_t max_chunks) {
   using Frag = typename Op<P>::Frag;
-  __shared__ __attribute__((aligned(16))) uint8_t Stb[8 * kLdsBlk];    // S: B of K S, Q S (2 col x 4 k tiles)
-  __shared__ __attribute__((aligned(16))) uint8_t Rtb[4 * kLdsBlk];    // R: B of Tm R (2 x 2)
-  __shared__ __attribute__((aligned(16))) uint8_t Dtb[4 * kLdsBlk];    // D: B of P D
-  __shared__ __attribute__((aligned(16))) uint8_t Dsb[4 * kLdsBlk];    // diag(k~) D: B of K^T (.)
-  __shared__ __attribute__((aligned(16))) float Vs[kChunk * kLdV];    // V rows of the slab (fp32)
-  __shared__ __attribute__((aligned(16))) float Os[4 * 16 * kLdOs];   // O staging, 16 rows per y-wave
+  __shared__ __attribute__((aligned(16))) uint8_t Stb[8 * kLdsBlk];      // S: B of K S, Q S (2 col x 4 k tiles)
+  __shared__ __attribute__((aligned(16))) uint8_t Rtb[4 * kLdsBlk];      // R: B of Tm R (2 x 2)
+  __shared__ __attribute__((aligned(16))) uint8_t Dtb[2][4 * kLdsBlk];   // D: B of P D, by chunk parity
+  __shared__ __attribute__((aligned(16))) uint8_t Dsb[4 * kLdsBlk];      // diag(k~) D: B of K^T (.)
+  __shared__ __attribute__((aligned(16))) float Vs[kChunk * kLdV];      // V rows of the slab (fp32)
+  __shared__ __attribute__((aligned(16))) float Os[4 * 16 * kLdOs];     // O staging, 16 rows per y-wave
   __shared__ __attribute__((aligned(16))) uint8_t Ktb[KtLds<P>::kBytes];   // K rows of the chunk
-  __shared__ float G_s[kChunk];            // exp(gam_r)
-  __shared__ float ksc_s[kChunk];          // exp(gam_n - gam_r)
+  __shared__ float4 Vw[kFused ? kSlab : 1];  // conv taps of the slab's V channels
+  __shared__ float G_s[kChunk];              // exp(gam_r)
+  __shared__ float ksc_s[kChunk];            // exp(gam_n - gam_r)
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = lane_id();
   const int rt = wave & 3;
-  const bool x_wave = wave < 4;
+  const bool x_wave = __builtin_amdgcn_readfirstlane(wave) < 4;   // uniform per wave
   const int lr = 4 * (lane >> 4);    // accumulator row offset of this lane
   const int lc = lane & 15;          // accumulator column of this lane
   // Block order: workgroups are dealt to the 8 XCDs round-robin (block b on
@@ -661,38 +669,39 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
   // Operand sources of chunk c (fragment-major blocks).
   const size_t qk_step = static_cast<size_t>(p.n_qk) * kQkBytes;
   const size_t v_step = static_cast<size_t>(p.n_v) * kVBytes;
-  const uint8_t *qk0 = ws.qk + (static_cast<size_t>(cid0) * p.n_qk + hk) * kQkBytes;
-  const uint8_t *v0 = ws.v + (static_cast<size_t>(cid0) * p.n_v + j) * kVBytes;
-  const uint8_t *xy_src0 = qk0 + (x_wave ? 0 : kKBytes);             // K rows or Q rows
-  const uint8_t *d_src0 = v0 + (x_wave ? 0 : kMatBytes);             // Tm rows or P rows
-  const int v_row = tid / (kSlab / 4), v_c4 = tid % (kSlab / 4);
+  const uint8_t *k_src0 = ws.qk + (static_cast<size_t>(cid0) * p.n_qk + hk) * kQkBytes;   // K rows
+  const uint8_t *q_src0 = k_src0 + kKBytes;                                               // Q rows
+  const uint8_t *t_src0 = ws.v + (static_cast<size_t>(cid0) * p.n_v + j) * kVBytes;       // Tm rows
+  const uint8_t *p_src0 = t_src0 + kMatBytes;                                             // P rows
+  // V rows (x-waves): thread tid holds row tid / 4, slab channels
+  // 8 (tid % 4) .. +7.
+  const int v_row = (tid & (4 * kWave - 1)) >> 2, v_c8 = tid & 3;
 
-  Frag fxy[kHeadDim / 32], fd[kChunk / 32];
-  f32x4 pvv;
-  // Fused form: the raw rows t - 3 .. t of this thread's 4 V channels are
+  Frag fk[kHeadDim / 32], fq[kHeadDim / 32], ft[kChunk / 32], fp[kChunk / 32];
+  f32x4 pv[2];
+  // Fused form: the raw rows t - 3 .. t of this thread's 8 V channels are
   // loaded with the other operands of the next chunk and turned into
-  // conv + SiLU when committed to LDS; the taps of the 4 channels are loaded
-  // once.
+  // conv + SiLU when committed to LDS.
   using Raw = typename RawAct<TA>::type;
-  Raw vraw[kConvK];
-  float4 vw[4];
+  Raw vraw[kConvK][2];
   const int Cq = kHeadDim * (2 * p.n_qk + p.n_v);
-  const int vch = 2 * p.n_qk * kHeadDim + j * kHeadDim + col_base + 4 * v_c4;   // first channel in qkv
+  const int vch0 = 2 * p.n_qk * kHeadDim + j * kHeadDim + col_base;   // first slab channel in qkv
   if constexpr (kFused) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) vw[e] = reinterpret_cast<const float4 *>(p.conv_w)[vch + e];
+    if (tid < kSlab) Vw[tid] = reinterpret_cast<const float4 *>(p.conv_w)[vch0 + tid];
+    block_sync_lds();
   }
   double pg = 0.0, pg_end = 0.0;
 
-#define GDN_LOAD_XY(c)                                                                               \
+#define GDN_LOAD_ROWS(dst, src0, c)                                                                   \
   _Pragma("unroll") for (int ks = 0; ks < kHeadDim / 32; ++ks)                                       \
-    fxy[ks] = FragIO<P>::load(xy_src0 + (c) * qk_step, kHeadDim / 32, rt, ks)
+    dst[ks] = FragIO<P>::load(src0 + (c) * qk_step, kHeadDim / 32, rt, ks)
   // Row tiles 0 and 1 of Tm and P end before column 32: their second k
   // step is zero and skipped.
-#define GDN_LOAD_D(c)                                                                                \
+#define GDN_LOAD_MAT(dst, src0, c)                                                                    \
   _Pragma("unroll") for (int ks = 0; ks < kChunk / 32; ++ks)                                         \
-    if (ks == 0 || rt >= 2) fd[ks] = FragIO<P>::load(d_src0 + (c) * v_step, kChunk / 32, rt, ks)
-  // V slab piece and gam of chunk c (committed to LDS after the chunk before it).
+    if (ks == 0 || rt >= 2) dst[ks] = FragIO<P>::load(src0 + (c) * v_step, kChunk / 32, rt, ks)
+  // V slab rows and gam of chunk c (x-waves; committed to LDS after the chunk
+  // before it).
 #define GDN_LOAD_VG(c)                                                                               \
   do {                                                                                               \
     const int t0_ = seq0 + (c) * kChunk, len_ = min(kChunk, L - (c) * kChunk);                       \
@@ -703,11 +712,13 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
         const TA *src_ = pos_ < 0 ? static_cast<const TA *>(p.st_in) +                               \
                                         (static_cast<size_t>(n) * (kConvK - 1) + (pos_ + kConvK - 1)) * Cq \
                                   : static_cast<const TA *>(p.qkv) + static_cast<size_t>(seq0 + pos_) * Cq; \
-        vraw[r_] = *reinterpret_cast<const Raw *>(src_ + vch);                                       \
+        vraw[r_][0] = *reinterpret_cast<const Raw *>(src_ + vch0 + 8 * v_c8);                        \
+        vraw[r_][1] = *reinterpret_cast<const Raw *>(src_ + vch0 + 8 * v_c8 + 4);                    \
       }                                                                                              \
     } else {                                                                                         \
-      pvv = *reinterpret_cast<const f32x4 *>(p.v + (t0_ + min(v_row, len_ - 1)) * v_stride +        \
-                                             j * kHeadDim + col_base + 4 * v_c4);                    \
+      const float *src_ = p.v + (t0_ + min(v_row, len_ - 1)) * v_stride + j * kHeadDim + col_base + 8 * v_c8; \
+      pv[0] = *reinterpret_cast<const f32x4 *>(src_);                                                \
+      pv[1] = *reinterpret_cast<const f32x4 *>(src_ + 4);                                            \
     }                                                                                                \
     if (tid < kChunk) {                                                                              \
       const double *gm = ws.gam + (static_cast<size_t>(cid0 + (c)) * p.n_v + j) * kChunk;            \
@@ -721,126 +732,172 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
   do {                                                                                               \
     const int len_ = min(kChunk, L - (c) * kChunk);                                                  \
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};                                                        \
-    if constexpr (kFused) pvv = conv_silu4(vraw, vw);                                                \
-    *reinterpret_cast<f32x4 *>(Vs + v_row * kLdV + 4 * v_c4) = v_row < len_ ? pvv : zero4;          \
+    if constexpr (kFused) {                                                                          \
+      _Pragma("unroll") for (int h_ = 0; h_ < 2; ++h_) {                                             \
+        const Raw raw_[kConvK] = {vraw[0][h_], vraw[1][h_], vraw[2][h_], vraw[3][h_]};               \
+        const float4 w_[4] = {Vw[8 * v_c8 + 4 * h_], Vw[8 * v_c8 + 4 * h_ + 1], Vw[8 * v_c8 + 4 * h_ + 2], \
+                              Vw[8 * v_c8 + 4 * h_ + 3]};                                            \
+        pv[h_] = conv_silu4(raw_, w_);                                                               \
+      }                                                                                              \
+    }                                                                                                \
+    float *dst_ = Vs + v_row * kLdV + 8 * v_c8;                                                      \
+    *reinterpret_cast<f32x4 *>(dst_) = v_row < len_ ? pv[0] : zero4;                                 \
+    *reinterpret_cast<f32x4 *>(dst_ + 4) = v_row < len_ ? pv[1] : zero4;                             \
     if (tid < kChunk) {                                                                              \
       G_s[tid] = expf(static_cast<float>(pg));                                                       \
       ksc_s[tid] = expf(static_cast<float>(pg_end - pg));                                            \
     }                                                                                                \
   } while (0)
 
-  if (nchunks > 0) {
-    GDN_LOAD_XY(0);
-    GDN_LOAD_D(0);
-    GDN_LOAD_VG(0);
-    GDN_COMMIT_VG(0);
-  }
-
-  for (int ci = 0; ci < nchunks; ++ci) {
-    const int t0 = seq0 + ci * kChunk;
-    const int len = min(kChunk, L - ci * kChunk);
-    // Operands of the next chunk (the last chunk reloads itself, so every
-    // iteration issues the same loads).
-    const int cn = min(ci + 1, nchunks - 1);
-    block_sync_lds();                        // St, V, gam of chunk ci visible
-    const float g_end = G_s[kChunk - 1];
-    GDN_LOAD_VG(cn);
-
-    // X = K S (waves 0-3) or Y = Q S (waves 4-7), rows 16 rt, both column tiles.
-    f32x4 XY[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  // y-waves: O rows 16 rt of chunk c = s * acc, staged in LDS and written out
+  // with one 16-byte store per lane (bf16) or two (fp32).
+  auto store_o = [&](int c, const f32x4 (&acc)[2]) {
+    const int t0_ = seq0 + c * kChunk, len_ = min(kChunk, L - c * kChunk);
+    float *Ow = Os + rt * 16 * kLdOs;
 #pragma unroll
-    for (int ks = 0; ks < kHeadDim / 32; ++ks)
-      Op<P>::mma2(XY[0], XY[1], fxy[ks], lds_frag<P>(Stb, ks), lds_frag<P>(Stb, 4 + ks));
-    if (x_wave) {  // K of this chunk to LDS for the K^T fragments of the state update
+    for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-      for (int ks = 0; ks < kHeadDim / 32; ++ks) KtLds<P>::put(Ktb, rt, ks, fxy[ks]);
+      for (int r = 0; r < 4; ++r) Ow[acc_row(r) * kLdOs + 16 * ct + acc_col()] = scale * acc[ct][r];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave reads back only its own rows
+    const int orow = lane >> 2, oc = 8 * (lane & 3);
+    const float *src = Ow + orow * kLdOs + oc;
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(src);
+    const f32x4 b = *reinterpret_cast<const f32x4 *>(src + 4);
+    if (16 * rt + orow < len_) {
+      const size_t dst = (t0_ + 16 * rt + orow) * v_stride + j * kHeadDim + col_base + oc;
+      Act<TA>::store4(o, dst, make_float4(a[0], a[1], a[2], a[3]));
+      Act<TA>::store4(o, dst + 4, make_float4(b[0], b[1], b[2], b[3]));
     }
-    GDN_LOAD_XY(cn);
-    if (x_wave) {
+  };
+
+  // 3. S <- Gam_n S + K^T (diag(k~) D), state rows 16 wave; then the
+  // checkpoint (the state after token (ci + 1) * 64 of the sequence) and,
+  // once every LDS read of the chunk is done, S back to LDS.
+  auto update_state = [&](int ci, float g_end) {
+    block_sync_lds();                        // D and diag(k~) D visible
+    S[0] = S[0] * g_end;
+    S[1] = S[1] * g_end;
+#pragma unroll
+    for (int ks = 0; ks < kChunk / 32; ++ks)
+      Op<P>::mma2(S[0], S[1], KtLds<P>::get(Ktb, wave, ks), lds_frag<P>(Dsb, ks), lds_frag<P>(Dsb, 2 + ks));
+    if constexpr (kCkpt) {
+      if ((ci + 1) % p.ckpt_chunks == 0 && (ci + 1) * kChunk <= L) {
+        const int c = (ci + 1) / p.ckpt_chunks - 1;
+        if (c < p.ckpt_cap) {
+          float *dst = p.S_ckpt + ((static_cast<size_t>(n) * p.ckpt_cap + c) * p.n_v + j) * kHeadDim * kHeadDim;
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              dst[static_cast<size_t>(16 * wave + acc_row(r)) * kHeadDim + col_base + 16 * ct + acc_col()] = S[ct][r];
+        }
+      }
+    }
+    block_sync_lds();                        // every LDS read of chunk ci is done
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) lds_put4<P>(Stb, 4, 16 * wave + lr, 16 * ct + lc, S[ct]);
+  };
+
+  // The two roles run loops of their own (the branch is uniform per wave),
+  // with the same four barriers per chunk.
+  if (x_wave) {
+    if (nchunks > 0) {
+      GDN_LOAD_ROWS(fk, k_src0, 0);
+      GDN_LOAD_MAT(ft, t_src0, 0);
+      GDN_LOAD_VG(0);
+      GDN_COMMIT_VG(0);
+    }
+    for (int ci = 0; ci < nchunks; ++ci) {
+      // Operands of the next chunk (the last chunk reloads itself, so every
+      // iteration issues the same loads).
+      const int cn = min(ci + 1, nchunks - 1);
+      block_sync_lds();                      // S, V, gam of chunk ci visible
+      const float g_end = G_s[kChunk - 1];
+      GDN_LOAD_VG(cn);
+      // 1. X = K S, rows 16 rt, both column tiles; R = V - diag(Gam) X.
+      f32x4 X[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int ks = 0; ks < kHeadDim / 32; ++ks)
+        Op<P>::mma2(X[0], X[1], fk[ks], lds_frag<P>(Stb, ks), lds_frag<P>(Stb, 4 + ks));
+#pragma unroll
+      for (int ks = 0; ks < kHeadDim / 32; ++ks) KtLds<P>::put(Ktb, rt, ks, fk[ks]);
+      GDN_LOAD_ROWS(fk, k_src0, cn);
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         f32x4 rv;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = 16 * rt + acc_row(r);
-          rv[r] = Vs[row * kLdV + 16 * ct + acc_col()] - G_s[row] * XY[ct][r];
+          rv[r] = Vs[row * kLdV + 16 * ct + acc_col()] - G_s[row] * X[ct][r];
         }
         lds_put4<P>(Rtb, 2, 16 * rt + lr, 16 * ct + lc, rv);
       }
-    }
-    block_sync_lds();
-
-    if (x_wave) {  // D = Tm R, rows 16 rt; D^T and (diag(k~) D)^T to LDS.
+      block_sync_lds();                      // R visible
+      // 2. D = Tm R, rows 16 rt -> D and diag(k~) D in LDS.
       f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int ks = 0; ks < kChunk / 32; ++ks)
         if (ks == 0 || rt >= 2)
-          Op<P>::mma2(acc[0], acc[1], fd[ks], lds_frag<P>(Rtb, ks), lds_frag<P>(Rtb, 2 + ks));
-      GDN_LOAD_D(cn);
+          Op<P>::mma2(acc[0], acc[1], ft[ks], lds_frag<P>(Rtb, ks), lds_frag<P>(Rtb, 2 + ks));
+      GDN_LOAD_MAT(ft, t_src0, cn);
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        lds_put4<P>(Dtb, 2, 16 * rt + lr, 16 * ct + lc, acc[ct]);
+        lds_put4<P>(Dtb[ci & 1], 2, 16 * rt + lr, 16 * ct + lc, acc[ct]);
         f32x4 ds;
 #pragma unroll
         for (int r = 0; r < 4; ++r) ds[r] = acc[ct][r] * ksc_s[16 * rt + acc_row(r)];
         lds_put4<P>(Dsb, 2, 16 * rt + lr, 16 * ct + lc, ds);
       }
+      update_state(ci, g_end);
+      GDN_COMMIT_VG(cn);
     }
-    block_sync_lds();
-
-    if (!x_wave) {  // O = s (diag(Gam) Y + P D), rows 16 rt.
-      f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  } else {
+    f32x4 oy[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};   // diag(Gam) Y of the previous chunk
+    if (nchunks > 0) {
+      GDN_LOAD_ROWS(fq, q_src0, 0);
+      GDN_LOAD_MAT(fp, p_src0, 0);
+    }
+    for (int ci = 0; ci < nchunks; ++ci) {
+      const int cn = min(ci + 1, nchunks - 1);
+      block_sync_lds();                      // S, V, gam of chunk ci visible
+      const float g_end = G_s[kChunk - 1];
+      // 1. Y = Q S, rows 16 rt, both column tiles.
+      f32x4 Y[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-      for (int ks = 0; ks < kChunk / 32; ++ks)
-        if (ks == 0 || rt >= 2)
-          Op<P>::mma2(acc[0], acc[1], fd[ks], lds_frag<P>(Dtb, ks), lds_frag<P>(Dtb, 2 + ks));
-      GDN_LOAD_D(cn);
-      // Stage this wave's 16 x 32 rows of O in LDS, then write them out with
-      // one 16-byte store per lane (bf16) or two (fp32).
-      float *Ow = Os + rt * 16 * kLdOs;
+      for (int ks = 0; ks < kHeadDim / 32; ++ks)
+        Op<P>::mma2(Y[0], Y[1], fq[ks], lds_frag<P>(Stb, ks), lds_frag<P>(Stb, 4 + ks));
+      GDN_LOAD_ROWS(fq, q_src0, cn);
+      block_sync_lds();                      // (the x-waves' R)
+      // 2. O of the previous chunk = s (diag(Gam) Y + P D).
+      if (ci > 0) {
+        f32x4 acc[2] = {oy[0], oy[1]};
+#pragma unroll
+        for (int ks = 0; ks < kChunk / 32; ++ks)
+          if (ks == 0 || rt >= 2)
+            Op<P>::mma2(acc[0], acc[1], fp[ks], lds_frag<P>(Dtb[(ci - 1) & 1], ks),
+                        lds_frag<P>(Dtb[(ci - 1) & 1], 2 + ks));
+        GDN_LOAD_MAT(fp, p_src0, ci);
+        store_o(ci - 1, acc);
+      }
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 16 * rt + acc_row(r);
-          Ow[acc_row(r) * kLdOs + 16 * ct + acc_col()] = scale * (G_s[row] * XY[ct][r] + acc[ct][r]);
-        }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave reads back only its own rows
-      const int orow = lane >> 2, oc = 8 * (lane & 3);
-      const float *src = Ow + orow * kLdOs + oc;
-      const f32x4 a = *reinterpret_cast<const f32x4 *>(src);
-      const f32x4 b = *reinterpret_cast<const f32x4 *>(src + 4);
-      if (16 * rt + orow < len) {
-        const size_t dst = (t0 + 16 * rt + orow) * v_stride + j * kHeadDim + col_base + oc;
-        Act<TA>::store4(o, dst, make_float4(a[0], a[1], a[2], a[3]));
-        Act<TA>::store4(o, dst + 4, make_float4(b[0], b[1], b[2], b[3]));
-      }
+        for (int r = 0; r < 4; ++r) oy[ct][r] = G_s[16 * rt + acc_row(r)] * Y[ct][r];
+      update_state(ci, g_end);
     }
-    // S <- Gam_n S + K^T (diag(k~) D); state rows 16 wave.
-    S[0] = S[0] * g_end;
-    S[1] = S[1] * g_end;
+    // O of the last chunk (its D was made visible by the loop's barriers).
+    if (nchunks > 0) {
+      const int cl = nchunks - 1;
+      f32x4 acc[2] = {oy[0], oy[1]};
 #pragma unroll
-    for (int ks = 0; ks < kChunk / 32; ++ks)
-      Op<P>::mma2(S[0], S[1], KtLds<P>::get(Ktb, wave, ks), lds_frag<P>(Dsb, ks), lds_frag<P>(Dsb, 2 + ks));
-    // Checkpoint: the state after token (ci + 1) * 64 of the sequence.
-    if (p.ckpt_chunks > 0 && (ci + 1) % p.ckpt_chunks == 0 && (ci + 1) * kChunk <= L) {
-      const int c = (ci + 1) / p.ckpt_chunks - 1;
-      if (c < p.ckpt_cap) {
-        float *dst = p.S_ckpt + ((static_cast<size_t>(n) * p.ckpt_cap + c) * p.n_v + j) * kHeadDim * kHeadDim;
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            dst[static_cast<size_t>(16 * wave + acc_row(r)) * kHeadDim + col_base + 16 * ct + acc_col()] = S[ct][r];
-      }
+      for (int ks = 0; ks < kChunk / 32; ++ks)
+        if (ks == 0 || rt >= 2)
+          Op<P>::mma2(acc[0], acc[1], fp[ks], lds_frag<P>(Dtb[cl & 1], ks), lds_frag<P>(Dtb[cl & 1], 2 + ks));
+      store_o(cl, acc);
     }
-    block_sync_lds();                        // every LDS read of chunk ci is done
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) lds_put4<P>(Stb, 4, 16 * wave + lr, 16 * ct + lc, S[ct]);
-    GDN_COMMIT_VG(cn);
   }
-#undef GDN_LOAD_XY
-#undef GDN_LOAD_D
+#undef GDN_LOAD_ROWS
+#undef GDN_LOAD_MAT
 #undef GDN_LOAD_VG
 #undef GDN_COMMIT_VG
 
@@ -864,11 +921,17 @@ hipError_t launch_prefill(const PrefillParams &p, gdn_dtype act, hipStream_t s) 
   const int64_t pairs = static_cast<int64_t>(p.n_seqs) * p.n_v;
   const dim3 grid_state(static_cast<unsigned>((pairs + kXcds - 1) / kXcds * kXcds * (kHeadDim / kSlab)));
   const bool fused = p.qkv != nullptr;
+  if (fused && p.ckpt_chunks > 0) return hipErrorInvalidValue;   // the fused form writes no checkpoints
 #define GDN_LAUNCH(PR, TA, FU)                                                                                \
   do {                                                                                                        \
     if (p.n_tokens > 0)                                                                                       \
       hipLaunchKernelGGL((chunk_local_kernel<PR, TA, FU>), grid_local, dim3(kLocalThreads), 0, s, p, chunks); \
-    hipLaunchKernelGGL((chunk_state_kernel<PR, TA, FU>), grid_state, dim3(kStateThreads), 0, s, p, chunks);   \
+    if (p.ckpt_chunks > 0 && !(FU))                                                                           \
+      hipLaunchKernelGGL((chunk_state_kernel<PR, TA, false, true>), grid_state, dim3(kStateThreads), 0, s, p,  \
+                         chunks);                                                                             \
+    else                                                                                                      \
+      hipLaunchKernelGGL((chunk_state_kernel<PR, TA, FU, false>), grid_state, dim3(kStateThreads), 0, s, p,    \
+                         chunks);                                                                             \
   } while (0)
   if (act == GDN_BF16) {
     if (fused) GDN_LAUNCH(Prec::BF16X3, bf16_t, true);
