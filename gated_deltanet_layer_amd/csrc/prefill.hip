@@ -593,7 +593,9 @@ __device__ __forceinline__ f32x4 conv_silu4(const Raw (&raw)[kConvK], const floa
 //   2. x: D = Tm R -> D (one buffer per chunk parity) and diag(k~) D in LDS,
 //         k~_r = exp(gam_n - gam_r)
 //      y: O of chunk c - 1 = s (diag(Gam) Y + P D), from that chunk's D
-//   3. all: S <- Gam_n S + K^T diag(k~) D (state rows 16 w)
+//   3. all: S <- Gam_n S + K^T diag(k~) D (state rows 16 w) -> S in LDS
+// S lives in two LDS buffers by chunk parity, so that writing the new S
+// needs no barrier of its own: three barriers per chunk.
 // O trails D by one chunk, so it is formed while the x-waves form D, off the
 // chain S -> X -> D -> S that orders the chunks; the last chunk's O follows
 // the loop.
@@ -610,7 +612,7 @@ __device__ __forceinline__ f32x4 conv_silu4(const Raw (&raw)[kConvK], const floa
 template <Prec P, typename TA, bool kFused, bool kCkpt>
 __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParams p, int64_t max_chunks) {
   using Frag = typename Op<P>::Frag;
-  __shared__ __attribute__((aligned(16))) uint8_t Stb[8 * kLdsBlk];      // S: B of K S, Q S (2 col x 4 k tiles)
+  __shared__ __attribute__((aligned(16))) uint8_t Stb[2][8 * kLdsBlk];   // S: B of K S, Q S, by chunk parity
   __shared__ __attribute__((aligned(16))) uint8_t Rtb[4 * kLdsBlk];      // R: B of Tm R (2 x 2)
   __shared__ __attribute__((aligned(16))) uint8_t Dtb[2][4 * kLdsBlk];   // D: B of P D, by chunk parity
   __shared__ __attribute__((aligned(16))) uint8_t Dsb[4 * kLdsBlk];      // diag(k~) D: B of K^T (.)
@@ -664,7 +666,7 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
     for (int r = 0; r < 4; ++r)
       S[ct][r] = p.S_in[sbase + static_cast<size_t>(16 * wave + acc_row(r)) * kHeadDim + col_base + 16 * ct + acc_col()];
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) lds_put4<P>(Stb, 4, 16 * wave + lr, 16 * ct + lc, S[ct]);
+  for (int ct = 0; ct < 2; ++ct) lds_put4<P>(Stb[0], 4, 16 * wave + lr, 16 * ct + lc, S[ct]);
 
   // Operand sources of chunk c (fragment-major blocks).
   const size_t qk_step = static_cast<size_t>(p.n_qk) * kQkBytes;
@@ -771,8 +773,8 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
   };
 
   // 3. S <- Gam_n S + K^T (diag(k~) D), state rows 16 wave; then the
-  // checkpoint (the state after token (ci + 1) * 64 of the sequence) and,
-  // once every LDS read of the chunk is done, S back to LDS.
+  // checkpoint (the state after token (ci + 1) * 64 of the sequence) and S
+  // to the other S buffer, whose last readers (chunk ci - 1) are done.
   auto update_state = [&](int ci, float g_end) {
     block_sync_lds();                        // D and diag(k~) D visible
     S[0] = S[0] * g_end;
@@ -793,13 +795,12 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
         }
       }
     }
-    block_sync_lds();                        // every LDS read of chunk ci is done
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) lds_put4<P>(Stb, 4, 16 * wave + lr, 16 * ct + lc, S[ct]);
+    for (int ct = 0; ct < 2; ++ct) lds_put4<P>(Stb[(ci + 1) & 1], 4, 16 * wave + lr, 16 * ct + lc, S[ct]);
   };
 
   // The two roles run loops of their own (the branch is uniform per wave),
-  // with the same four barriers per chunk.
+  // with the same three barriers per chunk.
   if (x_wave) {
     if (nchunks > 0) {
       GDN_LOAD_ROWS(fk, k_src0, 0);
@@ -818,7 +819,7 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
       f32x4 X[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int ks = 0; ks < kHeadDim / 32; ++ks)
-        Op<P>::mma2(X[0], X[1], fk[ks], lds_frag<P>(Stb, ks), lds_frag<P>(Stb, 4 + ks));
+        Op<P>::mma2(X[0], X[1], fk[ks], lds_frag<P>(Stb[ci & 1], ks), lds_frag<P>(Stb[ci & 1], 4 + ks));
 #pragma unroll
       for (int ks = 0; ks < kHeadDim / 32; ++ks) KtLds<P>::put(Ktb, rt, ks, fk[ks]);
       GDN_LOAD_ROWS(fk, k_src0, cn);
@@ -865,7 +866,7 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
       f32x4 Y[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int ks = 0; ks < kHeadDim / 32; ++ks)
-        Op<P>::mma2(Y[0], Y[1], fq[ks], lds_frag<P>(Stb, ks), lds_frag<P>(Stb, 4 + ks));
+        Op<P>::mma2(Y[0], Y[1], fq[ks], lds_frag<P>(Stb[ci & 1], ks), lds_frag<P>(Stb[ci & 1], 4 + ks));
       GDN_LOAD_ROWS(fq, q_src0, cn);
       block_sync_lds();                      // (the x-waves' R)
       // 2. O of the previous chunk = s (diag(Gam) Y + P D).
