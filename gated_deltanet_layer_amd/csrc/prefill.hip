@@ -585,6 +585,38 @@ __device__ __forceinline__ f32x4 conv_silu4(const Raw (&raw)[kConvK], const floa
   return y;
 }
 
+// c[t][d] += a[d] b[t][d] for column tiles t = 0, 1 and contraction steps
+// d = 0, 1, each (t, d) into an accumulator of its own. A dependent MFMA
+// accumulation waits about 50 cycles for the one before it, while a wave can
+// issue an independent MFMA about every 20: BF16X3 therefore issues one split
+// pass of all four products at a time, so that no product feeds any of the
+// next three.
+template <Prec P>
+__device__ __forceinline__ void mma_2x2(f32x4 (&c)[2][2], const typename Op<P>::Frag &a0,
+                                        const typename Op<P>::Frag &a1, const typename Op<P>::Frag &b00,
+                                        const typename Op<P>::Frag &b01, const typename Op<P>::Frag &b10,
+                                        const typename Op<P>::Frag &b11) {
+  if constexpr (P == Prec::BF16X3) {
+    c[0][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0.hi, b00.hi, c[0][0], 0, 0, 0);
+    c[1][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0.hi, b10.hi, c[1][0], 0, 0, 0);
+    c[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1.hi, b01.hi, c[0][1], 0, 0, 0);
+    c[1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1.hi, b11.hi, c[1][1], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);   // keep the passes in this order
+    c[0][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0.hi, b00.lo, c[0][0], 0, 0, 0);
+    c[1][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0.hi, b10.lo, c[1][0], 0, 0, 0);
+    c[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1.hi, b01.lo, c[0][1], 0, 0, 0);
+    c[1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1.hi, b11.lo, c[1][1], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    c[0][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0.lo, b00.hi, c[0][0], 0, 0, 0);
+    c[1][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0.lo, b10.hi, c[1][0], 0, 0, 0);
+    c[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1.lo, b01.hi, c[0][1], 0, 0, 0);
+    c[1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1.lo, b11.hi, c[1][1], 0, 0, 0);
+  } else {
+    Op<P>::mma2(c[0][0], c[1][0], a0, b00, b10);
+    Op<P>::mma2(c[0][1], c[1][1], a1, b01, b11);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // chunk_state: per (sequence, V-head, 32-column slab). 8 waves in two roles
 // of four, row tile rt = w % 4: waves 0-3 (x-waves) hold K and Tm rows,
@@ -626,8 +658,8 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = lane_id();
-  const int rt = wave & 3;
-  const bool x_wave = __builtin_amdgcn_readfirstlane(wave) < 4;   // uniform per wave
+  const int rt = __builtin_amdgcn_readfirstlane(wave) & 3;        // uniform per wave
+  const bool x_wave = __builtin_amdgcn_readfirstlane(wave) < 4;
   const int lr = 4 * (lane >> 4);    // accumulator row offset of this lane
   const int lc = lane & 15;          // accumulator column of this lane
   // Block order: workgroups are dealt to the 8 XCDs round-robin (block b on
@@ -772,16 +804,55 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
     }
   };
 
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  // out[t] = a S over rows 16 rt, column tile t: all eight S fragments are
+  // read first, then the products run as four accumulation chains.
+  auto times_s = [&](const Frag (&a)[kHeadDim / 32], const uint8_t *sbuf, f32x4 (&out)[2]) {
+    Frag b[2][kHeadDim / 32];
+#pragma unroll
+    for (int ks = 0; ks < kHeadDim / 32; ++ks) {
+      b[0][ks] = lds_frag<P>(sbuf, ks);
+      b[1][ks] = lds_frag<P>(sbuf, kHeadDim / 32 + ks);
+    }
+    __builtin_amdgcn_sched_barrier(0);       // every read in flight before the first product
+    f32x4 c[2][2] = {{zero4, zero4}, {zero4, zero4}};
+#pragma unroll
+    for (int ks = 0; ks < kHeadDim / 32; ks += 2)
+      mma_2x2<P>(c, a[ks], a[ks + 1], b[0][ks], b[0][ks + 1], b[1][ks], b[1][ks + 1]);
+    out[0] = c[0][0] + c[0][1];
+    out[1] = c[1][0] + c[1][1];
+  };
+  // out[t] += a B over rows 16 rt for a 64 x 32 right operand B in LDS (R or
+  // D); row tiles 0 and 1 of the lower-triangular a end before column 32.
+  auto times_mat = [&](const Frag (&a)[kChunk / 32], const uint8_t *buf, f32x4 (&out)[2]) {
+    const Frag b00 = lds_frag<P>(buf, 0), b10 = lds_frag<P>(buf, 2);
+    if (rt >= 2) {
+      const Frag b01 = lds_frag<P>(buf, 1), b11 = lds_frag<P>(buf, 3);
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 c[2][2] = {{out[0], zero4}, {out[1], zero4}};
+      mma_2x2<P>(c, a[0], a[1], b00, b01, b10, b11);
+      out[0] = c[0][0] + c[0][1];
+      out[1] = c[1][0] + c[1][1];
+    } else {
+      Op<P>::mma2(out[0], out[1], a[0], b00, b10);
+    }
+  };
+
   // 3. S <- Gam_n S + K^T (diag(k~) D), state rows 16 wave; then the
   // checkpoint (the state after token (ci + 1) * 64 of the sequence) and S
   // to the other S buffer, whose last readers (chunk ci - 1) are done.
   auto update_state = [&](int ci, float g_end) {
     block_sync_lds();                        // D and diag(k~) D visible
-    S[0] = S[0] * g_end;
-    S[1] = S[1] * g_end;
-#pragma unroll
-    for (int ks = 0; ks < kChunk / 32; ++ks)
-      Op<P>::mma2(S[0], S[1], KtLds<P>::get(Ktb, wave, ks), lds_frag<P>(Dsb, ks), lds_frag<P>(Dsb, 2 + ks));
+    {
+      const Frag k0 = KtLds<P>::get(Ktb, wave, 0), k1 = KtLds<P>::get(Ktb, wave, 1);
+      const Frag d00 = lds_frag<P>(Dsb, 0), d01 = lds_frag<P>(Dsb, 1);
+      const Frag d10 = lds_frag<P>(Dsb, 2), d11 = lds_frag<P>(Dsb, 3);
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 c[2][2] = {{S[0] * g_end, zero4}, {S[1] * g_end, zero4}};
+      mma_2x2<P>(c, k0, k1, d00, d01, d10, d11);
+      S[0] = c[0][0] + c[0][1];
+      S[1] = c[1][0] + c[1][1];
+    }
     if constexpr (kCkpt) {
       if ((ci + 1) % p.ckpt_chunks == 0 && (ci + 1) * kChunk <= L) {
         const int c = (ci + 1) / p.ckpt_chunks - 1;
@@ -816,10 +887,8 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
       const float g_end = G_s[kChunk - 1];
       GDN_LOAD_VG(cn);
       // 1. X = K S, rows 16 rt, both column tiles; R = V - diag(Gam) X.
-      f32x4 X[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-      for (int ks = 0; ks < kHeadDim / 32; ++ks)
-        Op<P>::mma2(X[0], X[1], fk[ks], lds_frag<P>(Stb[ci & 1], ks), lds_frag<P>(Stb[ci & 1], 4 + ks));
+      f32x4 X[2];
+      times_s(fk, Stb[ci & 1], X);
 #pragma unroll
       for (int ks = 0; ks < kHeadDim / 32; ++ks) KtLds<P>::put(Ktb, rt, ks, fk[ks]);
       GDN_LOAD_ROWS(fk, k_src0, cn);
@@ -835,11 +904,8 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
       }
       block_sync_lds();                      // R visible
       // 2. D = Tm R, rows 16 rt -> D and diag(k~) D in LDS.
-      f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-      for (int ks = 0; ks < kChunk / 32; ++ks)
-        if (ks == 0 || rt >= 2)
-          Op<P>::mma2(acc[0], acc[1], ft[ks], lds_frag<P>(Rtb, ks), lds_frag<P>(Rtb, 2 + ks));
+      f32x4 acc[2] = {zero4, zero4};
+      times_mat(ft, Rtb, acc);
       GDN_LOAD_MAT(ft, t_src0, cn);
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
@@ -863,20 +929,14 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
       block_sync_lds();                      // S, V, gam of chunk ci visible
       const float g_end = G_s[kChunk - 1];
       // 1. Y = Q S, rows 16 rt, both column tiles.
-      f32x4 Y[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-      for (int ks = 0; ks < kHeadDim / 32; ++ks)
-        Op<P>::mma2(Y[0], Y[1], fq[ks], lds_frag<P>(Stb[ci & 1], ks), lds_frag<P>(Stb[ci & 1], 4 + ks));
+      f32x4 Y[2];
+      times_s(fq, Stb[ci & 1], Y);
       GDN_LOAD_ROWS(fq, q_src0, cn);
       block_sync_lds();                      // (the x-waves' R)
       // 2. O of the previous chunk = s (diag(Gam) Y + P D).
       if (ci > 0) {
         f32x4 acc[2] = {oy[0], oy[1]};
-#pragma unroll
-        for (int ks = 0; ks < kChunk / 32; ++ks)
-          if (ks == 0 || rt >= 2)
-            Op<P>::mma2(acc[0], acc[1], fp[ks], lds_frag<P>(Dtb[(ci - 1) & 1], ks),
-                        lds_frag<P>(Dtb[(ci - 1) & 1], 2 + ks));
+        times_mat(fp, Dtb[(ci - 1) & 1], acc);
         GDN_LOAD_MAT(fp, p_src0, ci);
         store_o(ci - 1, acc);
       }
@@ -890,10 +950,7 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
     if (nchunks > 0) {
       const int cl = nchunks - 1;
       f32x4 acc[2] = {oy[0], oy[1]};
-#pragma unroll
-      for (int ks = 0; ks < kChunk / 32; ++ks)
-        if (ks == 0 || rt >= 2)
-          Op<P>::mma2(acc[0], acc[1], fp[ks], lds_frag<P>(Dtb[cl & 1], ks), lds_frag<P>(Dtb[cl & 1], 2 + ks));
+      times_mat(fp, Dtb[cl & 1], acc);
       store_o(cl, acc);
     }
   }
