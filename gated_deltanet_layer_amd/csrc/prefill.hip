@@ -218,22 +218,58 @@ __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(PrefillParam
   uint8_t *wk = ws.qk + (static_cast<size_t>(cid) * p.n_qk + h) * kQkBytes;   // K rows, Q rows
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
+  // Every global load of the block (K and Q rows, the gate inputs of the
+  // first round of V-heads) is issued before its first workspace store:
+  // once stores and loads are both in flight, the compiler's memory waits
+  // also wait for the stores to complete.
+  const int nvh = p.n_v / p.n_qk;
+  // Gates of V-head h + u Hqk for row lane of the chunk (rows past len repeat
+  // the last row and are masked where used), as the prep kernel forms them:
+  // the raw inputs are loaded by load_gates and turned into (g, beta) by
+  // form_gates at first use, so that the loads stay in flight meanwhile.
+  using RawGate = std::conditional_t<kFused && std::is_same<TA, bf16_t>::value, uint16_t, float>;
+  auto load_gates = [&](int u, RawGate &gr, RawGate &br) {
+    const int j = h + u * p.n_qk;
+    const size_t e = static_cast<size_t>(t0 + min(lane, len - 1)) * p.n_v + j;
+    if constexpr (kFused) {
+      br = static_cast<const RawGate *>(p.bl)[e];
+      gr = static_cast<const RawGate *>(p.al)[e];
+    } else {
+      br = p.beta[e];
+      gr = p.g[e];
+    }
+  };
+  auto form_gates = [&](int u, RawGate gr, RawGate br, float &gv, float &bv) {
+    if constexpr (kFused) {
+      const int j = h + u * p.n_qk;
+      float b_logit, a_logit;
+      if constexpr (std::is_same<RawGate, uint16_t>::value) {
+        b_logit = __uint_as_float(static_cast<uint32_t>(br) << 16);
+        a_logit = __uint_as_float(static_cast<uint32_t>(gr) << 16);
+      } else {
+        b_logit = br;
+        a_logit = gr;
+      }
+      bv = sigmoidf_(b_logit);
+      gv = -expf(p.A_log[j]) * softplusf_(a_logit + p.dt_bias[j]);
+    } else {
+      bv = br;
+      gv = gr;
+    }
+  };
+  RawGate g_first{}, b_first{};   // wave w < min(nvh, kSolveWaves): V-head h + w Hqk
+
   // Q rows of this wave's row tile as A fragments (rows >= len are zero);
   // they are also the Q operand blocks (wave, ks) of the workspace.
   const int rt = wave;
   const int qrow = 16 * rt + (lane & 15);
   Frag fq[kHeadDim / 32];
   if constexpr (kFused) {
-    // q and k of row qrow from the raw rows; k goes to LDS (blocked operand
+    // k and q of row qrow from the raw rows; k goes to LDS (blocked operand
     // rows, as below), q stays in this lane's A-fragment slots.
+    if (wave < min(nvh, kSolveWaves)) load_gates(wave, g_first, b_first);
     const bool valid = qrow < len;
     f32x4 ya[kHeadDim / 32], yb[kHeadDim / 32];
-    qk_row<TA>(p, n, seq0, L, ci * kChunk + qrow, valid, 0, h, ya, yb);
-#pragma unroll
-    for (int ks = 0; ks < kHeadDim / 32; ++ks) {
-      fq[ks] = make_frag<P>(ya[ks], yb[ks]);
-      FragIO<P>::store(wk + kKBytes, kHeadDim / 32, rt, ks, fq[ks]);
-    }
     qk_row<TA>(p, n, seq0, L, ci * kChunk + qrow, valid, 1, h, ya, yb);
 #pragma unroll
     for (int ks = 0; ks < kHeadDim / 32; ++ks) {
@@ -241,22 +277,11 @@ __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(PrefillParam
       Op<P>::put4(Kb + qrow * kPitch128, c, ya[ks]);
       Op<P>::put4(Kb + qrow * kPitch128, c + 4, yb[ks]);
     }
+    qk_row<TA>(p, n, seq0, L, ci * kChunk + qrow, valid, 0, h, ya, yb);
+#pragma unroll
+    for (int ks = 0; ks < kHeadDim / 32; ++ks) fq[ks] = make_frag<P>(ya[ks], yb[ks]);
   } else {
-    const float *qp = qg + min(qrow, len - 1) * qk_stride + 8 * (lane >> 4);
-    f32x4 qa[kHeadDim / 32], qb[kHeadDim / 32];
-#pragma unroll
-    for (int ks = 0; ks < kHeadDim / 32; ++ks) {
-      qa[ks] = *reinterpret_cast<const f32x4 *>(qp + 32 * ks);
-      qb[ks] = *reinterpret_cast<const f32x4 *>(qp + 32 * ks + 4);
-    }
-    const bool qvalid = qrow < len;
-#pragma unroll
-    for (int ks = 0; ks < kHeadDim / 32; ++ks) {
-      fq[ks] = make_frag<P>(qvalid ? qa[ks] : zero4, qvalid ? qb[ks] : zero4);
-      FragIO<P>::store(wk + kKBytes, kHeadDim / 32, rt, ks, fq[ks]);
-    }
-  }
-  if constexpr (!kFused) {  // K rows -> blocked operand rows in LDS; rows >= len are zero.
+    // K rows -> blocked operand rows in LDS; rows >= len are zero.
     constexpr int kPer = kChunk * (kHeadDim / 4) / kLocalThreads;
     f32x4 kb4[kPer];
 #pragma unroll
@@ -264,12 +289,30 @@ __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(PrefillParam
       const int idx = tid + u * kLocalThreads, r = idx / (kHeadDim / 4), c4 = idx % (kHeadDim / 4);
       kb4[u] = *reinterpret_cast<const f32x4 *>(kg + min(r, len - 1) * qk_stride + 4 * c4);
     }
+    const float *qp = qg + min(qrow, len - 1) * qk_stride + 8 * (lane >> 4);
+    f32x4 qa[kHeadDim / 32], qb[kHeadDim / 32];
+#pragma unroll
+    for (int ks = 0; ks < kHeadDim / 32; ++ks) {
+      qa[ks] = *reinterpret_cast<const f32x4 *>(qp + 32 * ks);
+      qb[ks] = *reinterpret_cast<const f32x4 *>(qp + 32 * ks + 4);
+    }
+    if (wave < min(nvh, kSolveWaves)) load_gates(wave, g_first, b_first);
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int idx = tid + u * kLocalThreads, r = idx / (kHeadDim / 4), c4 = idx % (kHeadDim / 4);
       Op<P>::put4(Kb + r * kPitch128, 4 * c4, r < len ? kb4[u] : zero4);
     }
+    const bool qvalid = qrow < len;
+#pragma unroll
+    for (int ks = 0; ks < kHeadDim / 32; ++ks)
+      fq[ks] = make_frag<P>(qvalid ? qa[ks] : zero4, qvalid ? qb[ks] : zero4);
   }
+  // The first round's gates are formed before the first store (a wait for
+  // their loads after it would also wait for the stores).
+  float g_first_v = 0.f, b_first_v = 0.f;
+  if (wave < min(nvh, kSolveWaves)) form_gates(wave, g_first, b_first, g_first_v, b_first_v);
+#pragma unroll
+  for (int ks = 0; ks < kHeadDim / 32; ++ks) FragIO<P>::store(wk + kKBytes, kHeadDim / 32, rt, ks, fq[ks]);
   block_sync_lds();
 
   // K rows (4 x 4 blocks) to the workspace, read out of LDS a whole
@@ -298,12 +341,13 @@ __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(PrefillParam
   block_sync_lds();   // K is dead from here: buf becomes the solving waves' matrices
 
   // The 16 x 32 blocks (rt, ks) of a 64 x 64 lower-triangular operand that
-  // are not all zero (blocks (0, 1) and (1, 1) are).
+  // are not all zero (blocks (0, 1) and (1, 1) are): block bl = 0 .. 5 is
+  // (0, 0), (1, 0), (2, 0), (2, 1), (3, 0), (3, 1), formed arithmetically (an
+  // indexed table would be read from global memory).
   constexpr int kLowBlocks = 6;
-  const int low_rt[kLowBlocks] = {0, 1, 2, 2, 3, 3};
-  const int low_ks[kLowBlocks] = {0, 0, 0, 1, 0, 1};
+  auto low_rt = [](int bl) { return bl < 2 ? bl : 2 + ((bl - 2) >> 1); };
+  auto low_ks = [](int bl) { return bl < 2 ? 0 : (bl & 1); };
 
-  const int nvh = p.n_v / p.n_qk;
   for (int u0 = 0; u0 < nvh; u0 += kSolveWaves) {
     const int nu = min(kSolveWaves, nvh - u0);   // V-heads of this round, slot s = head u0 + s
     if (u0 > 0) block_sync_lds();                // the previous round's readers are done
@@ -313,15 +357,11 @@ __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(PrefillParam
     // ~|gam| * 6e-8 to cancellation, so the scan and the differences are fp64.
     if (wave < nu) {
       const int j = h + (u0 + wave) * p.n_qk;
-      const size_t e = static_cast<size_t>(t0 + min(lane, len - 1)) * p.n_v + j;
-      float gv, bv;
-      if constexpr (kFused) {   // the gates, as the prep kernel forms them
-        const TA *bl = static_cast<const TA *>(p.bl), *al = static_cast<const TA *>(p.al);
-        bv = sigmoidf_(Act<TA>::load(bl, e));
-        gv = -expf(p.A_log[j]) * softplusf_(Act<TA>::load(al, e) + p.dt_bias[j]);
-      } else {
-        bv = p.beta[e];
-        gv = p.g[e];
+      float gv = g_first_v, bv = b_first_v;
+      if (u0 > 0) {
+        RawGate graw, braw;
+        load_gates(u0 + wave, graw, braw);
+        form_gates(u0 + wave, graw, braw, gv, bv);
       }
       const double gr = lane < len ? static_cast<double>(gv) : 0.0;
       const float br = lane < len ? bv : 0.f;
@@ -337,23 +377,32 @@ __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(PrefillParam
     // 32 ks + 8 (l / 16) + 0..7 of the block.
     for (int item = wave; item < nu * kLowBlocks; item += kLocalThreads / kWave) {
       const int s = item / kLowBlocks, bl = item % kLowBlocks;
-      const int brt = low_rt[bl], bks = low_ks[bl];
+      const int brt = low_rt(bl), bks = low_ks(bl);
       const int j = h + (u0 + s) * p.n_qk;
       float *Lx = reinterpret_cast<float *>(buf) + s * kChunk * kLdS;
       const double *gam = gam_s[s];
       const int r = 16 * brt + (lane & 15), m0 = 32 * bks + 8 * (lane >> 4);
       const double gr = gam[r];
       const float br = bet_s[s][r];
+      // Every operand of the lane's 8 entries is read first, above the
+      // diagonal too (in-bounds values that are then discarded), so that the
+      // reads overlap. gam_r - gam_m <= 0 for m <= r; the clamp only keeps the
+      // discarded entries finite.
+      double gm[8];
+      float qk[8], kk[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        gm[e] = gam[m0 + e];
+        qk[e] = Gq[tri(r, m0 + e)];
+        kk[e] = Gk[tri(r, m0 + e)];
+      }
       f32x4 pa, pb;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int m = m0 + e;
-        float pv = 0.f, lv = m == r ? 1.f : 0.f;
-        if (m <= r) {
-          const float dec = expf(static_cast<float>(gr - gam[m]));
-          pv = dec * Gq[tri(r, m)];
-          if (m < r) lv = br * dec * Gk[tri(r, m)];
-        }
+        const float dec = expf(fminf(static_cast<float>(gr - gm[e]), 0.f));
+        const float pv = m <= r ? dec * qk[e] : 0.f;
+        const float lv = m < r ? br * dec * kk[e] : (m == r ? 1.f : 0.f);
         Lx[r * kLdS + m] = lv;
         if (e < 4) pa[e] = pv; else pb[e - 4] = pv;
       }
@@ -421,16 +470,21 @@ __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(PrefillParam
     // per step over all waves.
     for (int item = wave; item < nu * kLowBlocks; item += kLocalThreads / kWave) {
       const int s = item / kLowBlocks, bl = item % kLowBlocks;
-      const int brt = low_rt[bl], bks = low_ks[bl];
+      const int brt = low_rt(bl), bks = low_ks(bl);
       const int j = h + (u0 + s) * p.n_qk;
       const float *Lx = reinterpret_cast<const float *>(buf) + s * kChunk * kLdS;
       const float *bet = bet_s[s];
       const int r = 16 * brt + (lane & 15), m0 = 32 * bks + 8 * (lane >> 4);
+      float xv[8], bv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {   // read first (in bounds above the diagonal too), then select
+        xv[e] = Lx[r * kLdS + m0 + e];
+        bv[e] = bet[m0 + e];
+      }
       f32x4 ta, tb;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int m = m0 + e;
-        const float tv = m <= r ? Lx[r * kLdS + m] * bet[m] : 0.f;
+        const float tv = m0 + e <= r ? xv[e] * bv[e] : 0.f;
         if (e < 4) ta[e] = tv; else tb[e - 4] = tv;
       }
       uint8_t *wv = ws.v + (static_cast<size_t>(cid) * p.n_v + j) * kVBytes;
