@@ -814,12 +814,10 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
       pg_end = gm[kChunk - 1];                                                                       \
     }                                                                                                \
   } while (0)
-  // Rows past the chunk's length were loaded from its last row and are zeroed
-  // here, at first use, so that the loads stay in flight until then.
-#define GDN_COMMIT_VG(c)                                                                             \
+  // Fused form: conv + SiLU of the loaded raw rows, formed while the x-waves
+  // wait for the y-waves at the chunk's last barrier (it is off the chain).
+#define GDN_FORM_V()                                                                                 \
   do {                                                                                               \
-    const int len_ = min(kChunk, L - (c) * kChunk);                                                  \
-    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};                                                        \
     if constexpr (kFused) {                                                                          \
       _Pragma("unroll") for (int h_ = 0; h_ < 2; ++h_) {                                             \
         const Raw raw_[kConvK] = {vraw[0][h_], vraw[1][h_], vraw[2][h_], vraw[3][h_]};               \
@@ -828,6 +826,13 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
         pv[h_] = conv_silu4(raw_, w_);                                                               \
       }                                                                                              \
     }                                                                                                \
+  } while (0)
+  // Rows past the chunk's length were loaded from its last row and are zeroed
+  // here, at first use, so that the loads stay in flight until then.
+#define GDN_COMMIT_VG(c)                                                                             \
+  do {                                                                                               \
+    const int len_ = min(kChunk, L - (c) * kChunk);                                                  \
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};                                                        \
     float *dst_ = Vs + v_row * kLdV + 8 * v_c8;                                                      \
     *reinterpret_cast<f32x4 *>(dst_) = v_row < len_ ? pv[0] : zero4;                                 \
     *reinterpret_cast<f32x4 *>(dst_ + 4) = v_row < len_ ? pv[1] : zero4;                             \
@@ -931,6 +936,7 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
       GDN_LOAD_ROWS(fk, k_src0, 0);
       GDN_LOAD_MAT(ft, t_src0, 0);
       GDN_LOAD_VG(0);
+      GDN_FORM_V();
       GDN_COMMIT_VG(0);
     }
     for (int ci = 0; ci < nchunks; ++ci) {
@@ -969,6 +975,7 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
         for (int r = 0; r < 4; ++r) ds[r] = acc[ct][r] * ksc_s[16 * rt + acc_row(r)];
         lds_put4<P>(Dsb, 2, 16 * rt + lr, 16 * ct + lc, ds);
       }
+      GDN_FORM_V();
       update_state(ci, g_end);
       GDN_COMMIT_VG(cn);
     }
@@ -1011,6 +1018,7 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
 #undef GDN_LOAD_ROWS
 #undef GDN_LOAD_MAT
 #undef GDN_LOAD_VG
+#undef GDN_FORM_V
 #undef GDN_COMMIT_VG
 
 #pragma unroll
