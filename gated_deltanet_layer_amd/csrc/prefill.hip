@@ -706,6 +706,9 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
   __shared__ __attribute__((aligned(16))) float Os[4 * 16 * kLdOs];     // O staging, 16 rows per y-wave
   __shared__ __attribute__((aligned(16))) uint8_t Ktb[KtLds<P>::kBytes];   // K rows of the chunk
   __shared__ float4 Vw[kFused ? kSlab : 1];  // conv taps of the slab's V channels
+  // Fused form: raw V rows of the slab by chunk parity; rows 0 .. 2 are the
+  // three rows before the chunk, rows 3 .. 66 the chunk's own.
+  __shared__ __attribute__((aligned(16))) TA Vr[kFused ? 2 : 1][kFused ? kChunk + kConvK - 1 : 1][kSlab];
   __shared__ float G_s[kChunk];              // exp(gam_r)
   __shared__ float ksc_s[kChunk];            // exp(gam_n - gam_r)
 
@@ -767,15 +770,41 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
 
   Frag fk[kHeadDim / 32], fq[kHeadDim / 32], ft[kChunk / 32], fp[kChunk / 32];
   f32x4 pv[2];
-  // Fused form: the raw rows t - 3 .. t of this thread's 8 V channels are
-  // loaded with the other operands of the next chunk and turned into
-  // conv + SiLU when committed to LDS.
+  // Fused form: the raw row of this thread's 8 V channels is loaded once per
+  // chunk (16 bytes for bf16, 32 for fp32), with the other operands of the
+  // next chunk, and staged in Vr, where every thread reads the four rows its
+  // conv needs.
   using Raw = typename RawAct<TA>::type;
-  Raw vraw[kConvK][2];
+  constexpr int kRawQ = static_cast<int>(sizeof(TA)) / 2;   // 16-byte pieces per 8 channels
+  uint4 vr[kRawQ];
   const int Cq = kHeadDim * (2 * p.n_qk + p.n_v);
   const int vch0 = 2 * p.n_qk * kHeadDim + j * kHeadDim + col_base;   // first slab channel in qkv
+  constexpr int kHalo = kConvK - 1;
   if constexpr (kFused) {
     if (tid < kSlab) Vw[tid] = reinterpret_cast<const float4 *>(p.conv_w)[vch0 + tid];
+    // Chunk 0's raw rows and the conv state before it; rows 61 .. 63 also
+    // seed the next chunk's first three rows.
+    if (nchunks > 0 && x_wave) {
+      const int row = min(v_row, min(kChunk, L) - 1);
+      const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const TA *>(p.qkv) +
+                                                         static_cast<size_t>(seq0 + row) * Cq + vch0 + 8 * v_c8);
+      uint4 *dst = reinterpret_cast<uint4 *>(&Vr[0][kHalo + v_row][8 * v_c8]);
+#pragma unroll
+      for (int q = 0; q < kRawQ; ++q) dst[q] = src[q];
+      if (v_row >= kChunk - kHalo) {
+        uint4 *dn = reinterpret_cast<uint4 *>(&Vr[1][v_row - (kChunk - kHalo)][8 * v_c8]);
+#pragma unroll
+        for (int q = 0; q < kRawQ; ++q) dn[q] = src[q];
+      }
+      if (tid < kHalo * 4) {
+        const int hr = tid >> 2, hc = tid & 3;
+        const uint4 *hs = reinterpret_cast<const uint4 *>(static_cast<const TA *>(p.st_in) +
+                                                          (static_cast<size_t>(n) * kHalo + hr) * Cq + vch0 + 8 * hc);
+        uint4 *hd = reinterpret_cast<uint4 *>(&Vr[0][hr][8 * hc]);
+#pragma unroll
+        for (int q = 0; q < kRawQ; ++q) hd[q] = hs[q];
+      }
+    }
     block_sync_lds();
   }
   double pg = 0.0, pg_end = 0.0;
@@ -794,15 +823,10 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
   do {                                                                                               \
     const int t0_ = seq0 + (c) * kChunk, len_ = min(kChunk, L - (c) * kChunk);                       \
     if constexpr (kFused) {                                                                          \
-      const int tl_ = (c) * kChunk + min(v_row, len_ - 1);                                           \
-      _Pragma("unroll") for (int r_ = 0; r_ < kConvK; ++r_) {                                        \
-        const int pos_ = tl_ - (kConvK - 1) + r_;                                                    \
-        const TA *src_ = pos_ < 0 ? static_cast<const TA *>(p.st_in) +                               \
-                                        (static_cast<size_t>(n) * (kConvK - 1) + (pos_ + kConvK - 1)) * Cq \
-                                  : static_cast<const TA *>(p.qkv) + static_cast<size_t>(seq0 + pos_) * Cq; \
-        vraw[r_][0] = *reinterpret_cast<const Raw *>(src_ + vch0 + 8 * v_c8);                        \
-        vraw[r_][1] = *reinterpret_cast<const Raw *>(src_ + vch0 + 8 * v_c8 + 4);                    \
-      }                                                                                              \
+      const uint4 *src_ = reinterpret_cast<const uint4 *>(static_cast<const TA *>(p.qkv) +           \
+                                                          static_cast<size_t>(t0_ + min(v_row, len_ - 1)) * Cq + \
+                                                          vch0 + 8 * v_c8);                          \
+      _Pragma("unroll") for (int q_ = 0; q_ < kRawQ; ++q_) vr[q_] = src_[q_];                        \
     } else {                                                                                         \
       const float *src_ = p.v + (t0_ + min(v_row, len_ - 1)) * v_stride + j * kHeadDim + col_base + 8 * v_c8; \
       pv[0] = *reinterpret_cast<const f32x4 *>(src_);                                                \
@@ -814,28 +838,49 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
       pg_end = gm[kChunk - 1];                                                                       \
     }                                                                                                \
   } while (0)
-  // Fused form: conv + SiLU of the loaded raw rows, formed while the x-waves
-  // wait for the y-waves at the chunk's last barrier (it is off the chain).
-#define GDN_FORM_V()                                                                                 \
+  // Fused form: the raw row of chunk c to Vr (rows 61 .. 63 also to the
+  // other buffer, as the first rows of chunk c + 1); visible after the next
+  // barrier.
+#define GDN_STAGE_V(c)                                                                               \
+  do {                                                                                               \
+    if constexpr (kFused) {                                                                          \
+      uint4 *dst_ = reinterpret_cast<uint4 *>(&Vr[(c) & 1][kHalo + v_row][8 * v_c8]);                \
+      _Pragma("unroll") for (int q_ = 0; q_ < kRawQ; ++q_) dst_[q_] = vr[q_];                        \
+      if (v_row >= kChunk - kHalo) {                                                                 \
+        uint4 *dn_ = reinterpret_cast<uint4 *>(&Vr[((c) + 1) & 1][v_row - (kChunk - kHalo)][8 * v_c8]); \
+        _Pragma("unroll") for (int q_ = 0; q_ < kRawQ; ++q_) dn_[q_] = vr[q_];                       \
+      }                                                                                              \
+    }                                                                                                \
+  } while (0)
+  // V rows of chunk c to LDS: the fused form first takes conv + SiLU of the
+  // staged raw rows (rows t - 3 .. t of row t sit at Vr rows t .. t + 3).
+  // Formed after the chunk's second barrier, while the x-waves wait for the
+  // y-waves at its third (it is off the chain): the previous chunk's V has
+  // been read by then. Rows past the chunk's length were loaded from its last
+  // row and are zeroed here, at first use, so that the loads stay in flight
+  // until then.
+#define GDN_FORM_V(c)                                                                                \
   do {                                                                                               \
     if constexpr (kFused) {                                                                          \
       _Pragma("unroll") for (int h_ = 0; h_ < 2; ++h_) {                                             \
-        const Raw raw_[kConvK] = {vraw[0][h_], vraw[1][h_], vraw[2][h_], vraw[3][h_]};               \
+        Raw raw_[kConvK];                                                                            \
+        _Pragma("unroll") for (int k_ = 0; k_ < kConvK; ++k_)                                        \
+          raw_[k_] = *reinterpret_cast<const Raw *>(&Vr[(c) & 1][v_row + k_][8 * v_c8 + 4 * h_]);     \
         const float4 w_[4] = {Vw[8 * v_c8 + 4 * h_], Vw[8 * v_c8 + 4 * h_ + 1], Vw[8 * v_c8 + 4 * h_ + 2], \
                               Vw[8 * v_c8 + 4 * h_ + 3]};                                            \
         pv[h_] = conv_silu4(raw_, w_);                                                               \
       }                                                                                              \
     }                                                                                                \
-  } while (0)
-  // Rows past the chunk's length were loaded from its last row and are zeroed
-  // here, at first use, so that the loads stay in flight until then.
-#define GDN_COMMIT_VG(c)                                                                             \
-  do {                                                                                               \
-    const int len_ = min(kChunk, L - (c) * kChunk);                                                  \
-    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};                                                        \
+    const int lenv_ = min(kChunk, L - (c) * kChunk);                                                 \
+    const f32x4 zv_ = {0.f, 0.f, 0.f, 0.f};                                                          \
     float *dst_ = Vs + v_row * kLdV + 8 * v_c8;                                                      \
-    *reinterpret_cast<f32x4 *>(dst_) = v_row < len_ ? pv[0] : zero4;                                 \
-    *reinterpret_cast<f32x4 *>(dst_ + 4) = v_row < len_ ? pv[1] : zero4;                             \
+    *reinterpret_cast<f32x4 *>(dst_) = v_row < lenv_ ? pv[0] : zv_;                                  \
+    *reinterpret_cast<f32x4 *>(dst_ + 4) = v_row < lenv_ ? pv[1] : zv_;                              \
+  } while (0)
+  // gam of chunk c to LDS (after the chunk's last barrier: the y-waves read
+  // the previous chunk's decays up to it).
+#define GDN_COMMIT_G()                                                                               \
+  do {                                                                                               \
     if (tid < kChunk) {                                                                              \
       G_s[tid] = expf(static_cast<float>(pg));                                                       \
       ksc_s[tid] = expf(static_cast<float>(pg_end - pg));                                            \
@@ -936,8 +981,8 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
       GDN_LOAD_ROWS(fk, k_src0, 0);
       GDN_LOAD_MAT(ft, t_src0, 0);
       GDN_LOAD_VG(0);
-      GDN_FORM_V();
-      GDN_COMMIT_VG(0);
+      GDN_FORM_V(0);
+      GDN_COMMIT_G();
     }
     for (int ci = 0; ci < nchunks; ++ci) {
       // Operands of the next chunk (the last chunk reloads itself, so every
@@ -962,7 +1007,8 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
         }
         lds_put4<P>(Rtb, 2, 16 * rt + lr, 16 * ct + lc, rv);
       }
-      block_sync_lds();                      // R visible
+      GDN_STAGE_V(cn);
+      block_sync_lds();                      // R (and the raw V rows) visible
       // 2. D = Tm R, rows 16 rt -> D and diag(k~) D in LDS.
       f32x4 acc[2] = {zero4, zero4};
       times_mat(ft, Rtb, acc);
@@ -975,9 +1021,9 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
         for (int r = 0; r < 4; ++r) ds[r] = acc[ct][r] * ksc_s[16 * rt + acc_row(r)];
         lds_put4<P>(Dsb, 2, 16 * rt + lr, 16 * ct + lc, ds);
       }
-      GDN_FORM_V();
+      GDN_FORM_V(cn);
       update_state(ci, g_end);
-      GDN_COMMIT_VG(cn);
+      GDN_COMMIT_G();
     }
   } else {
     f32x4 oy[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};   // diag(Gam) Y of the previous chunk
@@ -1018,8 +1064,9 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
 #undef GDN_LOAD_ROWS
 #undef GDN_LOAD_MAT
 #undef GDN_LOAD_VG
+#undef GDN_STAGE_V
 #undef GDN_FORM_V
-#undef GDN_COMMIT_VG
+#undef GDN_COMMIT_G
 
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct)
