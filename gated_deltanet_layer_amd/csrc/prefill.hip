@@ -626,6 +626,12 @@ template <> struct RawAct<bf16_t> {
   }
 };
 
+// SiLU with the hardware reciprocal and exp (a few ulp of fp32, far inside
+// what the bf16 activations carry); for large |x| it tends to x or to -0.
+__device__ __forceinline__ float silu_fast(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
+
 template <typename Raw>
 __device__ __forceinline__ f32x4 conv_silu4(const Raw (&raw)[kConvK], const float4 (&w)[4]) {
   using TA = std::conditional_t<std::is_same<Raw, float4>::value, float, bf16_t>;
@@ -635,7 +641,7 @@ __device__ __forceinline__ f32x4 conv_silu4(const Raw (&raw)[kConvK], const floa
   f32x4 y;
 #pragma unroll
   for (int e = 0; e < 4; ++e)
-    y[e] = siluf_(w[e].x * (&x[0].x)[e] + w[e].y * (&x[1].x)[e] + w[e].z * (&x[2].x)[e] + w[e].w * (&x[3].x)[e]);
+    y[e] = silu_fast(w[e].x * (&x[0].x)[e] + w[e].y * (&x[1].x)[e] + w[e].z * (&x[2].x)[e] + w[e].w * (&x[3].x)[e]);
   return y;
 }
 
@@ -680,8 +686,14 @@ __device__ __forceinline__ void mma_2x2(f32x4 (&c)[2][2], const typename Op<P>::
 //         k~_r = exp(gam_n - gam_r)
 //      y: O of chunk c - 1 = s (diag(Gam) Y + P D), from that chunk's D
 //   3. all: S <- Gam_n S + K^T diag(k~) D (state rows 16 w) -> S in LDS
+// V of chunk c + 1 goes to LDS in step 2 (it is first read in step 1 of that
+// chunk). The fused form stages each raw V row of the slab in LDS once and
+// takes conv + SiLU from there, half of every thread's channels on each
+// role, in the time the roles would otherwise wait at the third barrier.
 // S lives in two LDS buffers by chunk parity, so that writing the new S
-// needs no barrier of its own: three barriers per chunk.
+// needs no barrier of its own: three barriers per chunk; the two roles run
+// loops of their own (the branch is uniform per wave) with the same
+// barriers.
 // O trails D by one chunk, so it is formed while the x-waves form D, off the
 // chain S -> X -> D -> S that orders the chunks; the last chunk's O follows
 // the loop.
@@ -852,25 +864,29 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
       }                                                                                              \
     }                                                                                                \
   } while (0)
-  // V rows of chunk c to LDS: the fused form first takes conv + SiLU of the
-  // staged raw rows (rows t - 3 .. t of row t sit at Vr rows t .. t + 3).
-  // Formed after the chunk's second barrier, while the x-waves wait for the
-  // y-waves at its third (it is off the chain): the previous chunk's V has
-  // been read by then. Rows past the chunk's length were loaded from its last
-  // row and are zeroed here, at first use, so that the loads stay in flight
-  // until then.
-#define GDN_FORM_V(c)                                                                                \
+  // V rows of chunk c to LDS, formed after the chunk's second barrier (the
+  // previous chunk's V has been read by then) and before its third, while
+  // the waves would otherwise wait (it is off the chain). Rows past the
+  // chunk's length were loaded from its last row and are zeroed here, at
+  // first use, so that the loads stay in flight until then.
+  // Fused form: conv + SiLU of the staged raw rows (rows t - 3 .. t of row t
+  // sit at Vr rows t .. t + 3) of the thread's channels 8 (tid % 4) + 4 h
+  // .. +3: h = 0 on the x-waves, 1 on the y-waves, which share the work.
+#define GDN_FORM_V(c, h)                                                                             \
   do {                                                                                               \
-    if constexpr (kFused) {                                                                          \
-      _Pragma("unroll") for (int h_ = 0; h_ < 2; ++h_) {                                             \
-        Raw raw_[kConvK];                                                                            \
-        _Pragma("unroll") for (int k_ = 0; k_ < kConvK; ++k_)                                        \
-          raw_[k_] = *reinterpret_cast<const Raw *>(&Vr[(c) & 1][v_row + k_][8 * v_c8 + 4 * h_]);     \
-        const float4 w_[4] = {Vw[8 * v_c8 + 4 * h_], Vw[8 * v_c8 + 4 * h_ + 1], Vw[8 * v_c8 + 4 * h_ + 2], \
-                              Vw[8 * v_c8 + 4 * h_ + 3]};                                            \
-        pv[h_] = conv_silu4(raw_, w_);                                                               \
-      }                                                                                              \
-    }                                                                                                \
+    Raw raw_[kConvK];                                                                                \
+    _Pragma("unroll") for (int k_ = 0; k_ < kConvK; ++k_)                                            \
+      raw_[k_] = *reinterpret_cast<const Raw *>(&Vr[(c) & 1][v_row + k_][8 * v_c8 + 4 * (h)]);        \
+    const float4 w_[4] = {Vw[8 * v_c8 + 4 * (h)], Vw[8 * v_c8 + 4 * (h) + 1], Vw[8 * v_c8 + 4 * (h) + 2], \
+                          Vw[8 * v_c8 + 4 * (h) + 3]};                                               \
+    const f32x4 y_ = conv_silu4(raw_, w_);                                                           \
+    const f32x4 zv_ = {0.f, 0.f, 0.f, 0.f};                                                          \
+    *reinterpret_cast<f32x4 *>(Vs + v_row * kLdV + 8 * v_c8 + 4 * (h)) =                             \
+        v_row < min(kChunk, L - (c) * kChunk) ? y_ : zv_;                                            \
+  } while (0)
+  // Unfused form: the loaded V rows (x-waves).
+#define GDN_WRITE_V(c)                                                                               \
+  do {                                                                                               \
     const int lenv_ = min(kChunk, L - (c) * kChunk);                                                 \
     const f32x4 zv_ = {0.f, 0.f, 0.f, 0.f};                                                          \
     float *dst_ = Vs + v_row * kLdV + 8 * v_c8;                                                      \
@@ -981,7 +997,8 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
       GDN_LOAD_ROWS(fk, k_src0, 0);
       GDN_LOAD_MAT(ft, t_src0, 0);
       GDN_LOAD_VG(0);
-      GDN_FORM_V(0);
+      if constexpr (kFused) GDN_FORM_V(0, 0);
+      else GDN_WRITE_V(0);
       GDN_COMMIT_G();
     }
     for (int ci = 0; ci < nchunks; ++ci) {
@@ -1021,7 +1038,8 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
         for (int r = 0; r < 4; ++r) ds[r] = acc[ct][r] * ksc_s[16 * rt + acc_row(r)];
         lds_put4<P>(Dsb, 2, 16 * rt + lr, 16 * ct + lc, ds);
       }
-      GDN_FORM_V(cn);
+      if constexpr (kFused) GDN_FORM_V(cn, 0);
+      else GDN_WRITE_V(cn);
       update_state(ci, g_end);
       GDN_COMMIT_G();
     }
@@ -1030,6 +1048,7 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
     if (nchunks > 0) {
       GDN_LOAD_ROWS(fq, q_src0, 0);
       GDN_LOAD_MAT(fp, p_src0, 0);
+      if constexpr (kFused) GDN_FORM_V(0, 1);
     }
     for (int ci = 0; ci < nchunks; ++ci) {
       const int cn = min(ci + 1, nchunks - 1);
@@ -1051,6 +1070,7 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
       for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
         for (int r = 0; r < 4; ++r) oy[ct][r] = G_s[16 * rt + acc_row(r)] * Y[ct][r];
+      if constexpr (kFused) GDN_FORM_V(cn, 1);
       update_state(ci, g_end);
     }
     // O of the last chunk (its D was made visible by the loop's barriers).
@@ -1066,6 +1086,7 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
 #undef GDN_LOAD_VG
 #undef GDN_STAGE_V
 #undef GDN_FORM_V
+#undef GDN_WRITE_V
 #undef GDN_COMMIT_G
 
 #pragma unroll
