@@ -121,6 +121,12 @@ template <> __device__ __forceinline__ Op<Prec::BF16X3>::Frag make_frag<Prec::BF
 // local token tl (0 <= tl < L) of sequence n, from rows tl - 3 .. tl of
 // [st_in[n]; qkv rows of the sequence] (the same arithmetic as the prep
 // kernel: tap 3 meets the current row).
+// SiLU with the hardware reciprocal and exp (a few ulp of fp32, far inside
+// what the bf16 activations carry); for large |x| it tends to x or to -0.
+__device__ __forceinline__ float silu_fast(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
+
 template <typename TA>
 __device__ __forceinline__ void conv_silu8(const PrefillParams &p, int n, int seq0, int C, int tl, int c0,
                                            f32x4 &ya, f32x4 &yb) {
@@ -144,7 +150,7 @@ __device__ __forceinline__ void conv_silu8(const PrefillParams &p, int n, int se
     const float x1 = e < 4 ? (&xa[1].x)[e] : (&xb[1].x)[e - 4];
     const float x2 = e < 4 ? (&xa[2].x)[e] : (&xb[2].x)[e - 4];
     const float x3 = e < 4 ? (&xa[3].x)[e] : (&xb[3].x)[e - 4];
-    y[e] = siluf_(we.x * x0 + we.y * x1 + we.z * x2 + we.w * x3);
+    y[e] = silu_fast(we.x * x0 + we.y * x1 + we.z * x2 + we.w * x3);
   }
   ya = f32x4{y[0], y[1], y[2], y[3]};
   yb = f32x4{y[4], y[5], y[6], y[7]};
@@ -625,12 +631,6 @@ template <> struct RawAct<bf16_t> {
                        __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
   }
 };
-
-// SiLU with the hardware reciprocal and exp (a few ulp of fp32, far inside
-// what the bf16 activations carry); for large |x| it tends to x or to -0.
-__device__ __forceinline__ float silu_fast(float x) {
-  return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
-}
 
 template <typename Raw>
 __device__ __forceinline__ f32x4 conv_silu4(const Raw (&raw)[kConvK], const float4 (&w)[4]) {
