@@ -70,7 +70,9 @@ template <> struct Act<bf16_t> {
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
 // log(1 + e^x) without overflow: max(x, 0) + log1p(e^-|x|).
 __device__ __forceinline__ float softplusf_(float x) { return fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x))); }
-__device__ __forceinline__ float siluf_(float x) { return x / (1.0f + expf(-x)); }
+// SiLU x sigma(x) with the hardware reciprocal and exp: a few ulp of fp32,
+// far inside what bf16 activations carry; tends to x or to -0 for large |x|.
+__device__ __forceinline__ float siluf_(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 // 1 / (L2 norm) of a q or k head from its sum of squares: the clamp form
 // 1 / max(sqrt(ss), eps), or with rsqrt_form the form 1 / sqrt(ss + eps).

@@ -121,12 +121,6 @@ template <> __device__ __forceinline__ Op<Prec::BF16X3>::Frag make_frag<Prec::BF
 // local token tl (0 <= tl < L) of sequence n, from rows tl - 3 .. tl of
 // [st_in[n]; qkv rows of the sequence] (the same arithmetic as the prep
 // kernel: tap 3 meets the current row).
-// SiLU with the hardware reciprocal and exp (a few ulp of fp32, far inside
-// what the bf16 activations carry); for large |x| it tends to x or to -0.
-__device__ __forceinline__ float silu_fast(float x) {
-  return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
-}
-
 template <typename TA>
 __device__ __forceinline__ void conv_silu8(const PrefillParams &p, int n, int seq0, int C, int tl, int c0,
                                            f32x4 &ya, f32x4 &yb) {
@@ -150,7 +144,7 @@ __device__ __forceinline__ void conv_silu8(const PrefillParams &p, int n, int se
     const float x1 = e < 4 ? (&xa[1].x)[e] : (&xb[1].x)[e - 4];
     const float x2 = e < 4 ? (&xa[2].x)[e] : (&xb[2].x)[e - 4];
     const float x3 = e < 4 ? (&xa[3].x)[e] : (&xb[3].x)[e - 4];
-    y[e] = silu_fast(we.x * x0 + we.y * x1 + we.z * x2 + we.w * x3);
+    y[e] = siluf_(we.x * x0 + we.y * x1 + we.z * x2 + we.w * x3);
   }
   ya = f32x4{y[0], y[1], y[2], y[3]};
   yb = f32x4{y[4], y[5], y[6], y[7]};
@@ -641,7 +635,7 @@ __device__ __forceinline__ f32x4 conv_silu4(const Raw (&raw)[kConvK], const floa
   f32x4 y;
 #pragma unroll
   for (int e = 0; e < 4; ++e)
-    y[e] = silu_fast(w[e].x * (&x[0].x)[e] + w[e].y * (&x[1].x)[e] + w[e].z * (&x[2].x)[e] + w[e].w * (&x[3].x)[e]);
+    y[e] = siluf_(w[e].x * (&x[0].x)[e] + w[e].y * (&x[1].x)[e] + w[e].z * (&x[2].x)[e] + w[e].w * (&x[3].x)[e]);
   return y;
 }
 
