@@ -117,7 +117,7 @@ def measured_traffic(key: str):
 
 def _kernel_key(name: str) -> str:
     """A kernel's name without namespace noise and argument list, with the
-    precision enum spelled out (`chunk_state_kernel<BF16X3, gdn::bf16_t, true>`)."""
+    precision enum spelled out (`chunk_state_kernel<BF16X3, gdn::bf16_t, true, false>`)."""
     name = name.replace("(anonymous namespace)::", "").replace("void ", "")
     name = name.replace("(gdn::Prec)1", "BF16X3").replace("(gdn::Prec)0", "F32")
     return name.split("(")[0]
@@ -194,10 +194,10 @@ def write_traffic(dbs):
     kernels = {}
     for key, run, subs, what in (
             ("prefill_core", "prefill", ("chunk_local_kernel<BF16X3, gdn::bf16_t, false>",
-                                         "chunk_state_kernel<BF16X3, gdn::bf16_t, false>"),
+                                         "chunk_state_kernel<BF16X3, gdn::bf16_t, false, false>"),
              "gdn_prefill_chunked on the T=4096, Hv=48 bf16 workload (chunk_local + chunk_state)"),
             ("prefill_fused_core", "prefill", ("chunk_local_kernel<BF16X3, gdn::bf16_t, true>",
-                                               "chunk_state_kernel<BF16X3, gdn::bf16_t, true>"),
+                                               "chunk_state_kernel<BF16X3, gdn::bf16_t, true, false>"),
              "the chunked kernels of gdn_prefill_fused, T=4096 Hv=48 bf16 (q, k, v, gates formed inside)"),
             ("prefill_prep", "prefill", ("prep_kernel",), "gdn_conv_gate_prep, T=4096 Hv=48 bf16"),
             ("prefill_norm", "prefill", ("norm_kernel",), "gdn_gated_rmsnorm, T=4096 Hv=48 bf16"),
