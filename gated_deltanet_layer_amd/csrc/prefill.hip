@@ -117,25 +117,52 @@ template <> __device__ __forceinline__ Op<Prec::BF16X3>::Frag make_frag<Prec::BF
 //     substitution in place, one wave per V-head; Tm = L^-1 diag(beta) to
 //     the workspace over all waves. Blocks of P and Tm above the diagonal
 //     32 x 32 blocks are all zero and are never written or read.
-// Fused form: conv + SiLU of channels c0 .. c0 + 7 (c0 a multiple of 8) for
-// local token tl (0 <= tl < L) of sequence n, from rows tl - 3 .. tl of
-// [st_in[n]; qkv rows of the sequence] (the same arithmetic as the prep
-// kernel: tap 3 meets the current row).
+// Fused form: 4 consecutive raw activations as loaded (undecoded, so the load
+// can stay in flight until its first use).
+template <typename TA> struct RawAct;
+template <> struct RawAct<float> {
+  using type = float4;
+  static __device__ __forceinline__ float4 f4(float4 x) { return x; }
+};
+template <> struct RawAct<bf16_t> {
+  using type = uint2;
+  static __device__ __forceinline__ float4 f4(uint2 w) {
+    return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                       __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
+  }
+};
+
+// Fused form: the raw activations of channels c0 .. c0 + 7 (c0 a multiple of
+// 8) on rows tl - 3 .. tl of [st_in[n]; qkv rows of sequence n] (0 <= tl <
+// L), the inputs of one conv. They are loaded first and decoded at use, so
+// that every load of a q or k row is in flight at once.
+template <typename TA> struct Raw8 {
+  typename RawAct<TA>::type v[kConvK][2];
+};
 template <typename TA>
-__device__ __forceinline__ void conv_silu8(const PrefillParams &p, int n, int seq0, int C, int tl, int c0,
-                                           f32x4 &ya, f32x4 &yb) {
+__device__ __forceinline__ void load_raw8(const PrefillParams &p, int n, int seq0, int C, int tl, int c0, Raw8<TA> &r) {
+  using Raw = typename RawAct<TA>::type;
   const TA *qkv = static_cast<const TA *>(p.qkv);
   const TA *st = static_cast<const TA *>(p.st_in);
-  float4 xa[kConvK], xb[kConvK];
 #pragma unroll
-  for (int r = 0; r < kConvK; ++r) {
-    const int pos = tl - (kConvK - 1) + r;
+  for (int k = 0; k < kConvK; ++k) {
+    const int pos = tl - (kConvK - 1) + k;
     const TA *src = pos < 0 ? st + (static_cast<size_t>(n) * (kConvK - 1) + (pos + kConvK - 1)) * C
                             : qkv + static_cast<size_t>(seq0 + pos) * C;
-    xa[r] = Act<TA>::load4(src, c0);
-    xb[r] = Act<TA>::load4(src, c0 + 4);
+    r.v[k][0] = *reinterpret_cast<const Raw *>(src + c0);
+    r.v[k][1] = *reinterpret_cast<const Raw *>(src + c0 + 4);
   }
-  const float4 *w = reinterpret_cast<const float4 *>(p.conv_w) + c0;
+}
+// conv + SiLU of those 8 channels (the same arithmetic as the prep kernel:
+// tap 3 meets the current row); w holds their taps.
+template <typename TA>
+__device__ __forceinline__ void conv_silu8(const Raw8<TA> &r, const float4 *w, f32x4 &ya, f32x4 &yb) {
+  float4 xa[kConvK], xb[kConvK];
+#pragma unroll
+  for (int k = 0; k < kConvK; ++k) {
+    xa[k] = RawAct<TA>::f4(r.v[k][0]);
+    xb[k] = RawAct<TA>::f4(r.v[k][1]);
+  }
   float y[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -151,18 +178,26 @@ __device__ __forceinline__ void conv_silu8(const PrefillParams &p, int n, int se
 }
 
 // Fused form: row tl of q (part 0) or k (part 1) of K-head h, the lane's 32
-// channels 32 ks + 8 (lane / 16) .. +7, conv + SiLU + L2 norm over the
-// row's 128 channels (spread over lanes l, l ^ 16, l ^ 32, l ^ 48).
+// channels 32 ks + 8 (lane / 16) .. +7: qk_load issues the raw loads,
+// qk_form takes conv + SiLU (taps w of the part's 128 channels) and the L2
+// norm over the row's 128 channels (spread over lanes l, l ^ 16, l ^ 32,
+// l ^ 48).
 template <typename TA>
-__device__ __forceinline__ void qk_row(const PrefillParams &p, int n, int seq0, int L, int tl, bool valid, int part,
-                                       int h, f32x4 (&ya)[kHeadDim / 32], f32x4 (&yb)[kHeadDim / 32]) {
+__device__ __forceinline__ void qk_load(const PrefillParams &p, int n, int seq0, int L, int tl, int part, int h,
+                                        Raw8<TA> (&raw)[kHeadDim / 32]) {
   const int C = kHeadDim * (2 * p.n_qk + p.n_v);
   const int cbase = (part * p.n_qk + h) * kHeadDim + 8 * (lane_id() >> 4);
   const int t = min(tl, L - 1);
+#pragma unroll
+  for (int ks = 0; ks < kHeadDim / 32; ++ks) load_raw8<TA>(p, n, seq0, C, t, cbase + 32 * ks, raw[ks]);
+}
+template <typename TA>
+__device__ __forceinline__ void qk_form(const PrefillParams &p, const Raw8<TA> (&raw)[kHeadDim / 32], const float4 *w,
+                                        bool valid, f32x4 (&ya)[kHeadDim / 32], f32x4 (&yb)[kHeadDim / 32]) {
   float ss = 0.f;
 #pragma unroll
   for (int ks = 0; ks < kHeadDim / 32; ++ks) {
-    conv_silu8<TA>(p, n, seq0, C, t, cbase + 32 * ks, ya[ks], yb[ks]);
+    conv_silu8<TA>(raw[ks], w + 32 * ks + 8 * (lane_id() >> 4), ya[ks], yb[ks]);
 #pragma unroll
     for (int e = 0; e < 4; ++e) ss += ya[ks][e] * ya[ks][e] + yb[ks][e] * yb[ks][e];
   }
@@ -197,6 +232,7 @@ __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(PrefillParam
   __shared__ float Tsc[kSolveWaves][16 * 17];
   __shared__ double gam_s[kSolveWaves][kChunk];
   __shared__ float bet_s[kSolveWaves][kChunk];
+  __shared__ float4 Wtap[kFused ? 2 * kHeadDim : 1];   // fused: conv taps of the q and k channels
   uint8_t *Kb = buf;
 
   const int tid = threadIdx.x;
@@ -266,18 +302,29 @@ __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(PrefillParam
   Frag fq[kHeadDim / 32];
   if constexpr (kFused) {
     // k and q of row qrow from the raw rows; k goes to LDS (blocked operand
-    // rows, as below), q stays in this lane's A-fragment slots.
+    // rows, as below), q stays in this lane's A-fragment slots. The conv
+    // taps of the K-head's q and k channels go to LDS; the raw loads of
+    // both rows (bf16; fp32 would need twice the registers: one row at a
+    // time) are issued before any is used.
+    constexpr bool kBoth = sizeof(TA) == 2;
+    const float4 wtap = reinterpret_cast<const float4 *>(p.conv_w)[((tid >> 7) * p.n_qk + h) * kHeadDim + (tid & 127)];
+    Raw8<TA> rk[kHeadDim / 32], rq[kHeadDim / 32];
+    qk_load<TA>(p, n, seq0, L, ci * kChunk + qrow, 1, h, rk);
+    if constexpr (kBoth) qk_load<TA>(p, n, seq0, L, ci * kChunk + qrow, 0, h, rq);
     if (wave < min(nvh, kSolveWaves)) load_gates(wave, g_first, b_first);
+    Wtap[tid] = wtap;   // q taps at 0, k taps at kHeadDim
+    block_sync_lds();
     const bool valid = qrow < len;
     f32x4 ya[kHeadDim / 32], yb[kHeadDim / 32];
-    qk_row<TA>(p, n, seq0, L, ci * kChunk + qrow, valid, 1, h, ya, yb);
+    qk_form<TA>(p, rk, Wtap + kHeadDim, valid, ya, yb);
 #pragma unroll
     for (int ks = 0; ks < kHeadDim / 32; ++ks) {
       const int c = 32 * ks + 8 * (lane >> 4);
       Op<P>::put4(Kb + qrow * kPitch128, c, ya[ks]);
       Op<P>::put4(Kb + qrow * kPitch128, c + 4, yb[ks]);
     }
-    qk_row<TA>(p, n, seq0, L, ci * kChunk + qrow, valid, 0, h, ya, yb);
+    if constexpr (!kBoth) qk_load<TA>(p, n, seq0, L, ci * kChunk + qrow, 0, h, rq);
+    qk_form<TA>(p, rq, Wtap, valid, ya, yb);
 #pragma unroll
     for (int ks = 0; ks < kHeadDim / 32; ++ks) fq[ks] = make_frag<P>(ya[ks], yb[ks]);
   } else {
@@ -611,20 +658,7 @@ template <> struct KtLds<Prec::F32> {
   }
 };
 
-// Fused form: 4 consecutive raw activations as loaded (undecoded, so the load
-// can stay in flight), and their conv + SiLU over rows t - 3 .. t.
-template <typename TA> struct RawAct;
-template <> struct RawAct<float> {
-  using type = float4;
-  static __device__ __forceinline__ float4 f4(float4 x) { return x; }
-};
-template <> struct RawAct<bf16_t> {
-  using type = uint2;
-  static __device__ __forceinline__ float4 f4(uint2 w) {
-    return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
-                       __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
-  }
-};
+// Fused form: conv + SiLU of 4 raw activations over rows t - 3 .. t.
 
 template <typename Raw>
 __device__ __forceinline__ f32x4 conv_silu4(const Raw (&raw)[kConvK], const float4 (&w)[4]) {
