@@ -200,7 +200,7 @@ def write_traffic(dbs):
                                                "chunk_state_kernel<BF16X3, gdn::bf16_t, true, false>"),
              "the chunked kernels of gdn_prefill_fused, T=4096 Hv=48 bf16 (q, k, v, gates formed inside)"),
             ("prefill_prep", "prefill", ("prep_kernel",), "gdn_conv_gate_prep, T=4096 Hv=48 bf16"),
-            ("prefill_norm", "prefill", ("norm_kernel",), "gdn_gated_rmsnorm, T=4096 Hv=48 bf16"),
+            ("prefill_norm", "prefill", ("norm_kernel<gdn::bf16_t, false>",), "gdn_gated_rmsnorm, T=4096 Hv=48 bf16"),
             ("decode_b64", "decode_b64", ("decode_kernel",), "gdn_decode_step, batch 64, Hv=32"),
             ("decode_fused_b64", "decode_b64", ("decode_tokens_kernel<gdn::bf16_t, true>",), "gdn_decode_fused, batch 64, Hv=32"),
             ("decode_b1", "decode_b1", ("decode_kernel",), "gdn_decode_step, batch 1, Hv=32"),

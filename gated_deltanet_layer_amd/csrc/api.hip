@@ -301,7 +301,9 @@ gdn_status gdn_prefill_fused(const gdn_config *cfg, int32_t n_seqs, int32_t n_to
   p.l2_eps = cfg->l2_eps;
   p.l2_mode = cfg->l2_mode;
   hipError_t e = gdn::launch_prefill(p, cfg->act_dtype, hs);
-  if (e == hipSuccess && n_tokens > 0) {
+  if (e == hipSuccess) {
+    // The norm, and the new conv states: last, since the kernels above read
+    // the old conv state (in-place safe).
     gdn::NormParams np;
     np.n_rows = static_cast<int64_t>(n_tokens) * Hv;
     np.o = o;
@@ -309,10 +311,6 @@ gdn_status gdn_prefill_fused(const gdn_config *cfg, int32_t n_seqs, int32_t n_to
     np.w = norm_w;
     np.y = y;
     np.eps = cfg->norm_eps;
-    e = gdn::launch_norm(np, cfg->act_dtype, hs);
-  }
-  if (e == hipSuccess) {
-    // Last: the kernels above read the old conv state (in-place safe).
     gdn::ConvStateParams cp;
     cp.cu = cu_seqlens;
     cp.n_seqs = n_seqs;
@@ -321,7 +319,7 @@ gdn_status gdn_prefill_fused(const gdn_config *cfg, int32_t n_seqs, int32_t n_to
     cp.qkv = qkv;
     cp.st_in = conv_state_in;
     cp.st_out = conv_state_out;
-    e = gdn::launch_conv_state(cp, cfg->act_dtype, hs);
+    e = gdn::launch_norm_conv_state(np, cp, cfg->act_dtype, hs);
   }
   return launched(e);
 }

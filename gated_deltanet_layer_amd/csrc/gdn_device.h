@@ -406,6 +406,30 @@ __device__ __forceinline__ void block_sync_lds() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// New conv state of packed sequence n, channels c and c + 1: rows L, L+1,
+// L+2 of [st_in[n]; qkv rows of the sequence] (its last 3 raw rows). The
+// thread reads its 3 source rows before writing, so st_out may be st_in.
+template <typename TA>
+__device__ __forceinline__ void conv_state_pair(const ConvStateParams &p, int n, int c) {
+  if (n >= p.n_seqs || c >= p.C) return;
+  const int seq0 = p.cu[n];
+  const int L = p.cu[n + 1] - seq0;
+  if (seq0 < 0 || L < 0 || seq0 + L > p.n_tokens) return;
+  const TA *qkv = static_cast<const TA *>(p.qkv);
+  const TA *st_in = static_cast<const TA *>(p.st_in);
+  TA *st_out = static_cast<TA *>(p.st_out);
+  const size_t st_base = static_cast<size_t>(n) * (kConvK - 1) * p.C;
+  float2 v[kConvK - 1];
+#pragma unroll
+  for (int r = 0; r < kConvK - 1; ++r) {
+    const int src = L + r;   // row of [state; x]
+    v[r] = src < kConvK - 1 ? Act<TA>::load2(st_in, st_base + static_cast<size_t>(src) * p.C + c)
+                            : Act<TA>::load2(qkv, static_cast<size_t>(seq0 + src - (kConvK - 1)) * p.C + c);
+  }
+#pragma unroll
+  for (int r = 0; r < kConvK - 1; ++r) Act<TA>::store2(st_out, st_base + static_cast<size_t>(r) * p.C + c, v[r]);
+}
+
 // Legacy fp32 fragments from row-major fp32 LDS (used by the small fp32 MFMA
 // steps of the triangular solve).
 }  // namespace gdn

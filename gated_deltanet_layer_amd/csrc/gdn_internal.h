@@ -88,6 +88,9 @@ struct ConvStateParams {
   void *st_out;
 };
 hipError_t launch_conv_state(const ConvStateParams &p, gdn_dtype act, hipStream_t s);
+// The gated RMSNorm and the new conv states in one launch (the states after
+// the norm's blocks).
+hipError_t launch_norm_conv_state(const NormParams &p, const ConvStateParams &cp, gdn_dtype act, hipStream_t s);
 
 // Non-finite guard over n_values fp32 state values: stats[0] = number of
 // non-finite values, stats[1] = bit pattern of max |x| over the finite ones.

@@ -47,8 +47,17 @@ __device__ __forceinline__ void store8(bf16_t *p, size_t i, float4 a, float4 b) 
 // 16 lanes per row, 8 values per lane (16-byte bf16 or 32-byte fp32 accesses),
 // 4 rows per wave at a time; each thread handles kRowsPerThread rows that
 // lie kRowsPerBlock apart, all loaded before any is used.
-template <typename TA>
-__global__ __launch_bounds__(kNormThreads) void norm_kernel(NormParams p) {
+// kConv: blocks past the norm's also write the new conv states of the
+// packed sequences (conv_state_pair, 2 channels per thread), in the same
+// launch: both only read what earlier kernels left.
+template <typename TA, bool kConv>
+__global__ __launch_bounds__(kNormThreads) void norm_kernel(NormParams p, ConvStateParams cp, int norm_blocks,
+                                                            int conv_per_seq) {
+  if (kConv && static_cast<int>(blockIdx.x) >= norm_blocks) {
+    const int b = blockIdx.x - norm_blocks;
+    conv_state_pair<TA>(cp, b / conv_per_seq, 2 * ((b % conv_per_seq) * kNormThreads + threadIdx.x));
+    return;
+  }
   const int sub = threadIdx.x % kLanesPerRow;
   const int64_t row0 = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock * kRowsPerThread + threadIdx.x / kLanesPerRow;
   const float4 w0 = *reinterpret_cast<const float4 *>(p.w + 8 * sub);
@@ -86,10 +95,27 @@ __global__ __launch_bounds__(kNormThreads) void norm_kernel(NormParams p) {
 
 hipError_t launch_norm(const NormParams &p, gdn_dtype act, hipStream_t s) {
   const int64_t blocks = (p.n_rows + kRowsPerBlock * kRowsPerThread - 1) / (kRowsPerBlock * kRowsPerThread);
+  const ConvStateParams none{};
   if (act == GDN_BF16)
-    hipLaunchKernelGGL(norm_kernel<bf16_t>, dim3(static_cast<unsigned>(blocks)), dim3(kNormThreads), 0, s, p);
+    hipLaunchKernelGGL((norm_kernel<bf16_t, false>), dim3(static_cast<unsigned>(blocks)), dim3(kNormThreads), 0, s, p,
+                       none, static_cast<int>(blocks), 1);
   else
-    hipLaunchKernelGGL(norm_kernel<float>, dim3(static_cast<unsigned>(blocks)), dim3(kNormThreads), 0, s, p);
+    hipLaunchKernelGGL((norm_kernel<float, false>), dim3(static_cast<unsigned>(blocks)), dim3(kNormThreads), 0, s, p,
+                       none, static_cast<int>(blocks), 1);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm_conv_state(const NormParams &p, const ConvStateParams &cp, gdn_dtype act, hipStream_t s) {
+  const int64_t blocks = (p.n_rows + kRowsPerBlock * kRowsPerThread - 1) / (kRowsPerBlock * kRowsPerThread);
+  const int per_seq = (cp.C / 2 + kNormThreads - 1) / kNormThreads;
+  const int64_t total = blocks + static_cast<int64_t>(cp.n_seqs) * per_seq;
+  if (total == 0) return hipSuccess;
+  if (act == GDN_BF16)
+    hipLaunchKernelGGL((norm_kernel<bf16_t, true>), dim3(static_cast<unsigned>(total)), dim3(kNormThreads), 0, s, p,
+                       cp, static_cast<int>(blocks), per_seq);
+  else
+    hipLaunchKernelGGL((norm_kernel<float, true>), dim3(static_cast<unsigned>(total)), dim3(kNormThreads), 0, s, p,
+                       cp, static_cast<int>(blocks), per_seq);
   return hipGetLastError();
 }
 

@@ -134,14 +134,33 @@ template <> struct RawAct<bf16_t> {
 
 // Fused form: the raw activations of channels c0 .. c0 + 7 (c0 a multiple of
 // 8) on rows tl - 3 .. tl of [st_in[n]; qkv rows of sequence n] (0 <= tl <
-// L), the inputs of one conv. They are loaded first and decoded at use, so
-// that every load of a q or k row is in flight at once.
-template <typename TA> struct Raw8 {
-  typename RawAct<TA>::type v[kConvK][2];
+// L), the inputs of one conv: one 16-byte load per row for bf16, two for
+// fp32. They are loaded first and decoded at use, so that every load of a q
+// or k row is in flight at once.
+template <typename TA> struct Raw8;
+template <> struct Raw8<bf16_t> {
+  uint4 v[kConvK];
+  __device__ __forceinline__ void load(int k, const bf16_t *src) { v[k] = *reinterpret_cast<const uint4 *>(src); }
+  __device__ __forceinline__ void get(int k, float4 &a, float4 &b) const {
+    a = make_float4(__uint_as_float(v[k].x << 16), __uint_as_float(v[k].x & 0xffff0000u),
+                    __uint_as_float(v[k].y << 16), __uint_as_float(v[k].y & 0xffff0000u));
+    b = make_float4(__uint_as_float(v[k].z << 16), __uint_as_float(v[k].z & 0xffff0000u),
+                    __uint_as_float(v[k].w << 16), __uint_as_float(v[k].w & 0xffff0000u));
+  }
+};
+template <> struct Raw8<float> {
+  float4 v[kConvK][2];
+  __device__ __forceinline__ void load(int k, const float *src) {
+    v[k][0] = *reinterpret_cast<const float4 *>(src);
+    v[k][1] = *reinterpret_cast<const float4 *>(src + 4);
+  }
+  __device__ __forceinline__ void get(int k, float4 &a, float4 &b) const {
+    a = v[k][0];
+    b = v[k][1];
+  }
 };
 template <typename TA>
 __device__ __forceinline__ void load_raw8(const PrefillParams &p, int n, int seq0, int C, int tl, int c0, Raw8<TA> &r) {
-  using Raw = typename RawAct<TA>::type;
   const TA *qkv = static_cast<const TA *>(p.qkv);
   const TA *st = static_cast<const TA *>(p.st_in);
 #pragma unroll
@@ -149,8 +168,7 @@ __device__ __forceinline__ void load_raw8(const PrefillParams &p, int n, int seq
     const int pos = tl - (kConvK - 1) + k;
     const TA *src = pos < 0 ? st + (static_cast<size_t>(n) * (kConvK - 1) + (pos + kConvK - 1)) * C
                             : qkv + static_cast<size_t>(seq0 + pos) * C;
-    r.v[k][0] = *reinterpret_cast<const Raw *>(src + c0);
-    r.v[k][1] = *reinterpret_cast<const Raw *>(src + c0 + 4);
+    r.load(k, src + c0);
   }
 }
 // conv + SiLU of those 8 channels (the same arithmetic as the prep kernel:
@@ -159,10 +177,7 @@ template <typename TA>
 __device__ __forceinline__ void conv_silu8(const Raw8<TA> &r, const float4 *w, f32x4 &ya, f32x4 &yb) {
   float4 xa[kConvK], xb[kConvK];
 #pragma unroll
-  for (int k = 0; k < kConvK; ++k) {
-    xa[k] = RawAct<TA>::f4(r.v[k][0]);
-    xb[k] = RawAct<TA>::f4(r.v[k][1]);
-  }
+  for (int k = 0; k < kConvK; ++k) r.get(k, xa[k], xb[k]);
   float y[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {

@@ -129,32 +129,14 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void prep_kernel(PrepParams p) 
   }
 }
 
-// New conv state of each packed sequence: rows L, L+1, L+2 of [state; x]
-// (the last 3 raw rows). A thread owns 2 channels of one sequence and reads
-// its 3 source rows before writing, so the update may be in place.
+// New conv state of each packed sequence (conv_state_pair): a thread owns 2
+// channels of one sequence.
 constexpr int kConvStateThreads = 256;
 
 template <typename TA>
 __global__ __launch_bounds__(kConvStateThreads) void conv_state_kernel(ConvStateParams p, int blocks_per_seq) {
-  const int n = blockIdx.x / blocks_per_seq;
-  const int c = 2 * ((blockIdx.x % blocks_per_seq) * kConvStateThreads + threadIdx.x);
-  if (n >= p.n_seqs || c >= p.C) return;
-  const int seq0 = p.cu[n];
-  const int L = p.cu[n + 1] - seq0;
-  if (seq0 < 0 || L < 0 || seq0 + L > p.n_tokens) return;
-  const TA *qkv = static_cast<const TA *>(p.qkv);
-  const TA *st_in = static_cast<const TA *>(p.st_in);
-  TA *st_out = static_cast<TA *>(p.st_out);
-  const size_t st_base = static_cast<size_t>(n) * (kConvK - 1) * p.C;
-  float2 v[kConvK - 1];
-#pragma unroll
-  for (int r = 0; r < kConvK - 1; ++r) {
-    const int src = L + r;   // row of [state; x]
-    v[r] = src < kConvK - 1 ? Act<TA>::load2(st_in, st_base + static_cast<size_t>(src) * p.C + c)
-                            : Act<TA>::load2(qkv, static_cast<size_t>(seq0 + src - (kConvK - 1)) * p.C + c);
-  }
-#pragma unroll
-  for (int r = 0; r < kConvK - 1; ++r) Act<TA>::store2(st_out, st_base + static_cast<size_t>(r) * p.C + c, v[r]);
+  conv_state_pair<TA>(p, blockIdx.x / blocks_per_seq,
+                      2 * ((blockIdx.x % blocks_per_seq) * kConvStateThreads + threadIdx.x));
 }
 
 }  // namespace
