@@ -87,7 +87,6 @@ struct ConvStateParams {
   const void *qkv, *st_in;
   void *st_out;
 };
-hipError_t launch_conv_state(const ConvStateParams &p, gdn_dtype act, hipStream_t s);
 // The gated RMSNorm and the new conv states in one launch (the states after
 // the norm's blocks).
 hipError_t launch_norm_conv_state(const NormParams &p, const ConvStateParams &cp, gdn_dtype act, hipStream_t s);

@@ -129,28 +129,7 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void prep_kernel(PrepParams p) 
   }
 }
 
-// New conv state of each packed sequence (conv_state_pair): a thread owns 2
-// channels of one sequence.
-constexpr int kConvStateThreads = 256;
-
-template <typename TA>
-__global__ __launch_bounds__(kConvStateThreads) void conv_state_kernel(ConvStateParams p, int blocks_per_seq) {
-  conv_state_pair<TA>(p, blockIdx.x / blocks_per_seq,
-                      2 * ((blockIdx.x % blocks_per_seq) * kConvStateThreads + threadIdx.x));
-}
-
 }  // namespace
-
-hipError_t launch_conv_state(const ConvStateParams &p, gdn_dtype act, hipStream_t s) {
-  if (p.n_seqs == 0) return hipSuccess;
-  const int per_seq = (p.C / 2 + kConvStateThreads - 1) / kConvStateThreads;
-  const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(p.n_seqs) * per_seq));
-  if (act == GDN_BF16)
-    hipLaunchKernelGGL(conv_state_kernel<bf16_t>, grid, dim3(kConvStateThreads), 0, s, p, per_seq);
-  else
-    hipLaunchKernelGGL(conv_state_kernel<float>, grid, dim3(kConvStateThreads), 0, s, p, per_seq);
-  return hipGetLastError();
-}
 
 hipError_t launch_prep(const PrepParams &p, gdn_dtype act, hipStream_t s) {
   const int64_t tiles = (static_cast<int64_t>(p.n_tokens) + kPrepTile - 1) / kPrepTile + p.n_seqs;
