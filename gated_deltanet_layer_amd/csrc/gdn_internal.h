@@ -16,7 +16,7 @@ constexpr int kHeadDim = 128;  // the only head dim the page's models use
 constexpr int kConvK = 4;      // conv kernel size
 
 // Token tile of the prep kernel and chunk length of the chunked delta rule.
-constexpr int kPrepTile = 16;
+constexpr int kPrepTile = 32;
 constexpr int kChunk = 64;
 
 struct PrepParams {

@@ -48,7 +48,8 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void prep_kernel(PrepParams p) 
   const int tau0 = tile * kPrepTile;
   const int ntok = min(kPrepTile, L - tau0);
 
-  // Raw rows tau0-3 .. tau0+15 of [state; x], all loaded before any is used.
+  // Raw rows tau0 - 3 .. tau0 + kPrepTile - 1 of [state; x], all loaded before
+  // any is used.
   // Rows before the sequence come from the conv state; rows past its end are
   // clamped to its last row and never used.
   constexpr int kRows = kPrepTile + kConvK - 1;
