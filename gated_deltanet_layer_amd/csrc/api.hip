@@ -106,7 +106,8 @@ gdn_status gdn_conv_gate_prep(const gdn_config *cfg, int32_t n_seqs, int32_t n_t
   const int Hqk = cfg->n_qk_heads, Hv = cfg->n_v_heads;
   const size_t C = static_cast<size_t>(kHeadDim) * (2 * Hqk + Hv);
   const size_t T = static_cast<size_t>(n_tokens), as = act_size(cfg);
-  const int64_t tiles = (static_cast<int64_t>(n_tokens) + gdn::kPrepTile - 1) / gdn::kPrepTile + n_seqs;
+  const int tile = gdn::prep_tile(n_seqs, n_tokens);
+  const int64_t tiles = (static_cast<int64_t>(n_tokens) + tile - 1) / tile + n_seqs;
   if (tiles > kMaxGrid) return GDN_E_UNSUPPORTED;
   const size_t st = static_cast<size_t>(n_seqs) * (gdn::kConvK - 1) * C * as;
   const Range outs[] = {{q, T * Hqk * kHeadDim * 4}, {k, T * Hqk * kHeadDim * 4}, {v, T * Hv * kHeadDim * 4},

@@ -15,8 +15,13 @@ constexpr int kWave = 64;      // wavefront width on CDNA
 constexpr int kHeadDim = 128;  // the only head dim the page's models use
 constexpr int kConvK = 4;      // conv kernel size
 
-// Token tile of the prep kernel and chunk length of the chunked delta rule.
-constexpr int kPrepTile = 32;
+// Token tile of the prep kernel: 32 tokens when sequences average at least
+// that many (the 3-row halo is re-read once per tile), else 8 (decode-like
+// calls, where a longer tile would load rows it never uses).
+inline int prep_tile(int n_seqs, int n_tokens) {
+  return static_cast<int64_t>(n_tokens) >= 32 * static_cast<int64_t>(n_seqs) ? 32 : 8;
+}
+// Chunk length of the chunked delta rule.
 constexpr int kChunk = 64;
 
 struct PrepParams {

@@ -8,7 +8,7 @@
 // with ssm_a = -exp(A_log) per the section "GGUF facts that differ from the
 // HF checkpoint").
 //
-// Grid: x = token tiles (kPrepTile tokens of one sequence; an empty sequence
+// Grid: x = token tiles (kTile tokens of one sequence; an empty sequence
 // owns one tile that only moves its conv state), y = groups of 4 head blocks
 // (a head block is 128 fused channels: Hqk q heads, Hqk k heads, Hv v
 // heads). One wave per head block, so a block reads 4 adjacent 256-byte
@@ -23,13 +23,13 @@ namespace {
 
 constexpr int kPrepWaves = 4;   // consecutive head blocks per block (1 KB of each bf16 row)
 
-template <typename TA>
+template <typename TA, int kTile>
 __global__ __launch_bounds__(kPrepWaves * kWave) void prep_kernel(PrepParams p) {
   const int lane = lane_id();
   const int hb = blockIdx.y * kPrepWaves + threadIdx.x / kWave;
   if (hb >= 2 * p.n_qk + p.n_v) return;
   int n, tile;
-  if (!find_unit(p.cu, p.n_seqs, blockIdx.x, kPrepTile, 1, &n, &tile)) return;
+  if (!find_unit(p.cu, p.n_seqs, blockIdx.x, kTile, 1, &n, &tile)) return;
   const int seq0 = p.cu[n];
   const int L = p.cu[n + 1] - seq0;
   // Indices derived from cu_seqlens must stay inside the buffers.
@@ -45,14 +45,14 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void prep_kernel(PrepParams p) 
   const float4 w0 = reinterpret_cast<const float4 *>(p.conv_w)[c];
   const float4 w1 = reinterpret_cast<const float4 *>(p.conv_w)[c + 1];
 
-  const int tau0 = tile * kPrepTile;
-  const int ntok = min(kPrepTile, L - tau0);
+  const int tau0 = tile * kTile;
+  const int ntok = min(kTile, L - tau0);
 
-  // Raw rows tau0 - 3 .. tau0 + kPrepTile - 1 of [state; x], all loaded before
+  // Raw rows tau0 - 3 .. tau0 + kTile - 1 of [state; x], all loaded before
   // any is used.
   // Rows before the sequence come from the conv state; rows past its end are
   // clamped to its last row and never used.
-  constexpr int kRows = kPrepTile + kConvK - 1;
+  constexpr int kRows = kTile + kConvK - 1;
   float2 xr[kRows];
 #pragma unroll
   for (int r = 0; r < kRows; ++r) {
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void prep_kernel(PrepParams p) 
   }
 
 #pragma unroll
-  for (int i = 0; i < kPrepTile; ++i) {
+  for (int i = 0; i < kTile; ++i) {
     if (i < ntok) {
       const size_t t = static_cast<size_t>(seq0 + tau0 + i);
       float y0 = w0.x * xr[i].x + w0.y * xr[i + 1].x + w0.z * xr[i + 2].x + w0.w * xr[i + 3].x;
@@ -133,13 +133,18 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void prep_kernel(PrepParams p) 
 }  // namespace
 
 hipError_t launch_prep(const PrepParams &p, gdn_dtype act, hipStream_t s) {
-  const int64_t tiles = (static_cast<int64_t>(p.n_tokens) + kPrepTile - 1) / kPrepTile + p.n_seqs;
+  const int tile = prep_tile(p.n_seqs, p.n_tokens);
+  const int64_t tiles = (static_cast<int64_t>(p.n_tokens) + tile - 1) / tile + p.n_seqs;
   const int head_blocks = 2 * p.n_qk + p.n_v;
   const dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>((head_blocks + kPrepWaves - 1) / kPrepWaves));
-  if (act == GDN_BF16)
-    hipLaunchKernelGGL(prep_kernel<bf16_t>, grid, dim3(kPrepWaves * kWave), 0, s, p);
-  else
-    hipLaunchKernelGGL(prep_kernel<float>, grid, dim3(kPrepWaves * kWave), 0, s, p);
+  const dim3 block(kPrepWaves * kWave);
+  if (act == GDN_BF16) {
+    if (tile == 32) hipLaunchKernelGGL((prep_kernel<bf16_t, 32>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((prep_kernel<bf16_t, 8>), grid, block, 0, s, p);
+  } else {
+    if (tile == 32) hipLaunchKernelGGL((prep_kernel<float, 32>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((prep_kernel<float, 8>), grid, block, 0, s, p);
+  }
   return hipGetLastError();
 }
 
