@@ -86,6 +86,17 @@ def test_prefill_varlen_edge_lengths(act):
     compare_prefill(w, x, P.gpu_prefill(w, x))
 
 
+@pytest.mark.parametrize("lens", [[1, 40, 64, 23], [1, 40, 64, 22]])
+def test_prep_tile_regimes(lens):
+    # The prep kernel takes 32-token tiles when sequences average at least 32
+    # tokens (first case: T = 128 = 32 N) and 8-token tiles otherwise (T = 127):
+    # both, with tiles that end inside and at the end of sequences.
+    w = wl.custom("prefill", len(lens), 2, 4, "bf16", seed=209, lengths=lens, s0_std=0.02, conv0_std=1.0)
+    x = wl.generate(w)
+    say(f"case prep tiles {lens} Hqk=2 Hv=4 bf16")
+    compare_prefill(w, x, P.gpu_prefill(w, x))
+
+
 def test_prefill_empty_call_passes_states_through():
     w = wl.custom("prefill", 3, 2, 4, "bf16", seed=203, lengths=[0, 0, 0], s0_std=0.02, conv0_std=1.0)
     x = wl.generate(w)
