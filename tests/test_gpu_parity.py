@@ -97,6 +97,18 @@ def test_prep_tile_regimes(lens):
     compare_prefill(w, x, P.gpu_prefill(w, x))
 
 
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+@pytest.mark.parametrize("heads", [(1, 7), (2, 8)])
+def test_prefill_many_v_heads_per_k_head(heads, act):
+    # chunk_local handles the V-heads of a K-head three at a time: seven and
+    # four of them take three and two rounds (the last one partial).
+    hqk, hv = heads
+    w = wl.custom("prefill", 2, hqk, hv, act, seed=210, lengths=[150, 67], s0_std=0.02, conv0_std=1.0)
+    x = wl.generate(w)
+    say(f"case prefill lengths [150, 67] Hqk={hqk} Hv={hv} {act}")
+    compare_prefill(w, x, P.gpu_prefill(w, x))
+
+
 def test_prefill_empty_call_passes_states_through():
     w = wl.custom("prefill", 3, 2, 4, "bf16", seed=203, lengths=[0, 0, 0], s0_std=0.02, conv0_std=1.0)
     x = wl.generate(w)

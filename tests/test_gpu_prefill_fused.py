@@ -38,6 +38,17 @@ def test_fused_varlen_edge_lengths(act):
     compare_prefill(w, x, P.gpu_prefill_fused(w, x))
 
 
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+@pytest.mark.parametrize("heads", [(1, 7), (2, 8)])
+def test_fused_many_v_heads_per_k_head(heads, act):
+    # Several rounds of V-heads per K-head in chunk_local (three at a time).
+    hqk, hv = heads
+    w = wl.custom("prefill", 2, hqk, hv, act, seed=503, lengths=[150, 67], s0_std=0.02, conv0_std=1.0)
+    x = wl.generate(w)
+    say(f"case fused prefill lengths [150, 67] Hqk={hqk} Hv={hv} {act}")
+    compare_prefill(w, x, P.gpu_prefill_fused(w, x))
+
+
 def test_fused_empty_call_passes_states_through():
     w = wl.custom("prefill", 3, 2, 4, "bf16", seed=503, lengths=[0, 0, 0], s0_std=0.02, conv0_std=1.0)
     x = wl.generate(w)
