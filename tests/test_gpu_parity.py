@@ -109,6 +109,16 @@ def test_prefill_many_v_heads_per_k_head(heads, act):
     compare_prefill(w, x, P.gpu_prefill(w, x))
 
 
+def test_prefill_many_short_sequences():
+    # 150 packed sequences (0..40 tokens): the kernels find their sequence
+    # and chunk by scanning the lengths 64 sequences at a time.
+    lens = [int(v) for v in np.random.default_rng(211).integers(0, 41, size=150)]
+    w = wl.custom("prefill", len(lens), 1, 2, "bf16", seed=211, lengths=lens, s0_std=0.02, conv0_std=1.0)
+    x = wl.generate(w)
+    say(f"case prefill 150 sequences, T={sum(lens)} Hqk=1 Hv=2 bf16")
+    compare_prefill(w, x, P.gpu_prefill(w, x))
+
+
 def test_prefill_empty_call_passes_states_through():
     w = wl.custom("prefill", 3, 2, 4, "bf16", seed=203, lengths=[0, 0, 0], s0_std=0.02, conv0_std=1.0)
     x = wl.generate(w)

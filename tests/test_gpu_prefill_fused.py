@@ -49,6 +49,15 @@ def test_fused_many_v_heads_per_k_head(heads, act):
     compare_prefill(w, x, P.gpu_prefill_fused(w, x))
 
 
+def test_fused_many_short_sequences():
+    # 150 packed sequences (0..40 tokens), beyond one 64-sequence scan step.
+    lens = [int(v) for v in np.random.default_rng(504).integers(0, 41, size=150)]
+    w = wl.custom("prefill", len(lens), 1, 2, "bf16", seed=504, lengths=lens, s0_std=0.02, conv0_std=1.0)
+    x = wl.generate(w)
+    say(f"case fused prefill 150 sequences, T={sum(lens)} Hqk=1 Hv=2 bf16")
+    compare_prefill(w, x, P.gpu_prefill_fused(w, x))
+
+
 def test_fused_empty_call_passes_states_through():
     w = wl.custom("prefill", 3, 2, 4, "bf16", seed=503, lengths=[0, 0, 0], s0_std=0.02, conv0_std=1.0)
     x = wl.generate(w)
