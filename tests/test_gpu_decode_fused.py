@@ -35,6 +35,13 @@ def test_fused_decode_small(act, heads):
     compare_decode(w, x, P.gpu_decode_fused(w, x))
 
 
+def test_fused_decode_many_sequences():
+    w = wl.custom("decode", 100, 1, 2, "bf16", seed=310, steps=5, s0_std=0.02, conv0_std=1.0)
+    x = wl.generate(w)
+    say("case fused decode N=100 steps=5 Hqk=1 Hv=2 bf16")
+    compare_decode(w, x, P.gpu_decode_fused(w, x))
+
+
 def test_fused_decode_workload2_full():
     w = wl.WORKLOADS[2]
     x = wl.generate(w)

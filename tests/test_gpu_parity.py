@@ -136,6 +136,14 @@ def test_decode_small(act):
     compare_decode(w, x, P.gpu_decode(w, x))
 
 
+def test_decode_many_sequences():
+    # 100 sequences: the prep kernel of each step scans them 64 at a time.
+    w = wl.custom("decode", 100, 1, 2, "bf16", seed=212, steps=5, s0_std=0.02, conv0_std=1.0)
+    x = wl.generate(w)
+    say("case decode N=100 steps=5 Hqk=1 Hv=2 bf16")
+    compare_decode(w, x, P.gpu_decode(w, x))
+
+
 def test_workload1_tiny_fp32_full():
     w = wl.WORKLOADS[1]
     x = wl.generate(w)
