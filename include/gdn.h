@@ -194,7 +194,8 @@ GDN_API gdn_status gdn_state_check(const float *S, int64_t n_values, int32_t *st
  *   S_in, S_out [N][Hv][d][d]: fp32; may be the same buffer
  * qkv, conv_w and both conv states must be 16-byte aligned; `workspace`
  * 256-byte aligned, of gdn_prefill_fused_workspace_bytes(cfg, n_seqs,
- * n_tokens) bytes (may be NULL when that is 0). Four kernels on `stream`.
+ * n_tokens) bytes (may be NULL when that is 0). Three kernels on `stream`; the last
+ * writes y and the new conv state.
  */
 GDN_API gdn_status gdn_prefill_fused(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens,
                              const int32_t *cu_seqlens, const void *qkv, const void *beta_logit,
