@@ -734,8 +734,8 @@ __device__ __forceinline__ void mma_2x2(f32x4 (&c)[2][2], const typename Op<P>::
 //   3. all: S <- Gam_n S + K^T diag(k~) D (state rows 16 w) -> S in LDS
 // V of chunk c + 1 goes to LDS in step 2 (it is first read in step 1 of that
 // chunk). The fused form stages each raw V row of the slab in LDS once and
-// takes conv + SiLU from there, half of every thread's channels on each
-// role, in the time the roles would otherwise wait at the third barrier.
+// the x-waves take conv + SiLU from there, in the time they would otherwise
+// wait at the third barrier.
 // S lives in two LDS buffers by chunk parity, so that writing the new S
 // needs no barrier of its own: three barriers per chunk; the two roles run
 // loops of their own (the branch is uniform per wave) with the same
@@ -917,7 +917,8 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
   // first use, so that the loads stay in flight until then.
   // Fused form: conv + SiLU of the staged raw rows (rows t - 3 .. t of row t
   // sit at Vr rows t .. t + 3) of the thread's channels 8 (tid % 4) + 4 h
-  // .. +3: h = 0 on the x-waves, 1 on the y-waves, which share the work.
+  // .. +3, both halves on the x-waves: the y-waves, which form O in the same
+  // interval, arrive at the third barrier later.
 #define GDN_FORM_V(c, h)                                                                             \
   do {                                                                                               \
     Raw raw_[kConvK];                                                                                \
@@ -1043,7 +1044,7 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
       GDN_LOAD_ROWS(fk, k_src0, 0);
       GDN_LOAD_MAT(ft, t_src0, 0);
       GDN_LOAD_VG(0);
-      if constexpr (kFused) GDN_FORM_V(0, 0);
+      if constexpr (kFused) { GDN_FORM_V(0, 0); GDN_FORM_V(0, 1); }
       else GDN_WRITE_V(0);
       GDN_COMMIT_G();
     }
@@ -1084,7 +1085,7 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
         for (int r = 0; r < 4; ++r) ds[r] = acc[ct][r] * ksc_s[16 * rt + acc_row(r)];
         lds_put4<P>(Dsb, 2, 16 * rt + lr, 16 * ct + lc, ds);
       }
-      if constexpr (kFused) GDN_FORM_V(cn, 0);
+      if constexpr (kFused) { GDN_FORM_V(cn, 0); GDN_FORM_V(cn, 1); }
       else GDN_WRITE_V(cn);
       update_state(ci, g_end);
       GDN_COMMIT_G();
@@ -1094,7 +1095,6 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
     if (nchunks > 0) {
       GDN_LOAD_ROWS(fq, q_src0, 0);
       GDN_LOAD_MAT(fp, p_src0, 0);
-      if constexpr (kFused) GDN_FORM_V(0, 1);
     }
     for (int ci = 0; ci < nchunks; ++ci) {
       const int cn = min(ci + 1, nchunks - 1);
@@ -1116,7 +1116,6 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
       for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
         for (int r = 0; r < 4; ++r) oy[ct][r] = G_s[16 * rt + acc_row(r)] * Y[ct][r];
-      if constexpr (kFused) GDN_FORM_V(cn, 1);
       update_state(ci, g_end);
     }
     // O of the last chunk (its D was made visible by the loop's barriers).
