@@ -8,7 +8,10 @@ call gdn_prefill_fused (q, k, v, beta, g computed inside the chunked
 kernels). Each runs as plain launches and as the step captured in a HIP
 graph and replayed; ``value`` is tokens per second over exactly ``--steps``
 timed steps (after ``--warmup`` untimed ones) of the fastest of the four,
-all reported under "prefill_modes".
+all reported under "prefill_modes" with the median and minimum of the
+per-step times (an event pair around every step). "varlen_prefill" times the
+varlen workload (8 packed sequences of 512 .. 8192 tokens, nonzero initial
+states) the same way, fused forms only.
 
 The same run also times the decode path on the batch-1 workload (32 V-heads,
 1024 consecutive steps) and the batch-64 workload (256 steps), and reports
@@ -26,8 +29,11 @@ on the stream the kernels run on:
     logits and the parameters, against 8 TB/s HBM; and the delta-rule
     kernel alone (gdn_decode_step): S read + written, q, k, v, beta, g read,
     o written.
-The CPU baseline is the fp64 oracle, single-threaded, over the whole prefill
-workload once.
+"roofline_fused" prices the same flops against the whole gdn_prefill_fused
+call (events around each call), a lower bound on its chunked kernels' own
+fraction. The CPU baseline is the fp64 oracle over the whole prefill workload
+once, on one thread and with the V-heads split over threads, with the host's
+CPU model and counts.
 
 "block" times the projections around the mixer as well (gdn_in_proj ->
 mixer -> gdn_out_proj) on the 27B prefill layer and the 35B-A3B batch-64
@@ -225,56 +231,89 @@ def write_traffic(dbs):
     print(json.dumps(kernels, indent=1))
 
 
-def bench_prefill(steps: int, warmup: int):
-    w = wl.WORKLOADS[3]
-    x = wl.generate(w)
-    t = {k: dev(v) for k, v in x.items()}
-    cfg = B.make_config(w.n_qk_heads, w.n_v_heads, w.act)
-    T = int(x["cu_seqlens"][-1])
-    run = Lyr.Prefill(cfg, 1, T)
-    conv_out = torch.empty_like(t["conv0"])
-    S_out = torch.empty_like(t["S0"])
-    args = (t["cu_seqlens"], t["qkv"], t["b"], t["a"], t["conv_w"], t["dt_bias"], t["A_log"], t["conv0"], conv_out)
-
-    def step(evs=None):
-        run.prep(*args)
-        if evs is not None:
-            evs[0].record()
-        run.core(t["cu_seqlens"], t["S0"], S_out)
-        if evs is not None:
-            evs[1].record()
-        run.norm(t["z"], t["norm_w"])
-
+def _timed_reps(fn, steps: int, warmup: int):
+    """Run fn `warmup` times untimed, then exactly `steps` times between two
+    events on the current stream (synchronised on both sides), with an event
+    pair around each rep as well. Returns (total ms, [ms per rep])."""
     for _ in range(warmup):
-        step()
-    core_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        fn()
+    evs = _events(steps)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for i in range(steps):
-        step(core_ev[i])
+        evs[i][0].record()
+        fn()
+        evs[i][1].record()
     end.record()
     torch.cuda.synchronize()
-    plain_ms = start.elapsed_time(end)
-    core_ms = float(np.mean([a.elapsed_time(b) for a, b in core_ev]))
-    # The same step captured once as a HIP graph (four kernel nodes, no
-    # memset nodes) and replayed: what a caller that captures its layer gets.
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        step()
-    for _ in range(warmup):
-        g.replay()
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(steps):
-        g.replay()
-    end.record()
-    torch.cuda.synchronize()
-    graph_ms = start.elapsed_time(end)
-    del g
+    return start.elapsed_time(end), [a.elapsed_time(b) for a, b in evs]
+
+
+def _mode_stats(total_ms: float, per: list, steps: int, tokens: int) -> dict:
+    return {"ms_per_step": round(total_ms / steps, 4), "tokens_per_s": round(tokens * steps / (total_ms * 1e-3), 1),
+            "median_ms": round(float(np.median(per)), 4), "min_ms": round(float(np.min(per)), 4)}
+
+
+def _core_roofline(flops: int, ms: float, what: str, traffic_key=None) -> dict:
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+            "traffic": measured_traffic(traffic_key) if traffic_key else None,
+            "kernel": what, "flop_per_launch": flops, "avg_launch_us": round(ms * 1e3, 2)}
+
+
+def bench_prefill(steps: int, warmup: int, wid: int = 3, three_call: bool = True):
+    """One prefill workload, whole mixer per step: the three calls (prep ->
+    chunked -> norm) and the single gdn_prefill_fused call, each plain and as
+    a captured graph (three_call=False: the fused forms only, plus the
+    three-call step once per rep for the chunked call's events)."""
+    w = wl.WORKLOADS[wid]
+    x = wl.generate(w)
+    t = {k: dev(v) for k, v in x.items()}
+    del x
+    cfg = B.make_config(w.n_qk_heads, w.n_v_heads, w.act)
+    N = w.n_seqs
+    lens = w.seq_lengths()
+    T = int(sum(lens))
+    run = Lyr.Prefill(cfg, N, T)
+    conv_out = torch.empty_like(t["conv0"])
+    S_out = torch.empty_like(t["S0"])
+    args = (t["cu_seqlens"], t["qkv"], t["b"], t["a"], t["conv_w"], t["dt_bias"], t["A_log"], t["conv0"], conv_out)
+    core_ev = []
+
+    def step():
+        run.prep(*args)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        run.core(t["cu_seqlens"], t["S0"], S_out)
+        b.record()
+        core_ev.append((a, b))
+        run.norm(t["z"], t["norm_w"])
+
+    modes = {}
+    total, per = _timed_reps(step, steps, warmup)
+    core_ev = core_ev[warmup:]
+    core_per = [a.elapsed_time(b) for a, b in core_ev]
+    core_ms = float(np.mean(core_per))
+    if three_call:
+        modes["plain"] = _mode_stats(total, per, steps, T)
+
+        def plain_step():
+            run.prep(*args)
+            run.core(t["cu_seqlens"], t["S0"], S_out)
+            run.norm(t["z"], t["norm_w"])
+        # The same step captured once as a HIP graph (kernel nodes only, no
+        # memset nodes) and replayed: what a caller that captures its layer gets.
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            plain_step()
+        total, per = _timed_reps(g.replay, steps, warmup)
+        modes["graph"] = _mode_stats(total, per, steps, T)
+        del g
     # The same step as one gdn_prefill_fused call (q, k, v, beta, g computed
     # inside the chunked kernels), plain and as a graph.
-    fused = Lyr.PrefillFused(cfg, 1, T)
+    fused = Lyr.PrefillFused(cfg, N, T)
     conv_f = torch.empty_like(t["conv0"])
     S_f = torch.empty_like(t["S0"])
 
@@ -282,44 +321,34 @@ def bench_prefill(steps: int, warmup: int):
         fused(t["cu_seqlens"], t["qkv"], t["z"], t["b"], t["a"], t["conv_w"], t["dt_bias"], t["A_log"],
               t["norm_w"], t["conv0"], conv_f, t["S0"], S_f)
 
-    for _ in range(warmup):
-        fstep()
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(steps):
-        fstep()
-    end.record()
-    torch.cuda.synchronize()
-    fused_ms = start.elapsed_time(end)
+    total, fper = _timed_reps(fstep, steps, warmup)
+    modes["fused"] = _mode_stats(total, fper, steps, T)
+    fused_call_ms = float(np.mean(fper))
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         fstep()
-    for _ in range(warmup):
-        g.replay()
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(steps):
-        g.replay()
-    end.record()
-    torch.cuda.synchronize()
-    fused_graph_ms = start.elapsed_time(end)
+    total, per = _timed_reps(g.replay, steps, warmup)
+    modes["fused_graph"] = _mode_stats(total, per, steps, T)
     del g
-    modes_ms = {"plain": plain_ms, "graph": graph_ms, "fused": fused_ms, "fused_graph": fused_graph_ms}
-    best = min(modes_ms, key=modes_ms.get)
-    total_ms = modes_ms[best]
-    n_chunk_heads = ((T + CHUNK - 1) // CHUNK) * w.n_v_heads
+    best = min(modes, key=lambda m: modes[m]["ms_per_step"])
+    n_chunk_heads = sum((L + CHUNK - 1) // CHUNK for L in lens) * w.n_v_heads
     flops = FLOP_PER_CHUNK_HEAD * n_chunk_heads
-    achieved = flops / (core_ms * 1e-3) / 1e12
-    return dict(total_ms=total_ms, ms_per_step=total_ms / steps, tokens=T, core_ms=core_ms, best=best,
-                modes={k: {"ms_per_step": round(v / steps, 4), "tokens_per_s": round(T * steps / (v * 1e-3), 1)}
-                       for k, v in modes_ms.items()},
-                roofline={"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
-                          "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-                          "traffic": measured_traffic("prefill_core"),
-                          "kernel": "gdn_prefill_chunked (chunk_local + chunk_state), timed in the three-call "
-                                    "step; the fused step runs the same kernels with the conv folded into "
-                                    "their loads",
-                          "flop_per_launch": flops, "avg_launch_us": round(core_ms * 1e3, 2)})
+    out = dict(workload=w.name, tokens=T, best=best, ms_per_step=modes[best]["ms_per_step"],
+               total_ms=modes[best]["ms_per_step"] * steps, core_ms=core_ms,
+               tokens_per_s=modes[best]["tokens_per_s"], modes=modes,
+               roofline=_core_roofline(flops, core_ms,
+                                       "gdn_prefill_chunked (chunk_local + chunk_state), HIP events around each "
+                                       "call in the three-call step", "prefill_core" if wid == 3 else None),
+               roofline_fused=_core_roofline(
+                   flops, fused_call_ms,
+                   "gdn_prefill_fused, the whole call (the chunked kernels with the conv, SiLU, L2 norm and gates "
+                   "folded in, and the norm launch): HIP events around each call; a lower bound on the chunked "
+                   "kernels' own fraction", None))
+    out["roofline"]["median_launch_us"] = round(float(np.median(core_per)) * 1e3, 2)
+    out["roofline"]["min_launch_us"] = round(float(np.min(core_per)) * 1e3, 2)
+    out["roofline_fused"]["median_launch_us"] = round(float(np.median(fper)) * 1e3, 2)
+    out["roofline_fused"]["min_launch_us"] = round(float(np.min(fper)) * 1e3, 2)
+    return out
 
 
 def _events(n):
@@ -661,7 +690,27 @@ def cpu_baseline(max_threads: int = 16):
     return {"value": round(T / dtn, 2), "unit": "tokens/s", "cores": nt, "kind": "oracle",
             "sample": f"the whole prefill workload once ({T} tokens x {Hv} V-heads), fp64; V-heads split over "
                       f"{nt} threads, {dtn:.2f} s",
+            "host": host_identity(), "threads_used": nt,
             "one_thread": {"value": round(T / dt1, 2), "unit": "tokens/s", "cores": 1, "seconds": round(dt1, 2)}}
+
+
+def host_identity() -> dict:
+    """The CPU the oracle ran on: its model name (/proc/cpuinfo), the logical
+    CPUs the OS reports and those this process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.lower().startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = None
+    return {"model_name": model, "nproc": os.cpu_count(), "affinity_cpus": avail}
 
 
 def main():
@@ -672,6 +721,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the oracle")
     ap.add_argument("--no-block", action="store_true", help="skip the block (projections + mixer)")
+    ap.add_argument("--no-varlen", action="store_true", help="skip the varlen prefill workload")
     ap.add_argument("--only", choices=["prefill", "decode-b1", "decode-b64", "block"], default=None,
                     help="run one workload only (for counter collection)")
     ap.add_argument("--summarize-rocprof", metavar="DB", default=None,
@@ -716,6 +766,12 @@ def main():
     log("prefill workload: T=4096 Hqk=16 Hv=48 bf16")
     pre = bench_prefill(a.steps, a.warmup)
     log(f"prefill: {pre['ms_per_step']:.3f} ms/step ({pre['best']}), core {pre['core_ms'] * 1e3:.1f} us; " + json.dumps(pre['modes']))
+    varlen = None
+    if not a.no_varlen and a.only is None:
+        log("varlen prefill workload: 8 sequences, L ~ U[512, 8192], nonzero states")
+        varlen = bench_prefill(a.steps, a.warmup, wid=5, three_call=False)
+        log(json.dumps(varlen))
+        torch.cuda.empty_cache()
     decode = None
     if not a.no_decode and a.only is None:
         decode = []
@@ -745,6 +801,8 @@ def main():
         "prefill_modes": pre["modes"],
         "prefill_best_mode": pre["best"],
         "roofline": pre["roofline"],
+        "roofline_fused": pre["roofline_fused"],
+        "varlen_prefill": varlen,
         "decode": decode,
         "block": block,
         "cpu_baseline": cpu,

@@ -59,6 +59,19 @@ gdn_status launched(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_E_HIP;
 
 bool aligned(const void *p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
 
+// Alignment a pointer needs for the widest vector access a kernel makes
+// through it (null pointers are checked elsewhere and pass here).
+struct Align {
+  const void *p;
+  size_t a;
+};
+template <size_t N>
+bool all_aligned(const Align (&v)[N]) {
+  for (size_t i = 0; i < N; ++i)
+    if (!aligned(v[i].p, v[i].a)) return false;
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -106,6 +119,11 @@ gdn_status gdn_conv_gate_prep(const gdn_config *cfg, int32_t n_seqs, int32_t n_t
   const int Hqk = cfg->n_qk_heads, Hv = cfg->n_v_heads;
   const size_t C = static_cast<size_t>(kHeadDim) * (2 * Hqk + Hv);
   const size_t T = static_cast<size_t>(n_tokens), as = act_size(cfg);
+  // Pairs of channels per access (qkv, conv states, q, k, v), four taps per
+  // channel (conv_w).
+  const Align al[] = {{qkv, 2 * as}, {conv_state_in, 2 * as}, {conv_state_out, 2 * as}, {conv_w, 16},
+                      {q, 8}, {k, 8}, {v, 8}};
+  if (!all_aligned(al)) return GDN_E_INVALID_ARG;
   const int tile = gdn::prep_tile(n_seqs, n_tokens);
   const int64_t tiles = (static_cast<int64_t>(n_tokens) + tile - 1) / tile + n_seqs;
   if (tiles > kMaxGrid) return GDN_E_UNSUPPORTED;
@@ -166,6 +184,9 @@ gdn_status gdn_prefill_chunked_ckpt(const gdn_config *cfg, int32_t n_seqs, int32
   const bool ckpt = ckpt_every > 0 && ckpt_cap > 0;
   if (ckpt && !S_ckpt) return GDN_E_INVALID_ARG;
   const int Hqk = cfg->n_qk_heads, Hv = cfg->n_v_heads;
+  // q, k, v rows are read 4 floats at a time; o is written 4 values at a time.
+  const Align al[] = {{q, 16}, {k, 16}, {v, 16}, {o, 4 * act_size(cfg)}};
+  if (!all_aligned(al)) return GDN_E_INVALID_ARG;
   const size_t need = gdn_prefill_workspace_bytes(cfg, n_seqs, n_tokens);
   if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_E_WORKSPACE;
   const int64_t chunks = gdn::max_chunks(n_seqs, n_tokens);
@@ -247,9 +268,11 @@ gdn_status gdn_prefill_fused(const gdn_config *cfg, int32_t n_seqs, int32_t n_to
       !S_out)
     return GDN_E_INVALID_ARG;
   if (n_tokens > 0 && (!qkv || !beta_logit || !alpha_logit || !z || !y)) return GDN_E_INVALID_ARG;
-  // The chunk kernels read qkv and the conv state 8 or 16 bytes at a time.
-  if (!aligned(qkv, 16) || !aligned(conv_state_in, 16) || !aligned(conv_state_out, 16) || !aligned(conv_w, 16))
-    return GDN_E_INVALID_ARG;
+  // The chunk kernels read qkv and the conv state 16 bytes at a time; the
+  // norm reads o and z and writes y 16 bytes at a time.
+  const Align al[] = {{qkv, 16}, {conv_state_in, 16}, {conv_state_out, 16}, {conv_w, 16},
+                      {z, 16}, {y, 16}, {norm_w, 16}};
+  if (!all_aligned(al)) return GDN_E_INVALID_ARG;
   const int Hqk = cfg->n_qk_heads, Hv = cfg->n_v_heads;
   const size_t need = gdn_prefill_fused_workspace_bytes(cfg, n_seqs, n_tokens);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return GDN_E_WORKSPACE;
@@ -336,6 +359,8 @@ gdn_status gdn_conv_state_ckpt(const gdn_config *cfg, int32_t n_seqs, int32_t n_
   if (static_cast<int64_t>(n_seqs) * ckpt_cap > kMaxGrid) return GDN_E_UNSUPPORTED;
   const int Hqk = cfg->n_qk_heads, Hv = cfg->n_v_heads;
   const size_t as = act_size(cfg), C = static_cast<size_t>(kHeadDim) * (2 * Hqk + Hv);
+  const Align al[] = {{qkv, 2 * as}, {conv_state_in, 2 * as}, {conv_ckpt, 2 * as}};
+  if (!all_aligned(al)) return GDN_E_INVALID_ARG;
   const size_t st = static_cast<size_t>(n_seqs) * (gdn::kConvK - 1) * C * as;
   const Range outs[] = {{conv_ckpt, static_cast<size_t>(n_seqs) * ckpt_cap * (gdn::kConvK - 1) * C * as}};
   const Range ins[] = {{qkv, static_cast<size_t>(n_tokens) * C * as}, {conv_state_in, st},
@@ -371,6 +396,9 @@ gdn_status gdn_decode_step(const gdn_config *cfg, int32_t n_seqs, const float *q
   if (n_seqs < 0) return GDN_E_INVALID_ARG;
   if (n_seqs == 0) return GDN_OK;
   if (!q || !k || !v || !beta || !g || !S_in || !S_out || !o) return GDN_E_INVALID_ARG;
+  // State, q, k, v read 4 floats at a time; o written 4 values at a time.
+  const Align al[] = {{S_in, 16}, {S_out, 16}, {q, 16}, {k, 16}, {v, 16}, {o, 4 * act_size(cfg)}};
+  if (!all_aligned(al)) return GDN_E_INVALID_ARG;
   const int Hqk = cfg->n_qk_heads, Hv = cfg->n_v_heads;
   if (static_cast<int64_t>(n_seqs) * Hv * (kHeadDim / 32) > kMaxGrid) return GDN_E_UNSUPPORTED;
   const size_t N = static_cast<size_t>(n_seqs);
@@ -511,6 +539,14 @@ gdn_status decode_tokens(const gdn_config *cfg, int32_t n_seqs, int32_t K, const
   if (!qkv || !beta_logit || !alpha_logit || !z || !conv_w || !dt_bias || !A_log || !norm_w ||
       !conv_state_in || !conv_snap || !S_in || !S_snap || !y)
     return GDN_E_INVALID_ARG;
+  {
+    // State, norm weights and conv taps 16 bytes at a time; z and y four
+    // values, qkv and the conv states two values at a time.
+    const size_t as = act_size(cfg);
+    const Align al[] = {{S_in, 16}, {S_snap, 16}, {norm_w, 16}, {conv_w, 16}, {z, 4 * as}, {y, 4 * as},
+                        {qkv, 2 * as}, {conv_state_in, 2 * as}, {conv_snap, 2 * as}};
+    if (!all_aligned(al)) return GDN_E_INVALID_ARG;
+  }
   const int Hqk = cfg->n_qk_heads, Hv = cfg->n_v_heads;
   if (static_cast<int64_t>(n_seqs) * Hv > kMaxGrid) return GDN_E_UNSUPPORTED;
   const size_t N = static_cast<size_t>(n_seqs), NK = N * static_cast<size_t>(K), as = act_size(cfg);
@@ -580,6 +616,9 @@ gdn_status gdn_gated_rmsnorm(const gdn_config *cfg, int64_t n_rows, const void *
   if (n_rows < 0) return GDN_E_INVALID_ARG;
   if (n_rows == 0) return GDN_OK;
   if (!o || !z || !norm_w || !y) return GDN_E_INVALID_ARG;
+  // Eight values of o, z, y and four weights per access: 16 bytes.
+  const Align al[] = {{o, 16}, {z, 16}, {y, 16}, {norm_w, 16}};
+  if (!all_aligned(al)) return GDN_E_INVALID_ARG;
   if ((n_rows + 15) / 16 > kMaxGrid) return GDN_E_UNSUPPORTED;
   const size_t bytes = static_cast<size_t>(n_rows) * kHeadDim * act_size(cfg);
   // y may be o (in place); nothing else may overlap y.

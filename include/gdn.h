@@ -103,8 +103,11 @@ typedef struct {
 GDN_API gdn_config gdn_default_config(int32_t n_qk_heads, int32_t n_v_heads, gdn_dtype act);
 
 /*
- * gdn_conv_gate_prep -- the steps before the delta rule (the page's gated
- * DeltaNet paragraph, up to the gates):
+ * gdn_conv_gate_prep -- the steps before the delta rule (the xwen CLAUDE.md
+ * page, section "Architecture cheat sheet", gated DeltaNet paragraph, up to
+ * the gates; the epsilon 1e-6 from the same section, the tiled V-head order
+ * and ssm_a = -exp(A_log) from its section "GGUF facts that differ from the
+ * HF checkpoint"):
  *   causal depthwise conv over all C fused channels, kernel 4, no bias, with
  *   the 3 rows of conv_state_in as left context of each sequence;
  *   SiLU over all C channels; split into q | k | v;
@@ -116,6 +119,9 @@ GDN_API gdn_config gdn_default_config(int32_t n_qk_heads, int32_t n_v_heads, gdn
  * conv_state_out may equal conv_state_in (in-place update). No other
  * buffers may overlap. n_tokens may be 0 (only the state copy runs).
  * Decode is the case n_tokens == n_seqs with cu_seqlens = {0, 1, ..., N}.
+ * Alignment: conv_w 16 bytes; qkv and both conv states two activation
+ * values (4 bytes bf16, 8 bytes fp32); q, k, v 8 bytes. A misaligned
+ * pointer is GDN_E_INVALID_ARG.
  */
 GDN_API gdn_status gdn_conv_gate_prep(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens,
                               const int32_t *cu_seqlens,
@@ -128,13 +134,17 @@ GDN_API gdn_status gdn_conv_gate_prep(const gdn_config *cfg, int32_t n_seqs, int
 /*
  * gdn_prefill_chunked -- the delta rule over packed sequences in its chunked
  * form (chunks of 64 tokens counted from each sequence's first token; the
- * page names chunk 64 in its section "Ground truth, in order of authority").
+ * xwen CLAUDE.md page names chunk 64 in its section "Ground truth, in order
+ * of authority", and gives the recurrent step this form rewrites exactly in
+ * its section "Architecture cheat sheet", gated DeltaNet paragraph).
  * Per sequence n and V-head j it produces the same result as the recurrent
  * step of gdn_decode_step applied token by token from S_in[n][j]:
  *   o[t][j] = readout after each token, S_out[n][j] = state after the last.
  * S_out may equal S_in. `workspace` is device scratch of at least
  * gdn_prefill_workspace_bytes(cfg, n_seqs, n_tokens) bytes (may be NULL
  * when that size is 0); it holds no result between calls.
+ * Alignment: q, k, v 16 bytes; o four activation values (8 bytes bf16,
+ * 16 bytes fp32).
  */
 GDN_API gdn_status gdn_prefill_chunked(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens,
                                const int32_t *cu_seqlens,
@@ -151,7 +161,11 @@ GDN_API gdn_status gdn_prefill_chunked(const gdn_config *cfg, int32_t n_seqs, in
  * the sequence (or at its end) with c < ckpt_cap; other planes are left
  * untouched. ckpt_every must be a multiple of the chunk length 64 (0, or
  * ckpt_cap = 0, writes no checkpoint). o and S_out are the same as without
- * checkpoints. S_ckpt must not overlap any other buffer.
+ * checkpoints. S_ckpt must not overlap any other buffer. Alignment as for
+ * gdn_prefill_chunked. Prefix-cache snapshots that carry the recurrent
+ * state are named in the xwen CLAUDE.md page's section "serve"; the
+ * serverAppConfigs commit log describes GDN states checkpointed once per
+ * block of tokens and re-seeded from there, one of which went non-finite.
  */
 GDN_API gdn_status gdn_prefill_chunked_ckpt(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens,
                                const int32_t *cu_seqlens, const float *q, const float *k, const float *v,
@@ -165,6 +179,7 @@ GDN_API gdn_status gdn_prefill_chunked_ckpt(const gdn_config *cfg, int32_t n_seq
  * [conv_state_in[n]; its qkv rows] before token (c + 1) * ckpt_every, copied
  * bit for bit (the conv state a call resuming there needs), for every such
  * token inside the sequence or at its end, c < ckpt_cap. ckpt_every >= 1.
+ * Alignment: qkv, conv_state_in and conv_ckpt two activation values.
  */
 GDN_API gdn_status gdn_conv_state_ckpt(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens,
                                const int32_t *cu_seqlens, const void *qkv, const void *conv_state_in,
@@ -195,7 +210,8 @@ GDN_API gdn_status gdn_state_check(const float *S, int64_t n_values, int32_t *st
  * qkv, conv_w and both conv states must be 16-byte aligned; `workspace`
  * 256-byte aligned, of gdn_prefill_fused_workspace_bytes(cfg, n_seqs,
  * n_tokens) bytes (may be NULL when that is 0). Three kernels on `stream`; the last
- * writes y and the new conv state.
+ * writes y and the new conv state. z, y and norm_w must be 16-byte aligned
+ * too.
  */
 GDN_API gdn_status gdn_prefill_fused(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens,
                              const int32_t *cu_seqlens, const void *qkv, const void *beta_logit,
@@ -213,10 +229,13 @@ GDN_API size_t gdn_prefill_workspace_bytes(const gdn_config *cfg, int32_t n_seqs
 /*
  * gdn_decode_step -- one recurrent step of the delta rule for n_seqs
  * sequences of one token each (inputs laid out with T = n_seqs). Per sequence
- * n and V-head j (the page's recurrent step, in its order):
+ * n and V-head j, the recurrent step of the xwen CLAUDE.md page (section
+ * "Architecture cheat sheet", gated DeltaNet paragraph), in its order:
  *   S <- exp(g) * S;  delta = beta * (v - S.k);  S <- S + k (x) delta;
  *   o = (S . q) / sqrt(head_dim)   (read from the updated state)
- * S_out may equal S_in (in-place update).
+ * with S [128 key][128 value] fp32 per (sequence, V-head) and V-head j
+ * reading q, k of K-head j mod Hqk. S_out may equal S_in (in-place update).
+ * Alignment: S_in, S_out, q, k, v 16 bytes; o four activation values.
  */
 GDN_API gdn_status gdn_decode_step(const gdn_config *cfg, int32_t n_seqs,
                            const float *q, const float *k, const float *v,
@@ -237,7 +256,8 @@ GDN_API gdn_status gdn_decode_step(const gdn_config *cfg, int32_t n_seqs,
  *     (blocks of the step read channels of the old state that other blocks
  *     write), so a caller alternates two buffers.
  *   S_in, S_out [N][Hv][d][d]: fp32; S_out may equal S_in.
- * n_seqs may be 0.
+ * n_seqs may be 0. Alignment: S_in, S_out, norm_w, conv_w 16 bytes; z, y
+ * four activation values; qkv and the conv states two.
  */
 GDN_API gdn_status gdn_decode_fused(const gdn_config *cfg, int32_t n_seqs, const void *qkv,
                             const void *beta_logit, const void *alpha_logit, const void *z,
@@ -261,7 +281,9 @@ GDN_API gdn_status gdn_decode_fused(const gdn_config *cfg, int32_t n_seqs, const
  *   S_in [N][Hv][d][d]                the state before the first token
  *   S_snap [N][K][Hv][d][d]           plane p = S after token K-1-p
  * conv_snap must not overlap conv_state_in; S_snap must not overlap S_in
- * (K = 1 may update S in place). n_seqs or n_tokens may be 0.
+ * (K = 1 may update S in place). n_seqs or n_tokens may be 0. Alignment as
+ * for gdn_decode_fused (S_snap and conv_snap in place of S_out and
+ * conv_state_out).
  */
 GDN_API gdn_status gdn_decode_verify(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens, const void *qkv,
                              const void *beta_logit, const void *alpha_logit, const void *z,
@@ -270,10 +292,16 @@ GDN_API gdn_status gdn_decode_verify(const gdn_config *cfg, int32_t n_seqs, int3
                              const float *S_in, float *S_snap, void *y, gdn_stream_t stream);
 
 /*
- * gdn_gated_rmsnorm -- per row of d values (n_rows = T * Hv):
+ * gdn_gated_rmsnorm -- the gated RMSNorm that ends the mixer (the xwen
+ * CLAUDE.md page, section "Architecture cheat sheet", gated DeltaNet
+ * paragraph: normalise, multiply by ssm_norm.weight [128], then by silu(z);
+ * the epsilon 1e-6 from the same section; the weight used as stored, without
+ * +1, from its section "GGUF facts that differ from the HF checkpoint"). Per
+ * row of d values (n_rows = T * Hv, one row per token and V-head):
  *   y = o / sqrt(mean(o^2) + norm_eps) * norm_w * silu(z)
- * with norm_w [d] fp32 shared by all heads and used as stored (no +1).
- * y may equal o (in place). n_rows may be 0.
+ * with norm_w [d] fp32 shared by all heads. y may equal o (in place); no
+ * other buffers may overlap. n_rows may be 0. Alignment: o, z, y and norm_w
+ * 16 bytes.
  */
 GDN_API gdn_status gdn_gated_rmsnorm(const gdn_config *cfg, int64_t n_rows, const void *o, const void *z,
                              const float *norm_w, void *y, gdn_stream_t stream);

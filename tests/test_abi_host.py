@@ -128,7 +128,7 @@ def test_prep_and_norm_validation(lib):
     assert lib.gdn_gated_rmsnorm(ctypes.byref(cfg), -1, *FAKE[:4], None) == B.GDN_E_INVALID_ARG
     assert lib.gdn_gated_rmsnorm(ctypes.byref(cfg), 4, None, *FAKE[1:4], None) == B.GDN_E_INVALID_ARG
     yz = FAKE[:4]
-    yz = [yz[0], yz[1], yz[2], yz[1] + 8]   # y overlapping z
+    yz = [yz[0], yz[1], yz[2], yz[1] + 16]   # y overlapping z
     assert lib.gdn_gated_rmsnorm(ctypes.byref(cfg), 4, *yz, None) == B.GDN_E_INVALID_ARG
 
 
@@ -262,3 +262,54 @@ def test_prefill_fused_validation(lib):
     assert call(100, q) == B.GDN_E_INVALID_ARG
     assert call(5, p, need, n=0) == B.GDN_E_INVALID_ARG     # tokens without sequences
     assert call(0, p, 0, n=0) == B.GDN_OK
+
+
+def test_misaligned_vector_pointers_are_rejected(lib):
+    """Every pointer a kernel reads or writes with vector accesses must meet
+    the alignment gdn.h states for it; an offset pointer is GDN_E_INVALID_ARG
+    (and nothing is launched)."""
+    cfg = B.make_config(2, 4, "bf16")
+    f32 = B.make_config(2, 4, "f32")
+    # gdn_gated_rmsnorm: o, z, y, norm_w 16 bytes.
+    for i in range(4):
+        p = FAKE[:4]
+        p[i] += 8
+        assert lib.gdn_gated_rmsnorm(ctypes.byref(cfg), 4, *p, None) == B.GDN_E_INVALID_ARG, i
+    # gdn_decode_step: q, k, v, S_in, S_out 16 bytes; o 4 values (8 bytes bf16, 16 fp32).
+    for i, off in ((0, 8), (1, 8), (2, 8), (5, 8), (6, 8), (7, 4)):
+        p = FAKE[:8]
+        p[i] += off
+        assert _decode(lib, cfg, 1, p) == B.GDN_E_INVALID_ARG, i
+    p = FAKE[:8]
+    p[7] += 8
+    assert _decode(lib, f32, 1, p) == B.GDN_E_INVALID_ARG
+    # gdn_decode_fused: S_in, S_out, norm_w, conv_w 16 bytes; z, y 4 values; qkv, conv states 2 values.
+    for i, off in ((10, 8), (11, 8), (7, 8), (4, 8), (3, 4), (12, 4), (0, 2), (8, 2), (9, 2)):
+        p = FAKE[:13]
+        p[i] += off
+        assert lib.gdn_decode_fused(ctypes.byref(cfg), 1, *p, None) == B.GDN_E_INVALID_ARG, i
+    # gdn_decode_verify: the same pointers.
+    p = FAKE[:13]
+    p[11] += 8
+    assert lib.gdn_decode_verify(ctypes.byref(cfg), 1, 2, *p, None) == B.GDN_E_INVALID_ARG
+    # gdn_conv_gate_prep: conv_w 16; qkv and conv states 2 values; q, k, v 8 bytes.
+    for i, off in ((4, 8), (1, 2), (7, 2), (8, 2), (9, 4), (10, 4), (11, 4)):
+        p = FAKE[:14]
+        p[i] += off
+        assert lib.gdn_conv_gate_prep(ctypes.byref(cfg), 1, 4, *p, None) == B.GDN_E_INVALID_ARG, i
+    # gdn_prefill_chunked: q, k, v 16 bytes; o 4 values.
+    need = B.gdn_prefill_workspace_bytes(cfg, 1, 100)
+    for i, off in ((1, 8), (2, 8), (3, 8), (8, 4)):
+        p = FAKE[:9]
+        p[i] += off
+        assert lib.gdn_prefill_chunked(ctypes.byref(cfg), 1, 100, *p, FAKE[10], need, None) == B.GDN_E_INVALID_ARG, i
+    # gdn_prefill_fused: z, y, norm_w 16 bytes too.
+    need = B.gdn_prefill_fused_workspace_bytes(cfg, 2, 100)
+    for i in (3, 7, 12):
+        p = FAKE[:14]
+        p[i] += 8
+        assert lib.gdn_prefill_fused(ctypes.byref(cfg), 2, 100, FAKE[15], *p, need, None) == B.GDN_E_INVALID_ARG, i
+    # gdn_conv_state_ckpt: qkv, conv_state_in, conv_ckpt 2 values.
+    c = (ctypes.byref(cfg), 1, 200)
+    assert lib.gdn_conv_state_ckpt(*c, FAKE[0], FAKE[1] + 2, FAKE[2], 5, 2, FAKE[3], None) == B.GDN_E_INVALID_ARG
+    assert lib.gdn_conv_state_ckpt(*c, FAKE[0], FAKE[1], FAKE[2], 5, 2, FAKE[3] + 2, None) == B.GDN_E_INVALID_ARG
