@@ -21,7 +21,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn.so")
 
-GDN_OK, GDN_E_INVALID_ARG, GDN_E_UNSUPPORTED, GDN_E_HIP, GDN_E_WORKSPACE = 0, 1, 2, 3, 4
+GDN_OK, GDN_E_INVALID_ARG, GDN_E_UNSUPPORTED, GDN_E_HIP, GDN_E_WORKSPACE, GDN_E_TOO_LARGE = 0, 1, 2, 3, 4, 5
+GDN_STATIC_SCRATCH_BYTES = 256 << 20   # the static scratch of gdn_prefill_fused_static (gdn.h)
 GDN_F32, GDN_BF16 = 0, 1
 GDN_L2_CLAMP, GDN_L2_RSQRT = 0, 1
 HEAD_DIM = 128
@@ -32,7 +33,7 @@ EXPORTS = ("gdn_default_config", "gdn_conv_gate_prep", "gdn_prefill_chunked",
            "gdn_prefill_workspace_bytes", "gdn_decode_step", "gdn_decode_fused", "gdn_decode_verify",
            "gdn_gated_rmsnorm", "gdn_prefill_chunked_ckpt", "gdn_conv_state_ckpt", "gdn_state_check",
            "gdn_in_proj", "gdn_out_proj", "gdn_prefill_fused", "gdn_prefill_fused_workspace_bytes",
-           "gdn_status_string", "gdn_version")
+           "gdn_status_string", "gdn_version", "gdn_prefill_fused_static")
 
 
 class GdnError(RuntimeError):
@@ -90,6 +91,8 @@ def load(path: Optional[str] = None):
     lib.gdn_decode_verify.restype = ctypes.c_int
     lib.gdn_prefill_fused.argtypes = [cfgp, ctypes.c_int32, ctypes.c_int32] + [_P] * 15 + [ctypes.c_size_t, _P]
     lib.gdn_prefill_fused.restype = ctypes.c_int
+    lib.gdn_prefill_fused_static.argtypes = [cfgp, ctypes.c_int32, ctypes.c_int32] + [_P] * 15
+    lib.gdn_prefill_fused_static.restype = ctypes.c_int
     lib.gdn_prefill_fused_workspace_bytes.argtypes = [cfgp, ctypes.c_int32, ctypes.c_int32]
     lib.gdn_prefill_fused_workspace_bytes.restype = ctypes.c_size_t
     lib.gdn_in_proj.argtypes = [cfgp, ctypes.c_int32, ctypes.c_int32] + [_P] * 9 + [_P]
@@ -298,6 +301,26 @@ def gdn_prefill_fused(cfg: gdn_config, n_seqs: int, n_tokens: int, cu_seqlens, q
     _check("gdn_prefill_fused", s)
 
 
+def gdn_prefill_fused_static(cfg: gdn_config, n_seqs: int, n_tokens: int, cu_seqlens, qkv, beta_logit, alpha_logit,
+                             z, conv_w, dt_bias, A_log, norm_w, conv_state_in, conv_state_out, S_in, S_out, y,
+                             stream=None):
+    """gdn_prefill_fused with the library's static device scratch as its
+    workspace: allocates nothing (GdnError with GDN_E_TOO_LARGE when the call
+    needs more than GDN_STATIC_SCRATCH_BYTES)."""
+    Hqk, Hv, d, N, T = cfg.n_qk_heads, cfg.n_v_heads, cfg.head_dim, n_seqs, n_tokens
+    C, ad = d * (2 * Hqk + Hv), _act_dtype(cfg)
+    s = load().gdn_prefill_fused_static(
+        ctypes.byref(cfg), N, T, _ptr(cu_seqlens, "cu_seqlens", torch.int32, N + 1), _ptr(qkv, "qkv", ad, T * C),
+        _ptr(beta_logit, "beta_logit", ad, T * Hv), _ptr(alpha_logit, "alpha_logit", ad, T * Hv),
+        _ptr(z, "z", ad, T * Hv * d), _ptr(conv_w, "conv_w", torch.float32, C * CONV_K),
+        _ptr(dt_bias, "dt_bias", torch.float32, Hv), _ptr(A_log, "A_log", torch.float32, Hv),
+        _ptr(norm_w, "norm_w", torch.float32, d), _ptr(conv_state_in, "conv_state_in", ad, N * (CONV_K - 1) * C),
+        _ptr(conv_state_out, "conv_state_out", ad, N * (CONV_K - 1) * C),
+        _ptr(S_in, "S_in", torch.float32, N * Hv * d * d), _ptr(S_out, "S_out", torch.float32, N * Hv * d * d),
+        _ptr(y, "y", ad, T * Hv * d), _stream(stream))
+    _check("gdn_prefill_fused_static", s)
+
+
 def gdn_in_proj(cfg: gdn_config, n_tokens: int, hidden: int, x, w_qkv, w_gate, w_beta, w_alpha, qkv, z,
                 beta_logit, alpha_logit, stream=None):
     Hqk, Hv, d, T, bf = cfg.n_qk_heads, cfg.n_v_heads, cfg.head_dim, n_tokens, torch.bfloat16
@@ -322,4 +345,5 @@ __all__ = ["load", "make_config", "gdn_config", "GdnError", "status_string", "EX
            "gdn_conv_gate_prep", "gdn_prefill_chunked", "gdn_prefill_workspace_bytes",
            "gdn_decode_step", "gdn_decode_fused", "gdn_decode_verify", "gdn_gated_rmsnorm",
            "gdn_prefill_chunked_ckpt", "gdn_conv_state_ckpt", "gdn_state_check", "gdn_in_proj",
-           "gdn_out_proj", "gdn_prefill_fused", "gdn_prefill_fused_workspace_bytes", "GDN_F32", "GDN_BF16"]
+           "gdn_out_proj", "gdn_prefill_fused", "gdn_prefill_fused_workspace_bytes", "gdn_prefill_fused_static",
+           "GDN_F32", "GDN_BF16", "GDN_STATIC_SCRATCH_BYTES"]

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "gdn.h"
 #include "gdn_internal.h"
 
@@ -96,6 +98,7 @@ const char *gdn_status_string(gdn_status s) {
     case GDN_E_UNSUPPORTED: return "unsupported configuration";
     case GDN_E_HIP: return "HIP launch or runtime error";
     case GDN_E_WORKSPACE: return "workspace missing or too small";
+    case GDN_E_TOO_LARGE: return "the call needs more scratch than the static scratch holds (split the tokens over calls)";
   }
   return "unknown status";
 }
@@ -632,6 +635,71 @@ gdn_status gdn_gated_rmsnorm(const gdn_config *cfg, int64_t n_rows, const void *
   p.y = y;
   p.eps = cfg->norm_eps;
   return launched(gdn::launch_norm(p, cfg->act_dtype, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// gdn_prefill_fused_static: gdn_prefill_fused with its workspace in a
+// file-scope device array instead of a caller buffer, for callers that cannot
+// allocate. Each device that runs it holds its own copy of the array from the
+// time the library's code is loaded there until the process ends. In host code
+// `scratch` is only a stand-in: its device address, which differs per device,
+// is looked up once per device with hipGetSymbolAddress (with that device
+// current) and kept in scratch_ptr, and only that address is ever handed to a
+// kernel.
+namespace {
+
+constexpr size_t kStaticScratchBytes = static_cast<size_t>(GDN_STATIC_SCRATCH_BYTES);
+__device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch (looked up on first use).
+gdn_status static_scratch(hipStream_t stream, void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return GDN_E_HIP;
+  if (stream) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return GDN_E_HIP;
+    if (sdev != dev) return GDN_E_INVALID_ARG;   // the stream must belong to the current device
+  }
+  if (dev < 0 || dev >= kMaxDevices) return GDN_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GDN_E_HIP;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_prefill_fused_static(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens,
+                                    const int32_t *cu_seqlens, const void *qkv, const void *beta_logit,
+                                    const void *alpha_logit, const void *z, const float *conv_w,
+                                    const float *dt_bias, const float *A_log, const float *norm_w,
+                                    const void *conv_state_in, void *conv_state_out, const float *S_in,
+                                    float *S_out, void *y, gdn_stream_t stream) {
+  const gdn_status cs = check_config(cfg);
+  if (cs != GDN_OK) return cs;
+  if (n_seqs < 0 || n_tokens < 0) return GDN_E_INVALID_ARG;
+  const size_t need = gdn_prefill_fused_workspace_bytes(cfg, n_seqs, n_tokens);
+  if (need > kStaticScratchBytes) return GDN_E_TOO_LARGE;
+  void *ws = nullptr;
+  if (need > 0) {
+    const gdn_status ss = static_scratch(static_cast<hipStream_t>(stream), &ws);
+    if (ss != GDN_OK) return ss;
+  }
+  return gdn_prefill_fused(cfg, n_seqs, n_tokens, cu_seqlens, qkv, beta_logit, alpha_logit, z, conv_w, dt_bias,
+                           A_log, norm_w, conv_state_in, conv_state_out, S_in, S_out, y, ws,
+                           need > 0 ? kStaticScratchBytes : 0, stream);
 }
 
 }  // extern "C"

@@ -75,7 +75,8 @@ typedef enum {
     GDN_E_INVALID_ARG = 1,   /* null pointer, bad size or count, aliasing not allowed */
     GDN_E_UNSUPPORTED = 2,   /* a configuration this build does not implement */
     GDN_E_HIP = 3,           /* a HIP runtime call or kernel launch failed */
-    GDN_E_WORKSPACE = 4      /* workspace missing or smaller than required */
+    GDN_E_WORKSPACE = 4,     /* workspace missing or smaller than required */
+    GDN_E_TOO_LARGE = 5      /* more scratch needed than gdn_prefill_fused_static holds */
 } gdn_status;
 
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
@@ -219,6 +220,38 @@ GDN_API gdn_status gdn_prefill_fused(const gdn_config *cfg, int32_t n_seqs, int3
                              const float *A_log, const float *norm_w, const void *conv_state_in,
                              void *conv_state_out, const float *S_in, float *S_out, void *y,
                              void *workspace, size_t workspace_bytes, gdn_stream_t stream);
+
+/*
+ * gdn_prefill_fused_static -- gdn_prefill_fused without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc). Same
+ * arguments, arithmetic, outputs, alignment and aliasing rules as
+ * gdn_prefill_fused, minus `workspace` and `workspace_bytes`.
+ *
+ * Its workspace is a static device array of GDN_STATIC_SCRATCH_BYTES
+ * (256 MiB) in the library, one per device, which each device that loads the
+ * library's code holds until the process ends. The call allocates nothing:
+ * no hipMalloc, no hipFree, no allocating library routine. Its first call on
+ * a device looks up that device's array (the stream, if not NULL, must belong
+ * to the current device, else GDN_E_INVALID_ARG).
+ *
+ * Limit: gdn_prefill_fused_workspace_bytes(cfg, n_seqs, n_tokens) must not
+ * exceed GDN_STATIC_SCRATCH_BYTES, else GDN_E_TOO_LARGE and nothing is
+ * launched. For 16 K-heads and 48 V-heads in bf16 that admits one sequence of
+ * up to 4,928 tokens (the 4,096-token prefill fits); a longer prefill
+ * is split over calls, since the conv and delta states carry it across.
+ *
+ * Every call on a device shares that device's array and nothing in it
+ * survives a call, so calls that overlap in time on one device (different
+ * streams, or host threads) race and corrupt each other: serialise them.
+ */
+GDN_API gdn_status gdn_prefill_fused_static(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens,
+                                    const int32_t *cu_seqlens, const void *qkv, const void *beta_logit,
+                                    const void *alpha_logit, const void *z, const float *conv_w,
+                                    const float *dt_bias, const float *A_log, const float *norm_w,
+                                    const void *conv_state_in, void *conv_state_out, const float *S_in,
+                                    float *S_out, void *y, gdn_stream_t stream);
+#define GDN_STATIC_SCRATCH_BYTES (256u * 1024u * 1024u)
 
 /* Workspace size gdn_prefill_fused needs for these sizes (0 for a bad cfg). */
 GDN_API size_t gdn_prefill_fused_workspace_bytes(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens);

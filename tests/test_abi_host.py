@@ -313,3 +313,20 @@ def test_misaligned_vector_pointers_are_rejected(lib):
     c = (ctypes.byref(cfg), 1, 200)
     assert lib.gdn_conv_state_ckpt(*c, FAKE[0], FAKE[1] + 2, FAKE[2], 5, 2, FAKE[3], None) == B.GDN_E_INVALID_ARG
     assert lib.gdn_conv_state_ckpt(*c, FAKE[0], FAKE[1], FAKE[2], 5, 2, FAKE[3] + 2, None) == B.GDN_E_INVALID_ARG
+
+
+def test_static_scratch_entry_point_limits(lib):
+    """gdn_prefill_fused_static checks its size against the static scratch
+    before touching the device: an oversize call is GDN_E_TOO_LARGE, a bad
+    config or count is rejected as in gdn_prefill_fused, an empty call is a
+    no-op."""
+    cfg = B.make_config(16, 48, "bf16")
+    p = FAKE[:15]
+    call = lambda n, t, c=cfg: lib.gdn_prefill_fused_static(ctypes.byref(c), n, t, *p, None)
+    assert B.gdn_prefill_fused_workspace_bytes(cfg, 1, 4096) <= B.GDN_STATIC_SCRATCH_BYTES
+    assert B.gdn_prefill_fused_workspace_bytes(cfg, 1, 8192) > B.GDN_STATIC_SCRATCH_BYTES
+    assert call(1, 8192) == B.GDN_E_TOO_LARGE
+    assert call(-1, 10) == B.GDN_E_INVALID_ARG
+    assert call(1, 64, B.make_config(16, 48, head_dim=64)) == B.GDN_E_UNSUPPORTED
+    assert call(0, 0) == B.GDN_OK
+    assert "static scratch" in B.status_string(B.GDN_E_TOO_LARGE)
