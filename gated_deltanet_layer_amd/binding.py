@@ -33,7 +33,7 @@ EXPORTS = ("gdn_default_config", "gdn_conv_gate_prep", "gdn_prefill_chunked",
            "gdn_prefill_workspace_bytes", "gdn_decode_step", "gdn_decode_fused", "gdn_decode_verify",
            "gdn_gated_rmsnorm", "gdn_prefill_chunked_ckpt", "gdn_conv_state_ckpt", "gdn_state_check",
            "gdn_in_proj", "gdn_out_proj", "gdn_prefill_fused", "gdn_prefill_fused_workspace_bytes",
-           "gdn_status_string", "gdn_version", "gdn_prefill_fused_static")
+           "gdn_status_string", "gdn_version", "gdn_prefill_fused_static", "gdn_prefill_fused_ckpt")
 
 
 class GdnError(RuntimeError):
@@ -91,6 +91,9 @@ def load(path: Optional[str] = None):
     lib.gdn_decode_verify.restype = ctypes.c_int
     lib.gdn_prefill_fused.argtypes = [cfgp, ctypes.c_int32, ctypes.c_int32] + [_P] * 15 + [ctypes.c_size_t, _P]
     lib.gdn_prefill_fused.restype = ctypes.c_int
+    lib.gdn_prefill_fused_ckpt.argtypes = ([cfgp, ctypes.c_int32, ctypes.c_int32] + [_P] * 14
+                                           + [ctypes.c_int32, ctypes.c_int32, _P, _P, _P, ctypes.c_size_t, _P])
+    lib.gdn_prefill_fused_ckpt.restype = ctypes.c_int
     lib.gdn_prefill_fused_static.argtypes = [cfgp, ctypes.c_int32, ctypes.c_int32] + [_P] * 15
     lib.gdn_prefill_fused_static.restype = ctypes.c_int
     lib.gdn_prefill_fused_workspace_bytes.argtypes = [cfgp, ctypes.c_int32, ctypes.c_int32]
@@ -301,6 +304,27 @@ def gdn_prefill_fused(cfg: gdn_config, n_seqs: int, n_tokens: int, cu_seqlens, q
     _check("gdn_prefill_fused", s)
 
 
+def gdn_prefill_fused_ckpt(cfg: gdn_config, n_seqs: int, n_tokens: int, cu_seqlens, qkv, beta_logit, alpha_logit, z,
+                           conv_w, dt_bias, A_log, norm_w, conv_state_in, conv_state_out, S_in, S_out, y,
+                           ckpt_every: int, ckpt_cap: int, S_ckpt, conv_ckpt, workspace, stream=None):
+    Hqk, Hv, d, N, T = cfg.n_qk_heads, cfg.n_v_heads, cfg.head_dim, n_seqs, n_tokens
+    C, ad = d * (2 * Hqk + Hv), _act_dtype(cfg)
+    ws = _ptr(workspace, "workspace", torch.uint8)
+    s = load().gdn_prefill_fused_ckpt(
+        ctypes.byref(cfg), N, T, _ptr(cu_seqlens, "cu_seqlens", torch.int32, N + 1), _ptr(qkv, "qkv", ad, T * C),
+        _ptr(beta_logit, "beta_logit", ad, T * Hv), _ptr(alpha_logit, "alpha_logit", ad, T * Hv),
+        _ptr(z, "z", ad, T * Hv * d), _ptr(conv_w, "conv_w", torch.float32, C * CONV_K),
+        _ptr(dt_bias, "dt_bias", torch.float32, Hv), _ptr(A_log, "A_log", torch.float32, Hv),
+        _ptr(norm_w, "norm_w", torch.float32, d), _ptr(conv_state_in, "conv_state_in", ad, N * (CONV_K - 1) * C),
+        _ptr(conv_state_out, "conv_state_out", ad, N * (CONV_K - 1) * C),
+        _ptr(S_in, "S_in", torch.float32, N * Hv * d * d), _ptr(S_out, "S_out", torch.float32, N * Hv * d * d),
+        _ptr(y, "y", ad, T * Hv * d), ckpt_every, ckpt_cap,
+        _ptr(S_ckpt, "S_ckpt", torch.float32, N * ckpt_cap * Hv * d * d),
+        _ptr(conv_ckpt, "conv_ckpt", ad, N * ckpt_cap * (CONV_K - 1) * C),
+        ws, workspace.numel() if workspace is not None else 0, _stream(stream))
+    _check("gdn_prefill_fused_ckpt", s)
+
+
 def gdn_prefill_fused_static(cfg: gdn_config, n_seqs: int, n_tokens: int, cu_seqlens, qkv, beta_logit, alpha_logit,
                              z, conv_w, dt_bias, A_log, norm_w, conv_state_in, conv_state_out, S_in, S_out, y,
                              stream=None):
@@ -346,4 +370,4 @@ __all__ = ["load", "make_config", "gdn_config", "GdnError", "status_string", "EX
            "gdn_decode_step", "gdn_decode_fused", "gdn_decode_verify", "gdn_gated_rmsnorm",
            "gdn_prefill_chunked_ckpt", "gdn_conv_state_ckpt", "gdn_state_check", "gdn_in_proj",
            "gdn_out_proj", "gdn_prefill_fused", "gdn_prefill_fused_workspace_bytes", "gdn_prefill_fused_static",
-           "GDN_F32", "GDN_BF16", "GDN_STATIC_SCRATCH_BYTES"]
+           "gdn_prefill_fused_ckpt", "GDN_F32", "GDN_BF16", "GDN_STATIC_SCRATCH_BYTES"]

@@ -258,15 +258,20 @@ size_t gdn_prefill_fused_workspace_bytes(const gdn_config *cfg, int32_t n_seqs, 
          static_cast<size_t>(n_tokens) * cfg->n_v_heads * kHeadDim * act_size(cfg);
 }
 
-gdn_status gdn_prefill_fused(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens, const int32_t *cu_seqlens,
-                             const void *qkv, const void *beta_logit, const void *alpha_logit, const void *z,
-                             const float *conv_w, const float *dt_bias, const float *A_log, const float *norm_w,
-                             const void *conv_state_in, void *conv_state_out, const float *S_in, float *S_out,
-                             void *y, void *workspace, size_t workspace_bytes, gdn_stream_t stream) {
+gdn_status gdn_prefill_fused_ckpt(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens,
+                                  const int32_t *cu_seqlens, const void *qkv, const void *beta_logit,
+                                  const void *alpha_logit, const void *z, const float *conv_w,
+                                  const float *dt_bias, const float *A_log, const float *norm_w,
+                                  const void *conv_state_in, void *conv_state_out, const float *S_in, float *S_out,
+                                  void *y, int32_t ckpt_every, int32_t ckpt_cap, float *S_ckpt, void *conv_ckpt,
+                                  void *workspace, size_t workspace_bytes, gdn_stream_t stream) {
   const gdn_status cs = check_config(cfg);
   if (cs != GDN_OK) return cs;
   if (n_seqs < 0 || n_tokens < 0) return GDN_E_INVALID_ARG;
   if (n_seqs == 0) return n_tokens == 0 ? GDN_OK : GDN_E_INVALID_ARG;
+  if (ckpt_every < 0 || ckpt_cap < 0 || ckpt_every % gdn::kChunk != 0) return GDN_E_INVALID_ARG;
+  const bool ckpt = ckpt_every > 0 && ckpt_cap > 0;
+  if (ckpt && !S_ckpt) return GDN_E_INVALID_ARG;
   if (!cu_seqlens || !conv_w || !dt_bias || !A_log || !norm_w || !conv_state_in || !conv_state_out || !S_in ||
       !S_out)
     return GDN_E_INVALID_ARG;
@@ -304,6 +309,18 @@ gdn_status gdn_prefill_fused(const gdn_config *cfg, int32_t n_seqs, int32_t n_to
   if (overlap(conv_state_out, st, S_out, sb) || overlap(conv_state_in, st, S_out, sb) ||
       overlap(conv_state_out, st, S_in, sb))
     return GDN_E_INVALID_ARG;
+  if (ckpt) {
+    // The checkpoint planes overlap nothing else.
+    const size_t cb = static_cast<size_t>(n_seqs) * ckpt_cap * Hv * kHeadDim * kHeadDim * 4;
+    const size_t ccb = conv_ckpt ? static_cast<size_t>(n_seqs) * ckpt_cap * (gdn::kConvK - 1) * C * as : 0;
+    if (conv_ckpt && !aligned(conv_ckpt, 2 * as)) return GDN_E_INVALID_ARG;
+    for (const Range &r : ins)
+      if (overlap(r.p, r.n, S_ckpt, cb) || overlap(r.p, r.n, conv_ckpt, ccb)) return GDN_E_INVALID_ARG;
+    if (overlap(y, yb, S_ckpt, cb) || overlap(workspace, need, S_ckpt, cb) || overlap(y, yb, conv_ckpt, ccb) ||
+        overlap(workspace, need, conv_ckpt, ccb) || overlap(S_ckpt, cb, conv_ckpt, ccb))
+      return GDN_E_INVALID_ARG;
+    if (static_cast<int64_t>(n_seqs) * ckpt_cap > kMaxGrid) return GDN_E_UNSUPPORTED;
+  }
 
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   void *o = n_tokens > 0 ? static_cast<uint8_t *>(workspace) + fused_o_offset(cfg, n_seqs, n_tokens) : nullptr;
@@ -327,7 +344,25 @@ gdn_status gdn_prefill_fused(const gdn_config *cfg, int32_t n_seqs, int32_t n_to
   p.A_log = A_log;
   p.l2_eps = cfg->l2_eps;
   p.l2_mode = cfg->l2_mode;
+  p.S_ckpt = ckpt ? S_ckpt : nullptr;
+  p.ckpt_chunks = ckpt ? ckpt_every / gdn::kChunk : 0;
+  p.ckpt_cap = ckpt ? ckpt_cap : 0;
   hipError_t e = gdn::launch_prefill(p, cfg->act_dtype, hs);
+  if (e == hipSuccess && ckpt && conv_ckpt && n_tokens > 0) {
+    // Conv-state planes, before the last launch may update the conv state in place.
+    gdn::ConvCkptParams cp;
+    cp.cu = cu_seqlens;
+    cp.n_seqs = n_seqs;
+    cp.n_tokens = n_tokens;
+    cp.n_qk = Hqk;
+    cp.n_v = Hv;
+    cp.every = ckpt_every;
+    cp.cap = ckpt_cap;
+    cp.qkv = qkv;
+    cp.st_in = conv_state_in;
+    cp.ckpt = conv_ckpt;
+    e = gdn::launch_conv_ckpt(cp, cfg->act_dtype, hs);
+  }
   if (e == hipSuccess) {
     // The norm, and the new conv states: last, since the kernels above read
     // the old conv state (in-place safe).
@@ -349,6 +384,16 @@ gdn_status gdn_prefill_fused(const gdn_config *cfg, int32_t n_seqs, int32_t n_to
     e = gdn::launch_norm_conv_state(np, cp, cfg->act_dtype, hs);
   }
   return launched(e);
+}
+
+gdn_status gdn_prefill_fused(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens, const int32_t *cu_seqlens,
+                             const void *qkv, const void *beta_logit, const void *alpha_logit, const void *z,
+                             const float *conv_w, const float *dt_bias, const float *A_log, const float *norm_w,
+                             const void *conv_state_in, void *conv_state_out, const float *S_in, float *S_out,
+                             void *y, void *workspace, size_t workspace_bytes, gdn_stream_t stream) {
+  return gdn_prefill_fused_ckpt(cfg, n_seqs, n_tokens, cu_seqlens, qkv, beta_logit, alpha_logit, z, conv_w, dt_bias,
+                                A_log, norm_w, conv_state_in, conv_state_out, S_in, S_out, y, 0, 0, nullptr,
+                                nullptr, workspace, workspace_bytes, stream);
 }
 
 gdn_status gdn_conv_state_ckpt(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens, const int32_t *cu_seqlens,

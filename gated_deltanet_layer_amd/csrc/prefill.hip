@@ -1154,13 +1154,12 @@ hipError_t launch_prefill(const PrefillParams &p, gdn_dtype act, hipStream_t s) 
   const int64_t pairs = static_cast<int64_t>(p.n_seqs) * p.n_v;
   const dim3 grid_state(static_cast<unsigned>((pairs + kXcds - 1) / kXcds * kXcds * (kHeadDim / kSlab)));
   const bool fused = p.qkv != nullptr;
-  if (fused && p.ckpt_chunks > 0) return hipErrorInvalidValue;   // the fused form writes no checkpoints
 #define GDN_LAUNCH(PR, TA, FU)                                                                                \
   do {                                                                                                        \
     if (p.n_tokens > 0)                                                                                       \
       hipLaunchKernelGGL((chunk_local_kernel<PR, TA, FU>), grid_local, dim3(kLocalThreads), 0, s, p, chunks); \
-    if (p.ckpt_chunks > 0 && !(FU))                                                                           \
-      hipLaunchKernelGGL((chunk_state_kernel<PR, TA, false, true>), grid_state, dim3(kStateThreads), 0, s, p,  \
+    if (p.ckpt_chunks > 0)                                                                                    \
+      hipLaunchKernelGGL((chunk_state_kernel<PR, TA, FU, true>), grid_state, dim3(kStateThreads), 0, s, p,     \
                          chunks);                                                                             \
     else                                                                                                      \
       hipLaunchKernelGGL((chunk_state_kernel<PR, TA, FU, false>), grid_state, dim3(kStateThreads), 0, s, p,    \

@@ -253,6 +253,30 @@ GDN_API gdn_status gdn_prefill_fused_static(const gdn_config *cfg, int32_t n_seq
                                     float *S_out, void *y, gdn_stream_t stream);
 #define GDN_STATIC_SCRATCH_BYTES (256u * 1024u * 1024u)
 
+/*
+ * gdn_prefill_fused_ckpt -- gdn_prefill_fused that also keeps the states at
+ * block boundaries, for re-seeding later calls from a cached prefix (the same
+ * planes as gdn_prefill_chunked_ckpt and gdn_conv_state_ckpt, from the fused
+ * kernels):
+ *   S_ckpt    [N][ckpt_cap][Hv][d][d] fp32: plane c of sequence n = S after
+ *             its first (c + 1) * ckpt_every tokens
+ *   conv_ckpt [N][ckpt_cap][3][C] act dtype, or NULL for none: plane c = the
+ *             3 raw rows before token (c + 1) * ckpt_every (two activation
+ *             values aligned)
+ * for every such boundary inside the sequence or at its end with c <
+ * ckpt_cap; other planes are left untouched. ckpt_every is a multiple of the
+ * chunk length 64 (0, or ckpt_cap = 0, writes no checkpoint). y, S_out and the
+ * new conv state are the same as without checkpoints. The planes must not
+ * overlap any other buffer. Other arguments as for gdn_prefill_fused.
+ */
+GDN_API gdn_status gdn_prefill_fused_ckpt(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens,
+                                  const int32_t *cu_seqlens, const void *qkv, const void *beta_logit,
+                                  const void *alpha_logit, const void *z, const float *conv_w,
+                                  const float *dt_bias, const float *A_log, const float *norm_w,
+                                  const void *conv_state_in, void *conv_state_out, const float *S_in, float *S_out,
+                                  void *y, int32_t ckpt_every, int32_t ckpt_cap, float *S_ckpt, void *conv_ckpt,
+                                  void *workspace, size_t workspace_bytes, gdn_stream_t stream);
+
 /* Workspace size gdn_prefill_fused needs for these sizes (0 for a bad cfg). */
 GDN_API size_t gdn_prefill_fused_workspace_bytes(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens);
 

@@ -330,3 +330,17 @@ def test_static_scratch_entry_point_limits(lib):
     assert call(1, 64, B.make_config(16, 48, head_dim=64)) == B.GDN_E_UNSUPPORTED
     assert call(0, 0) == B.GDN_OK
     assert "static scratch" in B.status_string(B.GDN_E_TOO_LARGE)
+
+
+def test_prefill_fused_ckpt_validation(lib):
+    cfg = B.make_config(2, 4, "bf16")
+    need = B.gdn_prefill_fused_workspace_bytes(cfg, 2, 100)
+    p = FAKE[:13]   # qkv, b, a, z, conv_w, dt_bias, A_log, norm_w, conv_in, conv_out, S_in, S_out, y
+    call = lambda every, cap, sck, cck: lib.gdn_prefill_fused_ckpt(ctypes.byref(cfg), 2, 100, FAKE[15], *p, every, cap,
+                                                                   sck, cck, FAKE[13], need, None)
+    assert call(100, 2, FAKE[16], None) == B.GDN_E_INVALID_ARG            # not a multiple of 64
+    assert call(-64, 2, FAKE[16], None) == B.GDN_E_INVALID_ARG
+    assert call(64, 2, None, None) == B.GDN_E_INVALID_ARG                # planes missing
+    assert call(64, 2, FAKE[16], FAKE[16]) == B.GDN_E_INVALID_ARG        # S and conv planes overlap
+    assert call(64, 2, FAKE[0] + 64, None) == B.GDN_E_INVALID_ARG        # S planes on top of qkv
+    assert call(64, 2, FAKE[16], FAKE[17] + 2) == B.GDN_E_INVALID_ARG    # conv planes misaligned

@@ -86,6 +86,49 @@ def test_prefill_state_and_conv_checkpoints(act):
         assert np.array_equal(P.bits(conv_ckpt[:, c]), exp_bits), f"conv plane {c} (every {conv_every})"
 
 
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_fused_prefill_checkpoints(act):
+    """gdn_prefill_fused_ckpt: the same planes from the fused kernels, against
+    the oracle's prefixes; y, S_out and the new conv state identical to
+    gdn_prefill_fused without checkpoints (in place on the conv state)."""
+    lengths = [200, 140, 64]
+    w = wl.custom("prefill", 3, 2, 4, act, seed=342, lengths=lengths, s0_std=0.02, conv0_std=1.0)
+    x = wl.generate(w)
+    cfg = B.make_config(2, 4, act)
+    N, T, Hv, d = 3, sum(lengths), 4, 128
+    t = {k: P.dev(v) for k, v in x.items()}
+    plain = Lyr.PrefillFused(cfg, N, T)
+    conv_plain, S_plain = torch.empty_like(t["conv0"]), torch.empty_like(t["S0"])
+    plain(t["cu_seqlens"], t["qkv"], t["z"], t["b"], t["a"], t["conv_w"], t["dt_bias"], t["A_log"], t["norm_w"],
+          t["conv0"], conv_plain, t["S0"], S_plain)
+    every, cap = 64, 3
+    conv_io = t["conv0"].clone()                           # updated in place
+    S_out = torch.empty_like(t["S0"])
+    y = torch.empty_like(plain.y)
+    S_ckpt = torch.full((N, cap, Hv, d, d), float("nan"), device="cuda")
+    conv_ckpt = torch.zeros((N, cap) + tuple(t["conv0"].shape[1:]), dtype=t["conv0"].dtype, device="cuda")
+    say(f"case fused prefill checkpoints {act}")
+    B.gdn_prefill_fused_ckpt(cfg, N, T, t["cu_seqlens"], t["qkv"], t["b"], t["a"], t["z"], t["conv_w"],
+                             t["dt_bias"], t["A_log"], t["norm_w"], conv_io, conv_io, t["S0"], S_out, y, every, cap,
+                             S_ckpt, conv_ckpt, plain.ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(P.bits(S_out), P.bits(S_plain)), "checkpointing changed S_out"
+    assert np.array_equal(P.bits(y), P.bits(plain.y)), "checkpointing changed y"
+    assert np.array_equal(P.bits(conv_io), P.bits(conv_plain)), "checkpointing changed the new conv state"
+    for c in range(cap):
+        m = [min(L, (c + 1) * every) for L in lengths]
+        xm = _prefix(x, m)
+        ref = P.oracle_layer(w, P.inputs_f64(xm, act), xm["cu_seqlens"])
+        ref_conv = ref["conv_out"].astype(np.float32)
+        exp_bits = wl.bf16_bits(ref_conv) if act == "bf16" else ref_conv.view(np.uint32)
+        for n, L in enumerate(lengths):
+            if (c + 1) * every > L:
+                assert torch.isnan(S_ckpt[n, c]).all(), f"plane {c} of sequence {n} written past its end"
+                continue
+            P.check(f"S_ckpt[{n},{c}]", P.host(S_ckpt[n, c]), ref["S_out"][n], act)
+            assert np.array_equal(P.bits(conv_ckpt[n, c]), exp_bits[n]), f"conv plane {c} of sequence {n}"
+
+
 @pytest.mark.parametrize("n", [0, 7, 1 << 20])
 def test_state_check_counts_and_max(n):
     g = torch.Generator(device="cpu").manual_seed(341)
