@@ -11,8 +11,11 @@
 // with row pitch ld[s], so the four input projections run as one product
 // without stacking their weights.
 //
-// Tiling for gfx950. A block of 4 waves owns a kBM x BN tile (BN = 32 * WN);
-// wave (wr, wc) owns rows 128 wr .. +127 and columns 16 WN wc .. +16 WN - 1,
+// Tiling for gfx950. A block of 8 waves owns a kBM x BN tile (BN = 32 * WN):
+// waves 0-3 only compute, waves 4-7 only issue the operand loads, so that a
+// load instruction never holds up the issue of a compute wave's MFMAs (a
+// vector-memory instruction stalls the wave that issues it). Compute wave
+// (wr, wc) owns rows 128 wr .. +127 and columns 16 WN wc .. +16 WN - 1,
 // i.e. 8 x WN accumulator tiles of 16 x 16 (v_mfma_f32_16x16x32_bf16). The
 // contraction runs in k-tiles of 64 staged in a 3-deep LDS ring (see
 // gemm_dma_kernel), one barrier per k-tile. An LDS row is the 128 bytes of
@@ -39,7 +42,8 @@ namespace {
 constexpr int kBM = 256;          // rows of a block tile (2 waves x 8 fragments x 16)
 constexpr int kBK = 64;           // contraction indices per k-tile
 constexpr int kRowBytes = kBK * 2;
-constexpr int kGemmThreads = 256;
+constexpr int kGemmThreads = 512;          // 4 compute waves + 4 load waves
+constexpr int kComputeThreads = 256;
 constexpr int kGroupM = 4;        // row tiles per group in the tile walk
 constexpr int kGemmXcds = 8;
 // Per-lane source addresses of the 8 loads of a k-tile. A vector value, not
@@ -140,7 +144,7 @@ __device__ __forceinline__ void wait_vm_barrier() {
 template <int WN>
 __global__ __launch_bounds__(kGemmThreads) void gemm_dma_kernel(GemmParams p, int tiles_m, int tiles_n, int per_xcd) {
   constexpr int BN = 32 * WN;
-  constexpr int kBChunks = BN * 8 / kGemmThreads;
+  constexpr int kBChunks = BN * 8 / kComputeThreads;
   constexpr int kLoads = 8 + kBChunks;            // loads per thread and k-tile
   constexpr int kABytes = kBM * kRowBytes, kBBytes = BN * kRowBytes, kStage = kABytes + kBBytes;
   static_assert(kBChunks <= 8, "at most 8 weight chunks per thread");
@@ -156,13 +160,17 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_dma_kernel(GemmParams p, in
   const int tn = in_group / gsize;
   const int m0 = tm * kBM, n0 = tn * BN;
 
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int wr = wave >> 1, wc = wave & 1;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // uniform per wave
+  const bool loader = wave >= 4;
+  const int wr = (wave & 3) >> 1, wc = wave & 1;
   const int K = p.K;
   const Segs g(p);
 
-  // Load i of this lane: row lrow + 32 i of the tile, the chunk for slot lane & 7.
-  const int lrow = tid >> 3;
+  // Load waves: load i of this lane is row lrow + 32 i of the tile, the
+  // chunk for slot lane & 7.
+  const int ltid = tid & (kComputeThreads - 1);
+  const int lrow = ltid >> 3;
   const int gchunk = (lane & 7) ^ (lrow & 7);
   u64x8 asrc, bsrc = {};
 #pragma unroll
@@ -176,7 +184,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_dma_kernel(GemmParams p, in
     const int s = g.seg(n);
     bsrc[i] = reinterpret_cast<uint64_t>(g.w(s) + static_cast<int64_t>(n - g.start(s)) * K + 8 * gchunk);
   }
-  const int wdst = 8 * wave * kRowBytes;          // this wave's 8 rows of load i: + 32 i rows
+  const int wdst = 8 * (wave & 3) * kRowBytes;    // this wave's 8 rows of load i: + 32 i rows
 
 #define GDN_REP8(M) M(0) M(1) M(2) M(3) M(4) M(5) M(6) M(7)
 #define GDN_DMA(i)                                                                                \
@@ -203,15 +211,26 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_dma_kernel(GemmParams p, in
   const int a_row0 = 128 * wr + fr, b_row0 = 16 * WN * wc + fr;
 
   const int KT = K / kBK;
-  GDN_ISSUE(0, 0);
-  if (KT > 1) GDN_ISSUE(1, 1);
+  if (loader) {
+    // The load waves keep two k-tiles in flight: before each barrier they
+    // wait for the k-tile about to be used, after it they issue the one two
+    // ahead into the stage every wave has just finished with.
+    GDN_ISSUE(0, 0);
+    if (KT > 1) GDN_ISSUE(1, 1);
+    int stage = 0;
+    for (int kt = 0; kt < KT; ++kt) {
+      if (kt + 1 < KT)
+        wait_vm_barrier<kLoads>();
+      else
+        wait_vm_barrier<0>();
+      if (kt + 2 < KT) GDN_ISSUE(kt + 2, stage == 0 ? 2 : stage - 1);
+      stage = stage == kStages - 1 ? 0 : stage + 1;
+    }
+    return;
+  }
   int stage = 0;
   for (int kt = 0; kt < KT; ++kt) {
-    if (kt + 1 < KT)
-      wait_vm_barrier<kLoads>();
-    else
-      wait_vm_barrier<0>();
-    if (kt + 2 < KT) GDN_ISSUE(kt + 2, stage == 0 ? 2 : stage - 1);
+    wait_vm_barrier<0>();                      // (a compute wave has no loads: only its LDS reads)
     const uint8_t *a = smem + stage * kStage;
     const uint8_t *b = a + kABytes;
 #pragma unroll
