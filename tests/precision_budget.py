@@ -159,8 +159,6 @@ def budget_table(T: int = 1024, heads: Sequence[int] = (0, 7, 13, 22, 31, 40, 47
 
 
 if __name__ == "__main__":
-    import sys
-    import os
-    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    # from the repository root: python3 -m tests.precision_budget
     for name, r in budget_table().items():
         print(f"{name:45s} y {r['y']:8.3f}  o {r['o']:8.3f}  S_out {r['S_out']:8.3f}")
