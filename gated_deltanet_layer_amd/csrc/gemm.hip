@@ -100,10 +100,10 @@ __device__ __noinline__ void store4_split(Segs g, int m, int n, uint32_t lo, uin
   }
 }
 
-template <int WN>
-__device__ __forceinline__ void gemm_epilogue(const Segs &g, int M, const f32x4 (&acc)[8][WN], int mrow, int ncol) {
+template <int TM, int WN>
+__device__ __forceinline__ void gemm_epilogue(const Segs &g, int M, const f32x4 (&acc)[TM][WN], int mrow, int ncol) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < TM; ++i) {
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
       const int m = mrow + 16 * i, n = ncol + 16 * j;
@@ -141,24 +141,17 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-template <int WN>
-__global__ __launch_bounds__(kGemmThreads) void gemm_dma_kernel(GemmParams p, int tiles_m, int tiles_n, int per_xcd) {
-  constexpr int BN = 32 * WN;
+// One block tile of 32 TM rows x 32 WN columns at (m0, n0): compute wave
+// (wr, wc) owns rows 16 TM wr .. +16 TM - 1, i.e. TM x WN accumulator tiles.
+// smem holds kStages k-tiles of this shape.
+template <int TM, int WN>
+__device__ __forceinline__ void gemm_tile(const GemmParams &p, uint8_t *smem, int m0, int n0) {
+  constexpr int BM = 32 * TM, BN = 32 * WN;
+  constexpr int kAChunks = BM * 8 / kComputeThreads;
   constexpr int kBChunks = BN * 8 / kComputeThreads;
-  constexpr int kLoads = 8 + kBChunks;            // loads per thread and k-tile
-  constexpr int kABytes = kBM * kRowBytes, kBBytes = BN * kRowBytes, kStage = kABytes + kBBytes;
-  static_assert(kBChunks <= 8, "at most 8 weight chunks per thread");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStage];
-
-  const int logical = (blockIdx.x % kGemmXcds) * per_xcd + blockIdx.x / kGemmXcds;
-  if (logical >= tiles_m * tiles_n) return;
-  const int group = logical / (kGroupM * tiles_n);
-  const int gm0 = group * kGroupM;
-  const int gsize = min(kGroupM, tiles_m - gm0);
-  const int in_group = logical - group * kGroupM * tiles_n;
-  const int tm = gm0 + in_group % gsize;
-  const int tn = in_group / gsize;
-  const int m0 = tm * kBM, n0 = tn * BN;
+  constexpr int kLoads = kAChunks + kBChunks;     // loads per thread and k-tile
+  constexpr int kABytes = BM * kRowBytes, kBBytes = BN * kRowBytes, kStage = kABytes + kBBytes;
+  static_assert(kAChunks <= 8 && kBChunks <= 8, "at most 8 chunks per operand and thread");
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // uniform per wave
@@ -172,9 +165,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_dma_kernel(GemmParams p, in
   const int ltid = tid & (kComputeThreads - 1);
   const int lrow = ltid >> 3;
   const int gchunk = (lane & 7) ^ (lrow & 7);
-  u64x8 asrc, bsrc = {};
+  u64x8 asrc = {}, bsrc = {};
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < kAChunks; ++i) {
     const int m = min(m0 + lrow + 32 * i, p.M - 1);
     asrc[i] = reinterpret_cast<uint64_t>(p.x + static_cast<int64_t>(m) * K + 8 * gchunk);
   }
@@ -188,8 +181,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_dma_kernel(GemmParams p, in
 
 #define GDN_REP8(M) M(0) M(1) M(2) M(3) M(4) M(5) M(6) M(7)
 #define GDN_DMA(i)                                                                                \
-  __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint16_t *>(asrc[i]) + koff,           \
-                                   sa_ + wdst + 32 * (i) * kRowBytes, 16, 0, 0);                  \
+  if constexpr (i < kAChunks)                                                                     \
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint16_t *>(asrc[i]) + koff,         \
+                                     sa_ + wdst + 32 * (i) * kRowBytes, 16, 0, 0);                \
   if constexpr (i < kBChunks)                                                                     \
     __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint16_t *>(bsrc[i]) + koff,         \
                                      sb_ + wdst + 32 * (i) * kRowBytes, 16, 0, 0);
@@ -201,14 +195,14 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_dma_kernel(GemmParams p, in
     GDN_REP8(GDN_DMA)                                                                             \
   } while (0)
 
-  f32x4 acc[8][WN];
+  f32x4 acc[TM][WN];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < WN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int fr = lane & 15, fq = lane >> 4;
-  const int a_row0 = 128 * wr + fr, b_row0 = 16 * WN * wc + fr;
+  const int a_row0 = 16 * TM * wr + fr, b_row0 = 16 * WN * wc + fr;
 
   const int KT = K / kBK;
   if (loader) {
@@ -235,15 +229,15 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_dma_kernel(GemmParams p, in
     const uint8_t *b = a + kABytes;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 fa[8], fb[WN];
+      bf16x8 fa[TM], fb[WN];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < TM; ++i)
         fa[i] = *reinterpret_cast<const bf16x8 *>(a + lds_off(a_row0 + 16 * i, 4 * ks + fq));
 #pragma unroll
       for (int j = 0; j < WN; ++j)
         fb[j] = *reinterpret_cast<const bf16x8 *>(b + lds_off(b_row0 + 16 * j, 4 * ks + fq));
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < WN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
@@ -254,7 +248,28 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_dma_kernel(GemmParams p, in
 #undef GDN_DMA
 #undef GDN_REP8
 
-  gemm_epilogue<WN>(g, p.M, acc, m0 + 128 * wr + fr, n0 + 16 * WN * wc + 4 * fq);
+  gemm_epilogue<TM, WN>(g, p.M, acc, m0 + 16 * TM * wr + fr, n0 + 16 * WN * wc + 4 * fq);
+}
+
+// Tiles of 32 TM rows x 32 WN columns: tiles_m row tiles x the column tiles
+// [tn0, tn0 + tiles_n), dealt to the XCDs in contiguous ranges and walked in
+// groups of kGroupM row tiles. A launch whose last round of 256-row tiles
+// would leave most CUs idle runs its last column tiles as a second launch of
+// 128-row tiles instead (same operands, half the rows per tile).
+template <int TM, int WN>
+__global__ __launch_bounds__(kGemmThreads) void gemm_dma_kernel(GemmParams p, int tiles_m, int tn0, int tiles_n,
+                                                                int per_xcd) {
+  constexpr int BM = 32 * TM, BN = 32 * WN;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * (BM + BN) * kRowBytes];
+  const int logical = (blockIdx.x % kGemmXcds) * per_xcd + blockIdx.x / kGemmXcds;
+  if (logical >= tiles_m * tiles_n) return;
+  const int group = logical / (kGroupM * tiles_n);
+  const int gm0 = group * kGroupM;
+  const int gsize = min(kGroupM, tiles_m - gm0);
+  const int in_group = logical - group * kGroupM * tiles_n;
+  const int tm = gm0 + in_group % gsize;
+  const int tn = tn0 + in_group / gsize;
+  gemm_tile<TM, WN>(p, smem, tm * BM, tn * BN);
 }
 
 // Few rows (decode: M <= 64): the product is bound by streaming the weights
@@ -369,31 +384,59 @@ hipError_t launch_skinny_m(const GemmParams &p, hipStream_t s) {
   return launch_skinny<MF, 1>(p, s);
 }
 
+struct TilePlan {
+  int wn, tail_n;
+};
+
+template <int TM, int WN>
+void launch_tiles(const GemmParams &p, int tiles_m, int tn0, int tiles_n, hipStream_t s) {
+  const int tiles = tiles_m * tiles_n;
+  if (tiles == 0) return;
+  const int per_xcd = (tiles + kGemmXcds - 1) / kGemmXcds;
+  hipLaunchKernelGGL((gemm_dma_kernel<TM, WN>), dim3(per_xcd * kGemmXcds), dim3(kGemmThreads), 0, s, p, tiles_m, tn0,
+                     tiles_n, per_xcd);
+}
+
 template <int WN>
-hipError_t launch_wn(const GemmParams &p, hipStream_t s) {
+hipError_t launch_wn(const GemmParams &p, int tail_n, hipStream_t s) {
   constexpr int BN = 32 * WN;
   const int tiles_m = (p.M + kBM - 1) / kBM, tiles_n = (p.N + BN - 1) / BN;
-  const int tiles = tiles_m * tiles_n;
-  const int per_xcd = (tiles + kGemmXcds - 1) / kGemmXcds;
-  hipLaunchKernelGGL(gemm_dma_kernel<WN>, dim3(per_xcd * kGemmXcds), dim3(kGemmThreads), 0, s, p, tiles_m, tiles_n,
-                     per_xcd);
+  launch_tiles<kBM / 32, WN>(p, tiles_m, 0, tiles_n - tail_n, s);
+  launch_tiles<kBM / 64, WN>(p, (p.M + kBM / 2 - 1) / (kBM / 2), tiles_n - tail_n, tail_n, s);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// The column-tile width is chosen per call so that the number of rounds of
-// 256 concurrent tiles, times the tile width, is smallest (the last round of
-// a launch is often partly idle).
-static int gemm_tile_wn(int M, int N) {
+// The column-tile width, and how many of the last column tiles run as
+// 128-row tiles in a second launch, are chosen per call for the least
+// estimated time: rounds of 256 concurrent tiles times the tile width (plus a
+// fixed cost per tile), where the round of half-height tiles costs kHalfCost
+// of a full one (a 128-row tile moves the same weight tile through LDS for
+// half the MFMA work, and the launch adds its own start). The tail is used
+// only when the full tiles then fill whole rounds and the half-height ones
+// fit in one.
+constexpr int kCUs = 256;
+constexpr double kHalfCost = 0.65;
+
+static TilePlan gemm_tile_plan(int M, int N) {
   const int tiles_m = (M + kBM - 1) / kBM;
-  int best = kMaxWn;
-  int64_t best_cost = -1;
+  TilePlan best{kMaxWn, 0};
+  double best_cost = -1.0;
   for (int wn = kMaxWn; wn >= 4; --wn) {
-    const int64_t tiles = static_cast<int64_t>(tiles_m) * ((N + 32 * wn - 1) / (32 * wn));
-    const int64_t rounds = (tiles + 255) / 256;
-    const int64_t cost = rounds * (32 * wn + 16);   // + a fixed per-tile cost
-    if (best_cost < 0 || cost < best_cost) { best_cost = cost; best = wn; }
+    const int tiles_n = (N + 32 * wn - 1) / (32 * wn);
+    const double per_round = 32.0 * wn + 16.0;
+    for (int tail = 0; tail < tiles_n; ++tail) {
+      const int64_t main_tiles = static_cast<int64_t>(tiles_m) * (tiles_n - tail);
+      const int64_t half_tiles = 2LL * tiles_m * tail;
+      if (tail > 0 && (main_tiles % kCUs != 0 || half_tiles > kCUs)) continue;
+      const double cost = static_cast<double>((main_tiles + kCUs - 1) / kCUs) * per_round +
+                          (tail > 0 ? kHalfCost * per_round : 0.0);
+      if (best_cost < 0 || cost < best_cost) {
+        best_cost = cost;
+        best = TilePlan{wn, tail};
+      }
+    }
   }
   return best;
 }
@@ -403,8 +446,9 @@ hipError_t launch_gemm(const GemmParams &p, hipStream_t s) {
   if (p.M <= 16) return launch_skinny_m<1>(p, s);
   if (p.M <= 32) return launch_skinny_m<2>(p, s);
   if (p.M <= 64) return launch_skinny_m<4>(p, s);
-  if (gemm_tile_wn(p.M, p.N) == 4) return launch_wn<4>(p, s);
-  return launch_wn<5>(p, s);
+  const TilePlan plan = gemm_tile_plan(p.M, p.N);
+  if (plan.wn == 4) return launch_wn<4>(p, plan.tail_n, s);
+  return launch_wn<5>(p, plan.tail_n, s);
 }
 
 }  // namespace gdn

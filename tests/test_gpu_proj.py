@@ -6,7 +6,7 @@ element must be a bf16 rounding of a value within the fp32 accumulation
 error bound of the oracle's, and equal to the oracle's own rounding for all
 but a rare few (sums near a rounding midpoint), on top of the bf16 bar. At the full sizes of the 27B and 35B-A3B layers
 the oracle computes sampled rows (every column of them): the rows that open
-and close 256-row tiles, the first and last rows, and random ones.
+and close 256-row and 128-row tiles, the first and last rows, and random ones.
 
 In the block the oracle rounds qkv, z, the logits and y to bf16 as the HIP
 path stores them (and the readout o where the path stores it in bf16: the
@@ -101,7 +101,9 @@ def _check_in_proj(w, x, got, rows=None):
 
 def _rows(T, seed):
     base = {0, 1, T - 1, T - 2}
-    for t in range(255, T, 256):
+    # Tiles are 256 rows, and 128 in the half-height tiles that take the
+    # last column tiles when a launch's last round would be mostly idle.
+    for t in range(127, T, 128):
         base.update({t, min(t + 1, T - 1)})
     rng = np.random.default_rng(seed)
     base.update(int(r) for r in rng.integers(0, T, 4))
@@ -109,10 +111,13 @@ def _rows(T, seed):
 
 
 # Row counts up to 64 take the decode kernel (16, 32 or 64 rows per block;
-# 1 to 6 column fragments per block by width), more the tiled one.
+# 1 to 6 column fragments per block by width), more the tiled one; 4096 rows
+# x 2576 columns run 256 tiles of 256 rows and the last 5 column tiles as
+# 128-row tiles.
 @pytest.mark.parametrize("T,hidden,heads", [(1, 64, (1, 1)), (20, 128, (2, 6)), (40, 192, (2, 4)),
                                             (5, 64, (16, 64)), (64, 128, (16, 48)), (77, 128, (2, 6)),
-                                            (300, 192, (2, 4)), (513, 256, (4, 4)), (256, 320, (1, 2))])
+                                            (300, 192, (2, 4)), (513, 256, (4, 4)), (256, 320, (1, 2)),
+                                            (4096, 256, (2, 8))])
 def test_in_proj_small(T, hidden, heads):
     hqk, hv = heads
     w = wl.custom("prefill", 1, hqk, hv, "bf16", seed=400 + T, lengths=[T])
@@ -143,7 +148,8 @@ def _out_proj_gpu(cfg, x, hidden):
 
 
 @pytest.mark.parametrize("T,hidden,hv,full", [(1, 64, 1, False), (77, 200, 6, False), (513, 256, 4, False),
-                                              (4096, 5120, 48, True), (64, 2048, 32, True)])
+                                              (4096, 5120, 48, True), (64, 2048, 32, True),
+                                              (4096, 2720, 16, True)])
 def test_out_proj(T, hidden, hv, full):
     hqk = 16 if full else 1
     w = wl.custom("prefill", 1, hqk, hv, "bf16", seed=420 + T + hv, lengths=[T])
