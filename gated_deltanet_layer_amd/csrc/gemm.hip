@@ -412,12 +412,12 @@ hipError_t launch_wn(const GemmParams &p, int tail_n, hipStream_t s) {
 // 128-row tiles in a second launch, are chosen per call for the least
 // estimated time: rounds of 256 concurrent tiles times the tile width (plus a
 // fixed cost per tile), where the round of half-height tiles costs kHalfCost
-// of a full one (a 128-row tile moves the same weight tile through LDS for
-// half the MFMA work, and the launch adds its own start). The tail is used
-// only when the full tiles then fill whole rounds and the half-height ones
-// fit in one.
+// of a full one (LDS traffic bounds these tiles, and a 128 x 160 tile moves
+// 69% of a 256 x 160 tile's bytes through LDS for half its MFMA work). The
+// tail is used only when the full tiles then fill whole rounds and the
+// half-height ones fit in one.
 constexpr int kCUs = 256;
-constexpr double kHalfCost = 0.65;
+constexpr double kHalfCost = 0.7;
 
 static TilePlan gemm_tile_plan(int M, int N) {
   const int tiles_m = (M + kBM - 1) / kBM;
