@@ -280,6 +280,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_dma_kernel(GemmParams p, in
 // weights from HBM, the few activation rows from L2), U steps of loads in
 // flight before their MFMAs; the 8 partial sums meet in LDS.
 constexpr int kSkWaves = 8;
+constexpr int kSkMaxNf = 5;
+constexpr int kSkCUs = 256;
 
 template <int MF, int NF, int U>
 __global__ __launch_bounds__(kSkWaves * kWave) void gemm_skinny_kernel(GemmParams p) {
@@ -377,11 +379,26 @@ hipError_t launch_skinny(const GemmParams &p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Column fragments per block: a block's time is a fixed part (its walk of
+// the contraction: a few round trips of loads, then the reduction through
+// LDS) plus a part per fragment, measured at about 3.7 : 1, and the blocks
+// run in rounds of one per CU. NF minimises rounds x (3.7 + NF).
 template <int MF>
 hipError_t launch_skinny_m(const GemmParams &p, hipStream_t s) {
-  // Two fragments of columns per block when that still gives a block per CU.
-  if ((p.N + 31) / 32 >= 256) return launch_skinny<MF, 2>(p, s);
-  return launch_skinny<MF, 1>(p, s);
+  int best = 1;
+  double best_cost = -1.0;
+  for (int nf = 1; nf <= kSkMaxNf; ++nf) {
+    const int64_t blocks = (p.N + 16 * nf - 1) / (16 * nf);
+    const double cost = static_cast<double>((blocks + kSkCUs - 1) / kSkCUs) * (3.7 + nf);
+    if (best_cost < 0 || cost < best_cost - 1e-9) { best_cost = cost; best = nf; }
+  }
+  switch (best) {
+    case 1: return launch_skinny<MF, 1>(p, s);
+    case 2: return launch_skinny<MF, 2>(p, s);
+    case 3: return launch_skinny<MF, 3>(p, s);
+    case 4: return launch_skinny<MF, 4>(p, s);
+    default: return launch_skinny<MF, 5>(p, s);
+  }
 }
 
 struct TilePlan {
