@@ -716,8 +716,8 @@ def host_identity() -> dict:
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-decode", action="store_true", help="skip the decode workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the oracle")
     ap.add_argument("--no-block", action="store_true", help="skip the block (projections + mixer)")
