@@ -274,11 +274,12 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_dma_kernel(GemmParams p, in
 
 // Few rows (decode: M <= 64): the product is bound by streaming the weights
 // from HBM once, and there are too few row tiles to fill the chip. A block
-// owns 16 * NF output columns and all M rows (MF fragments of 16); its 8
-// waves split the contraction into contiguous ranges of 32-wide steps and
-// read both operands straight into MFMA fragments (16 bytes per lane: the
-// weights from HBM, the few activation rows from L2), U steps of loads in
-// flight before their MFMAs; the 8 partial sums meet in LDS.
+// owns 16 * NF output columns and 16 * MF rows (all of them, or one of two
+// row groups: blockIdx.y); its 8 waves split the contraction into contiguous
+// ranges of 32-wide steps and read both operands straight into MFMA
+// fragments (16 bytes per lane: the weights from HBM, the few activation rows
+// from L2), U steps of loads in flight before their MFMAs; the 8 partial sums
+// meet in LDS.
 constexpr int kSkWaves = 8;
 constexpr int kSkMaxNf = 5;
 constexpr int kSkCUs = 256;
@@ -290,12 +291,13 @@ __global__ __launch_bounds__(kSkWaves * kWave) void gemm_skinny_kernel(GemmParam
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int fr = lane & 15, fq = lane >> 4;
   const int n0 = blockIdx.x * 16 * NF;
+  const int m0 = blockIdx.y * 16 * MF;          // this block's group of rows
 
   // Row pointers at this lane's 8 contraction indices of a step (8 fq ..).
   u64x8 arow = {}, brow = {};
 #pragma unroll
   for (int i = 0; i < MF; ++i)
-    arow[i] = reinterpret_cast<uint64_t>(p.x + static_cast<int64_t>(min(16 * i + fr, M - 1)) * K + 8 * fq);
+    arow[i] = reinterpret_cast<uint64_t>(p.x + static_cast<int64_t>(min(m0 + 16 * i + fr, M - 1)) * K + 8 * fq);
 #pragma unroll
   for (int j = 0; j < NF; ++j) {
     const int n = min(n0 + 16 * j + fr, p.N - 1);
@@ -357,7 +359,7 @@ __global__ __launch_bounds__(kSkWaves * kWave) void gemm_skinny_kernel(GemmParam
 #pragma unroll
     for (int w = 1; w < kSkWaves; ++w) sum += part[w][f][lane];
     const int i = f / NF, j = f % NF;
-    const int m = 16 * i + fr, n = n0 + 16 * j + 4 * fq;
+    const int m = m0 + 16 * i + fr, n = n0 + 16 * j + 4 * fq;
     const uint32_t lo = static_cast<uint32_t>(f32_to_bf16(sum[0])) | (static_cast<uint32_t>(f32_to_bf16(sum[1])) << 16);
     const uint32_t hi = static_cast<uint32_t>(f32_to_bf16(sum[2])) | (static_cast<uint32_t>(f32_to_bf16(sum[3])) << 16);
     if (m < M && n < g.N) {
@@ -372,11 +374,38 @@ __global__ __launch_bounds__(kSkWaves * kWave) void gemm_skinny_kernel(GemmParam
 }
 
 template <int MF, int NF>
-hipError_t launch_skinny(const GemmParams &p, hipStream_t s) {
+hipError_t launch_skinny(const GemmParams &p, hipStream_t s, int row_groups) {
   constexpr int U = 4;   // steps of loads in flight per wave
   const int blocks = (p.N + 16 * NF - 1) / (16 * NF);
-  hipLaunchKernelGGL((gemm_skinny_kernel<MF, NF, U>), dim3(blocks), dim3(kSkWaves * kWave), 0, s, p);
+  hipLaunchKernelGGL((gemm_skinny_kernel<MF, NF, U>), dim3(blocks, row_groups), dim3(kSkWaves * kWave), 0, s, p);
   return hipGetLastError();
+}
+
+// NF column fragments per block; when that leaves at least half the CUs idle
+// and the rows span two or more fragments, the rows are split over two groups
+// of blocks (each half the fragments): twice the blocks, each with half the
+// activation loads (35B out-projection at 64 rows: 20.0 -> 13.0 us).
+template <int MF>
+hipError_t launch_skinny_nf(const GemmParams &p, hipStream_t s, int nf) {
+  const int64_t blocks = (p.N + 16 * nf - 1) / (16 * nf);
+  if constexpr (MF >= 2) {
+    if (blocks <= kSkCUs / 2) {
+      switch (nf) {
+        case 1: return launch_skinny<MF / 2, 1>(p, s, 2);
+        case 2: return launch_skinny<MF / 2, 2>(p, s, 2);
+        case 3: return launch_skinny<MF / 2, 3>(p, s, 2);
+        case 4: return launch_skinny<MF / 2, 4>(p, s, 2);
+        default: return launch_skinny<MF / 2, 5>(p, s, 2);
+      }
+    }
+  }
+  switch (nf) {
+    case 1: return launch_skinny<MF, 1>(p, s, 1);
+    case 2: return launch_skinny<MF, 2>(p, s, 1);
+    case 3: return launch_skinny<MF, 3>(p, s, 1);
+    case 4: return launch_skinny<MF, 4>(p, s, 1);
+    default: return launch_skinny<MF, 5>(p, s, 1);
+  }
 }
 
 // Column fragments per block: a block's time is a fixed part (its walk of
@@ -392,13 +421,7 @@ hipError_t launch_skinny_m(const GemmParams &p, hipStream_t s) {
     const double cost = static_cast<double>((blocks + kSkCUs - 1) / kSkCUs) * (3.7 + nf);
     if (best_cost < 0 || cost < best_cost - 1e-9) { best_cost = cost; best = nf; }
   }
-  switch (best) {
-    case 1: return launch_skinny<MF, 1>(p, s);
-    case 2: return launch_skinny<MF, 2>(p, s);
-    case 3: return launch_skinny<MF, 3>(p, s);
-    case 4: return launch_skinny<MF, 4>(p, s);
-    default: return launch_skinny<MF, 5>(p, s);
-  }
+  return launch_skinny_nf<MF>(p, s, best);
 }
 
 struct TilePlan {
