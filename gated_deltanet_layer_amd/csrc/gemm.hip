@@ -381,47 +381,46 @@ hipError_t launch_skinny(const GemmParams &p, hipStream_t s, int row_groups) {
   return hipGetLastError();
 }
 
-// NF column fragments per block; when that leaves at least half the CUs idle
-// and the rows span two or more fragments, the rows are split over two groups
-// of blocks (each half the fragments): twice the blocks, each with half the
-// activation loads (35B out-projection at 64 rows: 20.0 -> 13.0 us).
-template <int MF>
-hipError_t launch_skinny_nf(const GemmParams &p, hipStream_t s, int nf) {
-  const int64_t blocks = (p.N + 16 * nf - 1) / (16 * nf);
+// NF column fragments per block, and the rows either in one group or split
+// over two groups of blocks (blockIdx.y: each block then has half the rows
+// and half the activation loads). A block's time is a fixed part (its walk
+// of the contraction: a few round trips of loads, then the reduction through
+// LDS) plus a part per fragment, fitted at about 3.7 : 1, times about 0.65
+// when its rows are halved (the activation fragments are most of its loads);
+// blocks run in rounds of one per CU. The plan minimises
+// rounds x (3.7 + NF) x (0.65 if split).
+template <int MF, int NF>
+hipError_t launch_skinny_rg(const GemmParams &p, hipStream_t s, bool split) {
   if constexpr (MF >= 2) {
-    if (blocks <= kSkCUs / 2) {
-      switch (nf) {
-        case 1: return launch_skinny<MF / 2, 1>(p, s, 2);
-        case 2: return launch_skinny<MF / 2, 2>(p, s, 2);
-        case 3: return launch_skinny<MF / 2, 3>(p, s, 2);
-        case 4: return launch_skinny<MF / 2, 4>(p, s, 2);
-        default: return launch_skinny<MF / 2, 5>(p, s, 2);
-      }
-    }
+    if (split) return launch_skinny<MF / 2, NF>(p, s, 2);
   }
-  switch (nf) {
-    case 1: return launch_skinny<MF, 1>(p, s, 1);
-    case 2: return launch_skinny<MF, 2>(p, s, 1);
-    case 3: return launch_skinny<MF, 3>(p, s, 1);
-    case 4: return launch_skinny<MF, 4>(p, s, 1);
-    default: return launch_skinny<MF, 5>(p, s, 1);
-  }
+  return launch_skinny<MF, NF>(p, s, 1);
 }
 
-// Column fragments per block: a block's time is a fixed part (its walk of
-// the contraction: a few round trips of loads, then the reduction through
-// LDS) plus a part per fragment, measured at about 3.7 : 1, and the blocks
-// run in rounds of one per CU. NF minimises rounds x (3.7 + NF).
 template <int MF>
 hipError_t launch_skinny_m(const GemmParams &p, hipStream_t s) {
   int best = 1;
+  bool best_split = false;
   double best_cost = -1.0;
   for (int nf = 1; nf <= kSkMaxNf; ++nf) {
     const int64_t blocks = (p.N + 16 * nf - 1) / (16 * nf);
-    const double cost = static_cast<double>((blocks + kSkCUs - 1) / kSkCUs) * (3.7 + nf);
-    if (best_cost < 0 || cost < best_cost - 1e-9) { best_cost = cost; best = nf; }
+    for (int rg = 1; rg <= (MF >= 2 ? 2 : 1); ++rg) {
+      const double cost =
+          static_cast<double>((rg * blocks + kSkCUs - 1) / kSkCUs) * (3.7 + nf) * (rg == 2 ? 0.65 : 1.0);
+      if (best_cost < 0 || cost < best_cost - 1e-9) {
+        best_cost = cost;
+        best = nf;
+        best_split = rg == 2;
+      }
+    }
   }
-  return launch_skinny_nf<MF>(p, s, best);
+  switch (best) {
+    case 1: return launch_skinny_rg<MF, 1>(p, s, best_split);
+    case 2: return launch_skinny_rg<MF, 2>(p, s, best_split);
+    case 3: return launch_skinny_rg<MF, 3>(p, s, best_split);
+    case 4: return launch_skinny_rg<MF, 4>(p, s, best_split);
+    default: return launch_skinny_rg<MF, 5>(p, s, best_split);
+  }
 }
 
 struct TilePlan {
