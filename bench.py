@@ -204,7 +204,8 @@ def write_traffic(dbs):
              "gdn_prefill_chunked on the T=4096, Hv=48 bf16 workload (chunk_local + chunk_state)"),
             ("prefill_fused_core", "prefill", ("chunk_local_kernel<BF16X3, gdn::bf16_t, true>",
                                                "chunk_state_kernel<BF16X3, gdn::bf16_t, true, false>"),
-             "the chunked kernels of gdn_prefill_fused, T=4096 Hv=48 bf16 (q, k, v, gates formed inside)"),
+             "the kernels of gdn_prefill_fused, T=4096 Hv=48 bf16: chunk_local and chunk_state (q, k, v and the "
+             "gates formed inside; y and the new conv state formed in chunk_state's launch)"),
             ("prefill_prep", "prefill", ("prep_kernel",), "gdn_conv_gate_prep, T=4096 Hv=48 bf16"),
             ("prefill_norm", "prefill", ("norm_kernel<gdn::bf16_t, false>",), "gdn_gated_rmsnorm, T=4096 Hv=48 bf16"),
             ("decode_b64", "decode_b64", ("decode_kernel",), "gdn_decode_step, batch 64, Hv=32"),
@@ -332,6 +333,9 @@ def bench_prefill(steps: int, warmup: int, wid: int = 3, three_call: bool = True
     del g
     best = min(modes, key=lambda m: modes[m]["ms_per_step"])
     n_chunk_heads = sum((L + CHUNK - 1) // CHUNK for L in lens) * w.n_v_heads
+    # gdn_prefill_fused forms y inside chunk_state's launch when its 4 blocks
+    # per (sequence, V-head), in whole rounds of the 8 XCDs, leave >= 32 CUs.
+    folded = 256 - (len(lens) * w.n_v_heads + 7) // 8 * 8 * 4 >= 32
     flops = FLOP_PER_CHUNK_HEAD * n_chunk_heads
     out = dict(workload=w.name, tokens=T, best=best, ms_per_step=modes[best]["ms_per_step"],
                total_ms=modes[best]["ms_per_step"] * steps, core_ms=core_ms,
@@ -341,9 +345,11 @@ def bench_prefill(steps: int, warmup: int, wid: int = 3, three_call: bool = True
                                        "call in the three-call step", "prefill_core" if wid == 3 else None),
                roofline_fused=_core_roofline(
                    flops, fused_call_ms,
-                   "gdn_prefill_fused, the whole call (the chunked kernels with the conv, SiLU, L2 norm and gates "
-                   "folded in, and the norm launch): HIP events around each call; a lower bound on the chunked "
-                   "kernels' own fraction", None))
+                   "gdn_prefill_fused, the whole call, HIP events around each call: chunk_local and chunk_state "
+                   "with the conv, SiLU, L2 norm and gates folded in, and " +
+                   ("the gated RMSNorm and new conv states formed in chunk_state's launch (on the CUs its "
+                    "sequential blocks leave idle)" if folded else "a third launch for the norm and conv states"),
+                   "prefill_fused_core" if wid == 3 and folded else None))
     out["roofline"]["median_launch_us"] = round(float(np.median(core_per)) * 1e3, 2)
     out["roofline"]["min_launch_us"] = round(float(np.min(core_per)) * 1e3, 2)
     out["roofline_fused"]["median_launch_us"] = round(float(np.median(fper)) * 1e3, 2)

@@ -251,11 +251,19 @@ static size_t fused_o_offset(const gdn_config *cfg, int32_t n_seqs, int32_t n_to
   return (base + 255) / 256 * 256;
 }
 
+// Then the folded norm's counters, one uint32 per (chunk, V-head), 256-byte
+// aligned.
+static size_t fused_ready_offset(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens) {
+  const size_t end = fused_o_offset(cfg, n_seqs, n_tokens) +
+                     static_cast<size_t>(n_tokens) * cfg->n_v_heads * kHeadDim * act_size(cfg);
+  return (end + 255) / 256 * 256;
+}
+
 size_t gdn_prefill_fused_workspace_bytes(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens) {
   if (check_config(cfg) != GDN_OK || n_seqs < 0 || n_tokens < 0) return 0;
   if (n_tokens == 0) return 0;
-  return fused_o_offset(cfg, n_seqs, n_tokens) +
-         static_cast<size_t>(n_tokens) * cfg->n_v_heads * kHeadDim * act_size(cfg);
+  return fused_ready_offset(cfg, n_seqs, n_tokens) +
+         static_cast<size_t>(gdn::max_chunks(n_seqs, n_tokens)) * cfg->n_v_heads * gdn::kReadyStride * sizeof(uint32_t);
 }
 
 gdn_status gdn_prefill_fused_ckpt(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens,
@@ -347,9 +355,23 @@ gdn_status gdn_prefill_fused_ckpt(const gdn_config *cfg, int32_t n_seqs, int32_t
   p.S_ckpt = ckpt ? S_ckpt : nullptr;
   p.ckpt_chunks = ckpt ? ckpt_every / gdn::kChunk : 0;
   p.ckpt_cap = ckpt ? ckpt_cap : 0;
-  hipError_t e = gdn::launch_prefill(p, cfg->act_dtype, hs);
-  if (e == hipSuccess && ckpt && conv_ckpt && n_tokens > 0) {
-    // Conv-state planes, before the last launch may update the conv state in place.
+  // The gated RMSNorm and the new conv states are formed inside the
+  // sequential kernel's launch when that leaves CUs idle, else by a launch of
+  // their own after it.
+  p.fold_blocks = n_tokens > 0 ? gdn::prefill_fold_blocks(n_seqs, Hv) : 0;
+  if (p.fold_blocks > 0) {
+    p.ready = reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(workspace) +
+                                           fused_ready_offset(cfg, n_seqs, n_tokens));
+    p.z = z;
+    p.norm_w = norm_w;
+    p.y = y;
+    p.norm_eps = cfg->norm_eps;
+    p.st_out = conv_state_out;
+  }
+  hipError_t e = hipSuccess;
+  if (ckpt && conv_ckpt && n_tokens > 0) {
+    // Conv-state planes, first: they read the old conv state, which the
+    // launches below may update in place.
     gdn::ConvCkptParams cp;
     cp.cu = cu_seqlens;
     cp.n_seqs = n_seqs;
@@ -363,7 +385,8 @@ gdn_status gdn_prefill_fused_ckpt(const gdn_config *cfg, int32_t n_seqs, int32_t
     cp.ckpt = conv_ckpt;
     e = gdn::launch_conv_ckpt(cp, cfg->act_dtype, hs);
   }
-  if (e == hipSuccess) {
+  if (e == hipSuccess) e = gdn::launch_prefill(p, cfg->act_dtype, hs);
+  if (e == hipSuccess && p.fold_blocks == 0) {
     // The norm, and the new conv states: last, since the kernels above read
     // the old conv state (in-place safe).
     gdn::NormParams np;

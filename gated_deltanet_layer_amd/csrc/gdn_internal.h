@@ -139,12 +139,29 @@ struct PrefillParams {
   const float *conv_w, *dt_bias, *A_log;
   float l2_eps;
   int l2_mode;
+  // Fused form with the gated RMSNorm folded into chunk_state (fold_blocks >
+  // 0): fold_blocks extra blocks of that launch form y from o, z and norm_w
+  // as the slab blocks finish each (chunk, V-head); ready holds one counter
+  // per (chunk, V-head), zeroed by chunk_local.
+  const void *z;
+  const float *norm_w;
+  void *y;
+  float norm_eps;
+  uint32_t *ready;
+  int fold_blocks;
+  void *st_out;        // the new conv states (may be st_in)
 };
 // Upper bound on the number of chunks over all sequences.
 inline int64_t max_chunks(int n_seqs, int n_tokens) {
   return (static_cast<int64_t>(n_tokens) + kChunk - 1) / kChunk + n_seqs;
 }
 size_t prefill_workspace_bytes(int n_seqs, int n_tokens, int n_qk, int n_v);
+// uint32 words per ready counter of the folded norm (one 128-byte line each).
+constexpr int kReadyStride = 32;
+// Blocks of the folded norm for a fused prefill over n_seqs sequences and
+// n_v V-heads: the CUs the sequential kernel leaves idle, or 0 (the norm then
+// runs as a launch of its own).
+int prefill_fold_blocks(int n_seqs, int n_v);
 hipError_t launch_prefill(const PrefillParams &p, gdn_dtype act, hipStream_t s);
 
 }  // namespace gdn

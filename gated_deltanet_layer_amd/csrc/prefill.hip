@@ -556,6 +556,202 @@ __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(PrefillParam
       FragIO<P>::store(wv, kChunk / 32, brt, bks, make_frag<P>(ta, tb));
     }
   }
+  // Folded norm: the ready counters of this chunk's V-heads start at zero
+  // (the next launch sees them at zero: a kernel boundary orders the two).
+  if constexpr (kFused) {
+    if (p.fold_blocks > 0)
+      for (int u = tid; u < nvh; u += kLocalThreads)
+        p.ready[(static_cast<size_t>(cid) * p.n_v + h + u * p.n_qk) * kReadyStride] = 0u;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Folded gated RMSNorm and new conv state (fused form, when chunk_state's
+// slab blocks leave CUs idle). A row's norm needs all 128 columns of o, which
+// four slab blocks produce. Instead of a launch of its own after chunk_state,
+// extra "norm blocks" of the same launch, on the idle CUs, form y chunk by
+// chunk as the slab blocks finish:
+//  * each y-wave of a slab block stores its o rows of chunk c, and at the top
+//    of the iteration after next (its loads of the iteration between must
+//    land there anyway) waits for its memory operations and adds 1 to the
+//    ready counter of (chunk, V-head);
+//  * the norm wave that owns a quarter (16 rows) of the pair polls the
+//    counter until it reads 16 (4 slab blocks x 4 y-waves), then normalises
+//    those rows exactly as the norm kernel does.
+// Publication across XCDs (each has its own L2): o is written with
+// agent-scope atomic stores and read with agent-scope atomic loads, which
+// the compiler emits as device-coherent accesses (sc1) with no cache
+// maintenance; the counter is an agent-scope atomic. The writer's wait for
+// all of its memory operations before the add orders its o stores before
+// the add, and the reader issues its o loads only after its counter load
+// returned 16. This is the ordering a release/acquire pair gives, minus the
+// whole-L2 write-back and invalidate that such a pair emits on this chip
+// for plain accesses (measured: 1.8 ms instead of 0.24 ms per fused step).
+// z and y go through with non-temporal accesses: kept out of L2, where the
+// slab blocks share their K, Q, Tm and P operands (16 us per step).
+// Counters sit 128 bytes apart: polls and adds of neighbouring pairs on one
+// line slowed the step by tens of us.
+// Norm blocks only ever wait for slab blocks, never the reverse, so the
+// launch drains in whatever order its blocks are placed; each wave's polls
+// are bounded in total (about a second), and rows whose counter never
+// completes (only cu_seqlens outside the contract leave one short) get NaN.
+// The same norm waves write the new conv states: the V channels of head j
+// once the counter of the sequence's first chunk of j is full (the four slab
+// blocks of j read the old state only before that chunk, so the update can
+// be in place), the q and k channels of K-head h (read only by chunk_local,
+// in the launch before) with those of V-head h, and whole states of
+// sequences without tokens (which nothing else reads) first.
+constexpr uint32_t kFoldReady = 16;       // 4 slab blocks x 4 y-waves
+constexpr int kFoldSleep = 48;            // s_sleep units (64 cycles) between polls
+constexpr int kFoldSpins = 1 << 20;       // polls per wave, each a load and a sleep
+
+__device__ __forceinline__ void fold_put4(bf16_t *o, size_t i, f32x4 a) {
+  const uint64_t w = static_cast<uint64_t>(f32_to_bf16(a[0])) | (static_cast<uint64_t>(f32_to_bf16(a[1])) << 16) |
+                     (static_cast<uint64_t>(f32_to_bf16(a[2])) << 32) |
+                     (static_cast<uint64_t>(f32_to_bf16(a[3])) << 48);
+  __hip_atomic_store(reinterpret_cast<uint64_t *>(o + i), w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void fold_put4(float *o, size_t i, f32x4 a) {
+  uint64_t *d = reinterpret_cast<uint64_t *>(o + i);
+  __hip_atomic_store(d, (static_cast<uint64_t>(__float_as_uint(a[1])) << 32) | __float_as_uint(a[0]),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(d + 1, (static_cast<uint64_t>(__float_as_uint(a[3])) << 32) | __float_as_uint(a[2]),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t fold_ld64(const void *p) {
+  return __hip_atomic_load(reinterpret_cast<uint64_t *>(const_cast<void *>(p)), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float4 bf16x4_f4(uint32_t x, uint32_t y) {
+  return make_float4(__uint_as_float(x << 16), __uint_as_float(x & 0xffff0000u), __uint_as_float(y << 16),
+                     __uint_as_float(y & 0xffff0000u));
+}
+__device__ __forceinline__ void fold_get8(const bf16_t *o, size_t i, float4 &a, float4 &b) {
+  const uint64_t u = fold_ld64(o + i), v = fold_ld64(o + i + 4);
+  a = bf16x4_f4(static_cast<uint32_t>(u), static_cast<uint32_t>(u >> 32));
+  b = bf16x4_f4(static_cast<uint32_t>(v), static_cast<uint32_t>(v >> 32));
+}
+__device__ __forceinline__ void fold_get8(const float *o, size_t i, float4 &a, float4 &b) {
+  const uint64_t u0 = fold_ld64(o + i), u1 = fold_ld64(o + i + 2), u2 = fold_ld64(o + i + 4), u3 = fold_ld64(o + i + 6);
+  a = make_float4(__uint_as_float(static_cast<uint32_t>(u0)), __uint_as_float(static_cast<uint32_t>(u0 >> 32)),
+                  __uint_as_float(static_cast<uint32_t>(u1)), __uint_as_float(static_cast<uint32_t>(u1 >> 32)));
+  b = make_float4(__uint_as_float(static_cast<uint32_t>(u2)), __uint_as_float(static_cast<uint32_t>(u2 >> 32)),
+                  __uint_as_float(static_cast<uint32_t>(u3)), __uint_as_float(static_cast<uint32_t>(u3 >> 32)));
+}
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void fold_in8(const bf16_t *z, size_t i, float4 &a, float4 &b) {
+  const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(z + i));
+  a = bf16x4_f4(w[0], w[1]);
+  b = bf16x4_f4(w[2], w[3]);
+}
+__device__ __forceinline__ void fold_in8(const float *z, size_t i, float4 &a, float4 &b) {
+  const f32x4 u = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(z + i));
+  const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(z + i + 4));
+  a = make_float4(u[0], u[1], u[2], u[3]);
+  b = make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void fold_out8(bf16_t *y, size_t i, float4 a, float4 b) {
+  const u32x4 w = {static_cast<uint32_t>(f32_to_bf16(a.x)) | (static_cast<uint32_t>(f32_to_bf16(a.y)) << 16),
+                   static_cast<uint32_t>(f32_to_bf16(a.z)) | (static_cast<uint32_t>(f32_to_bf16(a.w)) << 16),
+                   static_cast<uint32_t>(f32_to_bf16(b.x)) | (static_cast<uint32_t>(f32_to_bf16(b.y)) << 16),
+                   static_cast<uint32_t>(f32_to_bf16(b.z)) | (static_cast<uint32_t>(f32_to_bf16(b.w)) << 16)};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(y + i));
+}
+__device__ __forceinline__ void fold_out8(float *y, size_t i, float4 a, float4 b) {
+  const f32x4 u = {a.x, a.y, a.z, a.w}, v = {b.x, b.y, b.z, b.w};
+  __builtin_nontemporal_store(u, reinterpret_cast<f32x4 *>(y + i));
+  __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(y + i + 4));
+}
+
+// One norm block (block fb of p.fold_blocks). Work items are 16-row quarters
+// of (chunk, V-head) pairs, so that the pairs of the last chunk, ready only
+// as the slab blocks end, spread over four times as many waves. Wave w owns
+// items i = g, g + G, ... with g = w * fold_blocks + fb and G the number of
+// norm waves (consecutive items on different CUs). 16 lanes per row (8
+// values each), 4 rows per pass, all 16 rows' loads in flight together.
+template <typename TA>
+__device__ __forceinline__ void fold_norm(const PrefillParams &p, int64_t max_chunks, int fb) {
+  constexpr int kWaves = kStateThreads / kWave;
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int sub = lane & 15, r4 = lane >> 4;
+  const int64_t g = static_cast<int64_t>(wave) * p.fold_blocks + fb;
+  const int64_t G = static_cast<int64_t>(p.fold_blocks) * kWaves;
+  const size_t stride = static_cast<size_t>(p.n_v) * kHeadDim;
+  const TA *o = static_cast<const TA *>(p.o);
+  const TA *z = static_cast<const TA *>(p.z);
+  TA *y = static_cast<TA *>(p.y);
+  ConvStateParams cp;
+  cp.cu = p.cu;
+  cp.n_seqs = p.n_seqs;
+  cp.n_tokens = p.n_tokens;
+  cp.C = kHeadDim * (2 * p.n_qk + p.n_v);
+  cp.qkv = p.qkv;
+  cp.st_in = p.st_in;
+  cp.st_out = p.st_out;
+  for (int64_t n = g; n < p.n_seqs; n += G)
+    if (p.cu[n + 1] == p.cu[n])
+      for (int c = 2 * lane; c < cp.C; c += 2 * kWave) conv_state_pair<TA>(cp, static_cast<int>(n), c);
+
+  const float4 w0 = *reinterpret_cast<const float4 *>(p.norm_w + 8 * sub);
+  const float4 w1 = *reinterpret_cast<const float4 *>(p.norm_w + 8 * sub + 4);
+  const int64_t items = max_chunks * p.n_v * 4;
+  int spins = 0;   // over all of the wave's items
+  for (int64_t it = g; it < items; it += G) {
+    const int64_t t = it >> 2;
+    const int rb = 16 * static_cast<int>(it & 3);
+    const int cid = static_cast<int>(t / p.n_v), j = static_cast<int>(t % p.n_v);
+    int n, ci;
+    if (!find_unit(p.cu, p.n_seqs, cid, kChunk, 0, &n, &ci)) break;   // every later item is past the last chunk
+    const int seq0 = p.cu[n];
+    const int L = p.cu[n + 1] - seq0;
+    if (seq0 < 0 || L < 0 || seq0 + L > p.n_tokens) continue;   // skipped by the slab blocks too
+    const int t0 = seq0 + ci * kChunk;
+    const int len = min(kChunk, L - ci * kChunk);
+    if (rb >= len) continue;
+    const uint32_t *rdy = p.ready + t * kReadyStride;
+    uint32_t cnt = __hip_atomic_load(rdy, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    while (__builtin_amdgcn_readfirstlane(cnt) < kFoldReady && spins < kFoldSpins) {
+      __builtin_amdgcn_s_sleep(kFoldSleep);
+      cnt = __hip_atomic_load(rdy, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ++spins;
+    }
+    const bool ok = __builtin_amdgcn_readfirstlane(cnt) >= kFoldReady;
+    float4 o0[4], o1[4], z0[4], z1[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int row = min(rb + 4 * u + r4, len - 1);
+      const size_t i = static_cast<size_t>(t0 + row) * stride + static_cast<size_t>(j) * kHeadDim + 8 * sub;
+      fold_get8(o, i, o0[u], o1[u]);
+      fold_in8(z, i, z0[u], z1[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int row = rb + 4 * u + r4;
+      float ss = o0[u].x * o0[u].x + o0[u].y * o0[u].y + o0[u].z * o0[u].z + o0[u].w * o0[u].w +
+                 o1[u].x * o1[u].x + o1[u].y * o1[u].y + o1[u].z * o1[u].z + o1[u].w * o1[u].w;
+      ss = row16_sum(ss);
+      const float inv = ok ? 1.0f / sqrtf(ss * (1.0f / kHeadDim) + p.norm_eps) : __builtin_nanf("");
+      float4 y0, y1;
+      y0.x = o0[u].x * inv * w0.x * siluf_(z0[u].x);
+      y0.y = o0[u].y * inv * w0.y * siluf_(z0[u].y);
+      y0.z = o0[u].z * inv * w0.z * siluf_(z0[u].z);
+      y0.w = o0[u].w * inv * w0.w * siluf_(z0[u].w);
+      y1.x = o1[u].x * inv * w1.x * siluf_(z1[u].x);
+      y1.y = o1[u].y * inv * w1.y * siluf_(z1[u].y);
+      y1.z = o1[u].z * inv * w1.z * siluf_(z1[u].z);
+      y1.w = o1[u].w * inv * w1.w * siluf_(z1[u].w);
+      if (row < len)
+        fold_out8(y, static_cast<size_t>(t0 + row) * stride + static_cast<size_t>(j) * kHeadDim + 8 * sub, y0, y1);
+    }
+    if (ok && ci == 0 && rb == 0) {
+      conv_state_pair<TA>(cp, n, kHeadDim * (2 * p.n_qk + j) + 2 * lane);
+      if (j < p.n_qk) {
+        conv_state_pair<TA>(cp, n, kHeadDim * j + 2 * lane);
+        conv_state_pair<TA>(cp, n, kHeadDim * (p.n_qk + j) + 2 * lane);
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -782,6 +978,13 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
   // of (sequence, V-head) pair 8 g + x, so the 4 slabs of a pair, and the
   // V-heads j, j + 8, ... that share K-head operands, run on one XCD and
   // share its L2.
+  if constexpr (kFused) {
+    const int first_fold = static_cast<int>(gridDim.x) - p.fold_blocks;
+    if (p.fold_blocks > 0 && static_cast<int>(blockIdx.x) >= first_fold) {
+      fold_norm<TA>(p, max_chunks, blockIdx.x - first_fold);
+      return;
+    }
+  }
   const int nslab = kHeadDim / kSlab;
   const int pair = kXcds * (blockIdx.x / (kXcds * nslab)) + blockIdx.x % kXcds;
   const int slab = (blockIdx.x / kXcds) % nslab;
@@ -966,8 +1169,23 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
     const f32x4 b = *reinterpret_cast<const f32x4 *>(src + 4);
     if (16 * rt + orow < len_) {
       const size_t dst = (t0_ + 16 * rt + orow) * v_stride + j * kHeadDim + col_base + oc;
-      Act<TA>::store4(o, dst, make_float4(a[0], a[1], a[2], a[3]));
-      Act<TA>::store4(o, dst + 4, make_float4(b[0], b[1], b[2], b[3]));
+      if (kFused && p.fold_blocks > 0) {
+        fold_put4(o, dst, a);
+        fold_put4(o, dst + 4, b);
+      } else {
+        Act<TA>::store4(o, dst, make_float4(a[0], a[1], a[2], a[3]));
+        Act<TA>::store4(o, dst + 4, make_float4(b[0], b[1], b[2], b[3]));
+      }
+    }
+  };
+  // Folded norm: this y-wave's o rows of chunk c are stored; count them in.
+  auto publish = [&](int c) {
+    if constexpr (kFused) {
+      if (p.fold_blocks > 0) {
+        uint32_t *ctr = p.ready + (static_cast<size_t>(cid0 + c) * p.n_v + j) * kReadyStride;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the o stores have completed
+        if (lane == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   };
 
@@ -1099,6 +1317,10 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
     for (int ci = 0; ci < nchunks; ++ci) {
       const int cn = min(ci + 1, nchunks - 1);
       block_sync_lds();                      // S, V, gam of chunk ci visible
+      // Chunk ci - 2's o rows went out in the last iteration, and this
+      // wave's loads of then are needed now: counting them in waits for
+      // nothing else.
+      if (ci >= 2) publish(ci - 2);
       const float g_end = G_s[kChunk - 1];
       // 1. Y = Q S, rows 16 rt, both column tiles.
       f32x4 Y[2];
@@ -1121,9 +1343,11 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
     // O of the last chunk (its D was made visible by the loop's barriers).
     if (nchunks > 0) {
       const int cl = nchunks - 1;
+      if (cl >= 1) publish(cl - 1);
       f32x4 acc[2] = {oy[0], oy[1]};
       times_mat(fp, Dtb[cl & 1], acc);
       store_o(cl, acc);
+      publish(cl);
     }
   }
 #undef GDN_LOAD_ROWS
@@ -1143,6 +1367,14 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
 
 }  // namespace
 
+int prefill_fold_blocks(int n_seqs, int n_v) {
+  constexpr int64_t kCUs = 256, kMinFold = 32, kMaxFold = 64;
+  const int64_t pairs = static_cast<int64_t>(n_seqs) * n_v;
+  const int64_t slab_blocks = (pairs + kXcds - 1) / kXcds * kXcds * (kHeadDim / kSlab);
+  const int64_t idle = kCUs - slab_blocks;
+  return idle >= kMinFold ? static_cast<int>(idle < kMaxFold ? idle : kMaxFold) : 0;
+}
+
 size_t prefill_workspace_bytes(int n_seqs, int n_tokens, int n_qk, int n_v) {
   const int64_t chunks = max_chunks(n_seqs, n_tokens);
   return static_cast<size_t>(chunks) * (n_qk * kQkBytes + n_v * (kVBytes + kChunk * sizeof(double)));
@@ -1152,7 +1384,8 @@ hipError_t launch_prefill(const PrefillParams &p, gdn_dtype act, hipStream_t s) 
   const int64_t chunks = max_chunks(p.n_seqs, p.n_tokens);
   const dim3 grid_local(static_cast<unsigned>(chunks), static_cast<unsigned>(p.n_qk));
   const int64_t pairs = static_cast<int64_t>(p.n_seqs) * p.n_v;
-  const dim3 grid_state(static_cast<unsigned>((pairs + kXcds - 1) / kXcds * kXcds * (kHeadDim / kSlab)));
+  const dim3 grid_state(static_cast<unsigned>((pairs + kXcds - 1) / kXcds * kXcds * (kHeadDim / kSlab) +
+                                             (p.qkv != nullptr ? p.fold_blocks : 0)));
   const bool fused = p.qkv != nullptr;
 #define GDN_LAUNCH(PR, TA, FU)                                                                                \
   do {                                                                                                        \

@@ -206,13 +206,16 @@ GDN_API gdn_status gdn_state_check(const float *S, int64_t n_values, int32_t *st
  *   qkv [T][C], beta_logit, alpha_logit [T][Hv], z, y [T][Hv][d]: act dtype
  *   conv_w [C][4], dt_bias, A_log [Hv], norm_w [d]: fp32
  *   conv_state_in, conv_state_out [N][3][C]: act dtype; may be the same
- *     buffer (the new state is written last)
+ *     buffer (each part of the old state is read before it is replaced)
  *   S_in, S_out [N][Hv][d][d]: fp32; may be the same buffer
  * qkv, conv_w and both conv states must be 16-byte aligned; `workspace`
  * 256-byte aligned, of gdn_prefill_fused_workspace_bytes(cfg, n_seqs,
- * n_tokens) bytes (may be NULL when that is 0). Three kernels on `stream`; the last
- * writes y and the new conv state. z, y and norm_w must be 16-byte aligned
- * too.
+ * n_tokens) bytes (may be NULL when that is 0). z, y and norm_w must be
+ * 16-byte aligned too. Kernels on `stream`: two when the sequential pass
+ * (4 blocks per sequence and V-head) leaves at least 32 of the chip's 256
+ * CUs idle, whose idle CUs then form y and the new conv state as the pass
+ * produces o; otherwise three, the last a norm launch that writes y and the
+ * new conv state.
  */
 GDN_API gdn_status gdn_prefill_fused(const gdn_config *cfg, int32_t n_seqs, int32_t n_tokens,
                              const int32_t *cu_seqlens, const void *qkv, const void *beta_logit,

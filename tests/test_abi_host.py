@@ -61,6 +61,16 @@ def test_workspace_size(lib):
     chunks = 64 + 1
     assert B.gdn_prefill_workspace_bytes(cfg, 1, 4096) == chunks * (16 * 2 * 64 * 128 * 4 + 48 * (2 * 64 * 64 * 4 + 64 * 8))
     assert B.gdn_prefill_workspace_bytes(cfg, 1, 0) == 0
+    # Fused: the chunked workspace, o (act dtype) and one 128-byte ready
+    # counter per (chunk, V-head), each part starting 256-byte aligned.
+    up = lambda v: (v + 255) // 256 * 256
+    for act, asz in (("bf16", 2), ("f32", 4)):
+        c = B.make_config(16, 48, act)
+        for n, t in ((1, 4096), (3, 1000), (2, 1)):
+            ch = (t + 63) // 64 + n
+            base = ch * (16 * 2 * 64 * 128 * 4 + 48 * (2 * 64 * 64 * 4 + 64 * 8))
+            assert B.gdn_prefill_fused_workspace_bytes(c, n, t) == up(up(base) + t * 48 * 128 * asz) + ch * 48 * 128
+    assert B.gdn_prefill_fused_workspace_bytes(cfg, 1, 0) == 0
     bad = B.make_config(16, 40)
     assert B.gdn_prefill_workspace_bytes(bad, 1, 64) == 0
 

@@ -92,6 +92,81 @@ def test_fused_packed_equals_separate_runs():
         assert np.array_equal(one["conv_out_bits"][0], packed["conv_out_bits"][n])
 
 
+def _norm_folded(n_seqs, hv):
+    """Whether gdn_prefill_fused forms y and the new conv states inside the
+    sequential kernel's launch: its 4 blocks per (sequence, V-head), rounded
+    up to whole rounds of the 8 XCDs, leave at least 32 of the 256 CUs idle."""
+    return 256 - (n_seqs * hv + 7) // 8 * 8 * 4 >= 32
+
+
+# (lengths, Hqk, Hv): the folded norm (20 pairs, 96 sequential blocks) and the
+# norm launch (60 pairs, 256 sequential blocks), both with empty sequences.
+FOLD_CASES = [([0, 65, 130, 0, 3], 2, 4),
+              ([40, 0, 1, 64, 2, 100, 7, 0, 12, 33, 5, 70, 9, 0, 90], 2, 4)]
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+@pytest.mark.parametrize("case", [0, 1], ids=["folded", "norm_launch"])
+def test_fused_norm_folded_and_apart(case, act):
+    """Both forms of the call against the oracle, and in-place states equal
+    to out-of-place ones (the folded form overwrites each part of the old conv
+    state inside the launch that reads it)."""
+    lens, hqk, hv = FOLD_CASES[case]
+    assert _norm_folded(len(lens), hv) == (case == 0)
+    w = wl.custom("prefill", len(lens), hqk, hv, act, seed=508 + case, lengths=lens, s0_std=0.02, conv0_std=1.0)
+    x = wl.generate(w)
+    say(f"case fused {'folded' if case == 0 else 'norm launch'} {lens} Hqk={hqk} Hv={hv} {act}")
+    a = P.gpu_prefill_fused(w, x)
+    compare_prefill(w, x, a)
+    b = P.gpu_prefill_fused(w, x, inplace=True)
+    for k in ("y", "S_out", "conv_out_bits"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("case", [0, 1], ids=["folded", "norm_launch"])
+def test_fused_graph_replay_matches_eager(case):
+    """The fused prefill captured in a HIP graph: every replay, with eager
+    work and synchronisations between replays, equals the eager call bit for
+    bit (the folded form's counters are cleared by a kernel of the call, not a
+    memset)."""
+    import torch
+    from gated_deltanet_layer_amd import binding as B
+    from gated_deltanet_layer_amd import layer as Lyr
+    lens, hqk, hv = FOLD_CASES[case]
+    w = wl.custom("prefill", len(lens), hqk, hv, "bf16", seed=510 + case, lengths=lens, s0_std=0.02,
+                  conv0_std=1.0)
+    x = wl.generate(w)
+    t = {k: P.dev(v) for k, v in x.items()}
+    run = Lyr.PrefillFused(B.make_config(hqk, hv, "bf16"), len(lens), sum(lens))
+    conv_out, S_out = torch.empty_like(t["conv0"]), torch.empty_like(t["S0"])
+
+    def step():
+        run(t["cu_seqlens"], t["qkv"], t["z"], t["b"], t["a"], t["conv_w"], t["dt_bias"], t["A_log"],
+            t["norm_w"], t["conv0"], conv_out, t["S0"], S_out)
+
+    def state():
+        return P.bits(run.y).copy(), P.bits(S_out).copy(), P.bits(conv_out).copy()
+
+    say(f"case fused graph replay ({'folded' if case == 0 else 'norm launch'}): eager")
+    step()
+    torch.cuda.synchronize()
+    ref = state()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        say(f"  replay {rep}")
+        run.y.zero_()
+        S_out.zero_()
+        conv_out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("y", "S", "conv"), state(), ref):
+            assert np.array_equal(a, b), f"replay {rep}: {name} differs from the eager call"
+        (t["z"].float() * 2.0).sum().item()
+
+
 def test_fused_l2_rsqrt_form():
     w = wl.custom("prefill", 2, 2, 4, "bf16", seed=506, lengths=[100, 37], s0_std=0.02, conv0_std=1.0)
     x = wl.generate(w)
