@@ -234,34 +234,52 @@ __device__ __forceinline__ int tri(int r, int m) { return r * (r + 1) / 2 + m; }
 // Orders this wave's earlier LDS accesses before its later ones.
 __device__ __forceinline__ void wave_sync_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// LDS of one chunk_local unit, carved from one byte array (so that a block
+// of the sequential kernel can hold two units):
+//   buf: K as blocked operand rows first; then the solving waves' fp32
+//        matrices (L, overwritten in place by L^-1) reuse the bytes
+//   Wtap (fused): conv taps of the K-head's q and k channels
+//   gam_s, bet_s: per solving wave; Gk, Gq: K K^T and Q K^T, lower
+//   triangles; Tsc: per solving wave, an off-diagonal block in transit
+struct LocalLds {
+  static constexpr int kKbBytes = kChunk * kPitch128;
+  static constexpr int kLxBytes = kSolveWaves * kChunk * kLdS * 4;
+  static constexpr size_t kBuf = 0;
+  static constexpr size_t kWtap = (kKbBytes > kLxBytes ? kKbBytes : kLxBytes);
+  static constexpr size_t kGam = kWtap + 2 * kHeadDim * sizeof(float4);
+  static constexpr size_t kGk = kGam + kSolveWaves * kChunk * sizeof(double);
+  static constexpr size_t kGq = kGk + kTri * sizeof(float);
+  static constexpr size_t kTsc = kGq + kTri * sizeof(float);
+  static constexpr size_t kBet = kTsc + kSolveWaves * 16 * 17 * sizeof(float);
+  static constexpr size_t kBytes = kBet + kSolveWaves * kChunk * sizeof(float);
+};
+static_assert(LocalLds::kWtap % 16 == 0 && LocalLds::kGam % 8 == 0, "LDS carve alignment");
+
+// One (chunk, K-head) unit of chunk_local: unit cid = chunk ci of sequence n
+// (a valid one), K-head h, on 4 waves (tid 0 .. 255 of them) with the LDS at
+// smem. Every barrier is taken by the whole block, the same number of times
+// whatever the unit, so two units can run side by side in one block. live =
+// false runs a unit without any global store (a block's second slot with no
+// unit of its own).
 template <Prec P, typename TA, bool kFused>
-__global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(PrefillParams p, int64_t max_chunks) {
+__device__ __forceinline__ void local_unit(const PrefillParams &p, int64_t max_chunks, int cid, int n, int ci, int h,
+                                           uint8_t *smem, int tid, bool live) {
   using Frag = typename Op<P>::Frag;
-  // K as blocked operand rows first; then the solving waves' fp32 matrices
-  // (L, overwritten in place by L^-1) reuse the bytes.
-  constexpr int kKbBytes = kChunk * kPitch128;
-  constexpr int kLxBytes = kSolveWaves * kChunk * kLdS * 4;
-  __shared__ __attribute__((aligned(16))) uint8_t buf[kKbBytes > kLxBytes ? kKbBytes : kLxBytes];
-  __shared__ float Gk[kTri];                  // K K^T, lower triangle
-  __shared__ float Gq[kTri];                  // Q K^T, lower triangle
-  __shared__ float Tsc[kSolveWaves][16 * 17];
-  __shared__ double gam_s[kSolveWaves][kChunk];
-  __shared__ float bet_s[kSolveWaves][kChunk];
-  __shared__ float4 Wtap[kFused ? 2 * kHeadDim : 1];   // fused: conv taps of the q and k channels
+  uint8_t *buf = smem + LocalLds::kBuf;
+  float4 *Wtap = reinterpret_cast<float4 *>(smem + LocalLds::kWtap);
+  double (*gam_s)[kChunk] = reinterpret_cast<double (*)[kChunk]>(smem + LocalLds::kGam);
+  float *Gk = reinterpret_cast<float *>(smem + LocalLds::kGk);
+  float *Gq = reinterpret_cast<float *>(smem + LocalLds::kGq);
+  float (*Tsc)[16 * 17] = reinterpret_cast<float (*)[16 * 17]>(smem + LocalLds::kTsc);
+  float (*bet_s)[kChunk] = reinterpret_cast<float (*)[kChunk]>(smem + LocalLds::kBet);
   uint8_t *Kb = buf;
 
-  const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = lane_id();
-  const int h = blockIdx.y;
-  int n, ci;
-  if (!find_unit(p.cu, p.n_seqs, blockIdx.x, kChunk, 0, &n, &ci)) return;
   const int seq0 = p.cu[n];
   const int L = p.cu[n + 1] - seq0;
-  if (seq0 < 0 || L < 0 || seq0 + L > p.n_tokens) return;
   const int t0 = seq0 + ci * kChunk;
   const int len = min(kChunk, L - ci * kChunk);
-  const int cid = blockIdx.x;
   const Workspace ws = carve(p.ws, max_chunks, p.n_qk, p.n_v);
   const size_t qk_stride = static_cast<size_t>(p.n_qk) * kHeadDim;
   const float *kg = kFused ? nullptr : p.k + t0 * qk_stride + h * kHeadDim;
@@ -373,15 +391,17 @@ __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(PrefillParam
   // their loads after it would also wait for the stores).
   float g_first_v = 0.f, b_first_v = 0.f;
   if (wave < min(nvh, kSolveWaves)) form_gates(wave, g_first, b_first, g_first_v, b_first_v);
+  if (live)
 #pragma unroll
-  for (int ks = 0; ks < kHeadDim / 32; ++ks) FragIO<P>::store(wk + kKBytes, kHeadDim / 32, rt, ks, fq[ks]);
+    for (int ks = 0; ks < kHeadDim / 32; ++ks) FragIO<P>::store(wk + kKBytes, kHeadDim / 32, rt, ks, fq[ks]);
   block_sync_lds();
 
   // K rows (4 x 4 blocks) to the workspace, read out of LDS a whole
   // fragment at a time: wave w stores blocks w, w + 4, ..
+  if (live)
 #pragma unroll
-  for (int b = wave; b < 16; b += 4)
-    FragIO<P>::store(wk, kHeadDim / 32, b >> 2, b & 3, frag<P>(Kb, kPitch128, 16 * (b >> 2), 32 * (b & 3)));
+    for (int b = wave; b < 16; b += 4)
+      FragIO<P>::store(wk, kHeadDim / 32, b >> 2, b & 3, frag<P>(Kb, kPitch128, 16 * (b >> 2), 32 * (b & 3)));
   // Row tile rt of the lower triangles of K K^T and Q K^T.
   for (int ct = 0; ct <= rt; ++ct) {
     f32x4 ak = zero4, aq = zero4;
@@ -430,7 +450,7 @@ __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(PrefillParam
       const double gm = wave_inclusive_scan_d(gr);
       gam_s[wave][lane] = gm;
       bet_s[wave][lane] = br;
-      ws.gam[(static_cast<size_t>(cid) * p.n_v + j) * kChunk + lane] = gm;
+      if (live) ws.gam[(static_cast<size_t>(cid) * p.n_v + j) * kChunk + lane] = gm;
     }
     block_sync_lds();
 
@@ -472,7 +492,7 @@ __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(PrefillParam
         if (e < 4) pa[e] = pv; else pb[e - 4] = pv;
       }
       uint8_t *wv = ws.v + (static_cast<size_t>(cid) * p.n_v + j) * kVBytes;   // Tm, then P
-      FragIO<P>::store(wv + kMatBytes, kChunk / 32, brt, bks, make_frag<P>(pa, pb));
+      if (live) FragIO<P>::store(wv + kMatBytes, kChunk / 32, brt, bks, make_frag<P>(pa, pb));
     }
     block_sync_lds();
 
@@ -553,15 +573,28 @@ __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(PrefillParam
         if (e < 4) ta[e] = tv; else tb[e - 4] = tv;
       }
       uint8_t *wv = ws.v + (static_cast<size_t>(cid) * p.n_v + j) * kVBytes;
-      FragIO<P>::store(wv, kChunk / 32, brt, bks, make_frag<P>(ta, tb));
+      if (live) FragIO<P>::store(wv, kChunk / 32, brt, bks, make_frag<P>(ta, tb));
     }
   }
+}
+
+template <Prec P, typename TA, bool kFused>
+__global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(PrefillParams p, int64_t max_chunks) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LocalLds::kBytes];
+  const int h = blockIdx.y;
+  int n, ci;
+  if (!find_unit(p.cu, p.n_seqs, blockIdx.x, kChunk, 0, &n, &ci)) return;
+  const int seq0 = p.cu[n];
+  const int L = p.cu[n + 1] - seq0;
+  if (seq0 < 0 || L < 0 || seq0 + L > p.n_tokens) return;
+  local_unit<P, TA, kFused>(p, max_chunks, blockIdx.x, n, ci, h, smem, threadIdx.x, true);
   // Folded norm: the ready counters of this chunk's V-heads start at zero
   // (the next launch sees them at zero: a kernel boundary orders the two).
   if constexpr (kFused) {
+    const int nvh = p.n_v / p.n_qk;
     if (p.fold_blocks > 0)
-      for (int u = tid; u < nvh; u += kLocalThreads)
-        p.ready[(static_cast<size_t>(cid) * p.n_v + h + u * p.n_qk) * kReadyStride] = 0u;
+      for (int u = threadIdx.x; u < nvh; u += kLocalThreads)
+        p.ready[(static_cast<size_t>(blockIdx.x) * p.n_v + h + u * p.n_qk) * kReadyStride] = 0u;
   }
 }
 
@@ -949,22 +982,50 @@ __device__ __forceinline__ void mma_2x2(f32x4 (&c)[2][2], const typename Op<P>::
 // pending O stores never hold them up. The K^T fragments of the state update
 // are not loaded: the x-waves leave their K fragments in LDS and every wave
 // reads its K^T fragments from there.
+// LDS of a chunk_state block, carved from one byte array (16-byte aligned
+// parts):
+//   Stb: S, the B operand of K S and Q S, by chunk parity
+//   Rtb: R, the B operand of Tm R (2 x 2 blocks)
+//   Dtb: D, the B operand of P D, by chunk parity
+//   Dsb: diag(k~) D, the B operand of K^T (.)
+//   Vs:  V rows of the slab (fp32); Os: O staging, 16 rows per y-wave
+//   Ktb: K rows of the chunk (for the K^T fragments)
+//   Vw:  fused form, conv taps of the slab's V channels
+//   Vr:  fused form, raw V rows of the slab by chunk parity (rows 0 .. 2 are
+//        the three rows before the chunk, rows 3 .. 66 the chunk's own)
+//   G_s: exp(gam_r); Ksc: exp(gam_n - gam_r)
+template <Prec P, typename TA, bool kFused> struct StateLds {
+  static constexpr int kVrRows = kFused ? kChunk + kConvK - 1 : 1;
+  static constexpr size_t kStb = 0;
+  static constexpr size_t kRtb = kStb + 2 * 8 * kLdsBlk;
+  static constexpr size_t kDtb = kRtb + 4 * kLdsBlk;
+  static constexpr size_t kDsb = kDtb + 2 * 4 * kLdsBlk;
+  static constexpr size_t kVs = kDsb + 4 * kLdsBlk;
+  static constexpr size_t kOs = kVs + kChunk * kLdV * sizeof(float);
+  static constexpr size_t kKtb = kOs + 4 * 16 * kLdOs * sizeof(float);
+  static constexpr size_t kVw = kKtb + (KtLds<P>::kBytes + 15) / 16 * 16;
+  static constexpr size_t kVr = kVw + (kFused ? kSlab : 1) * sizeof(float4);
+  static constexpr size_t kG = kVr + ((kFused ? 2 : 1) * kVrRows * kSlab * sizeof(TA) + 15) / 16 * 16;
+  static constexpr size_t kKsc = kG + kChunk * sizeof(float);
+  static constexpr size_t kBytes = kKsc + kChunk * sizeof(float);
+};
+
 template <Prec P, typename TA, bool kFused, bool kCkpt>
 __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParams p, int64_t max_chunks) {
   using Frag = typename Op<P>::Frag;
-  __shared__ __attribute__((aligned(16))) uint8_t Stb[2][8 * kLdsBlk];   // S: B of K S, Q S, by chunk parity
-  __shared__ __attribute__((aligned(16))) uint8_t Rtb[4 * kLdsBlk];      // R: B of Tm R (2 x 2)
-  __shared__ __attribute__((aligned(16))) uint8_t Dtb[2][4 * kLdsBlk];   // D: B of P D, by chunk parity
-  __shared__ __attribute__((aligned(16))) uint8_t Dsb[4 * kLdsBlk];      // diag(k~) D: B of K^T (.)
-  __shared__ __attribute__((aligned(16))) float Vs[kChunk * kLdV];      // V rows of the slab (fp32)
-  __shared__ __attribute__((aligned(16))) float Os[4 * 16 * kLdOs];     // O staging, 16 rows per y-wave
-  __shared__ __attribute__((aligned(16))) uint8_t Ktb[KtLds<P>::kBytes];   // K rows of the chunk
-  __shared__ float4 Vw[kFused ? kSlab : 1];  // conv taps of the slab's V channels
-  // Fused form: raw V rows of the slab by chunk parity; rows 0 .. 2 are the
-  // three rows before the chunk, rows 3 .. 66 the chunk's own.
-  __shared__ __attribute__((aligned(16))) TA Vr[kFused ? 2 : 1][kFused ? kChunk + kConvK - 1 : 1][kSlab];
-  __shared__ float G_s[kChunk];              // exp(gam_r)
-  __shared__ float ksc_s[kChunk];            // exp(gam_n - gam_r)
+  using SL = StateLds<P, TA, kFused>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SL::kBytes];
+  uint8_t (*Stb)[8 * kLdsBlk] = reinterpret_cast<uint8_t (*)[8 * kLdsBlk]>(smem + SL::kStb);
+  uint8_t *Rtb = smem + SL::kRtb;
+  uint8_t (*Dtb)[4 * kLdsBlk] = reinterpret_cast<uint8_t (*)[4 * kLdsBlk]>(smem + SL::kDtb);
+  uint8_t *Dsb = smem + SL::kDsb;
+  float *Vs = reinterpret_cast<float *>(smem + SL::kVs);
+  float *Os = reinterpret_cast<float *>(smem + SL::kOs);
+  uint8_t *Ktb = smem + SL::kKtb;
+  float4 *Vw = reinterpret_cast<float4 *>(smem + SL::kVw);
+  TA (*Vr)[SL::kVrRows][kSlab] = reinterpret_cast<TA (*)[SL::kVrRows][kSlab]>(smem + SL::kVr);
+  float *G_s = reinterpret_cast<float *>(smem + SL::kG);
+  float *ksc_s = reinterpret_cast<float *>(smem + SL::kKsc);
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
