@@ -17,14 +17,15 @@
 // vector-memory instruction stalls the wave that issues it). Compute wave
 // (wr, wc) owns rows 128 wr .. +127 and columns 16 WN wc .. +16 WN - 1,
 // i.e. 8 x WN accumulator tiles of 16 x 16 (v_mfma_f32_16x16x32_bf16). The
-// contraction runs in k-tiles of 64 staged in a 3-deep LDS ring (see
-// gemm_dma_kernel), one barrier per k-tile. An LDS row is the 128 bytes of
+// contraction runs in k-tiles of 64 staged in an LDS ring (3 deep; 4 for the
+// decode-sized tiles; see gemm_dma_kernel), one barrier per k-tile. An LDS row is the 128 bytes of
 // one operand row in a k-tile, as 8 chunks of 16 bytes (8 k values); chunk c
 // of row r is stored at slot c ^ (r & 7), which makes both the 16-byte writes
 // and the 16-byte fragment reads free of bank conflicts.
 //
-// Up to 64 rows (decode) take gemm_skinny_kernel instead: the weights are
-// streamed once, and the work is split over the contraction.
+// 17 to 64 rows (decode batches) take the same kernel with tiles of 32 or 64
+// rows (launch_decode); up to 16 rows take gemm_skinny_kernel instead, which
+// streams the weights once and splits the work over the contraction.
 //
 // The weight fragment is the MFMA's first operand and the activation fragment
 // its second, so an accumulator lane holds 4 consecutive output columns of
@@ -140,11 +141,22 @@ __device__ __forceinline__ void wait_vm_barrier() {
   // the newest k-tile stays in flight).
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
+// The same with the newest `newer` k-tiles of L loads each still in flight
+// (newer <= S - 2).
+template <int L, int S>
+__device__ __forceinline__ void wait_vm_barrier_tiles(int newer) {
+#define GDN_WAIT_CASE(c) \
+  if constexpr ((c) <= S - 2) { if (newer == (c)) { wait_vm_barrier<L * (c)>(); return; } }
+  GDN_WAIT_CASE(7) GDN_WAIT_CASE(6) GDN_WAIT_CASE(5) GDN_WAIT_CASE(4)
+  GDN_WAIT_CASE(3) GDN_WAIT_CASE(2) GDN_WAIT_CASE(1)
+#undef GDN_WAIT_CASE
+  wait_vm_barrier<0>();
+}
 
 // One block tile of 32 TM rows x 32 WN columns at (m0, n0): compute wave
 // (wr, wc) owns rows 16 TM wr .. +16 TM - 1, i.e. TM x WN accumulator tiles.
-// smem holds kStages k-tiles of this shape.
-template <int TM, int WN>
+// smem holds a ring of S k-tiles of this shape, S - 1 of them loaded ahead.
+template <int TM, int WN, int S = kStages>
 __device__ __forceinline__ void gemm_tile(const GemmParams &p, uint8_t *smem, int m0, int n0) {
   constexpr int BM = 32 * TM, BN = 32 * WN;
   constexpr int kAChunks = BM * 8 / kComputeThreads;
@@ -206,19 +218,15 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &p, uint8_t *smem, in
 
   const int KT = K / kBK;
   if (loader) {
-    // The load waves keep two k-tiles in flight: before each barrier they
-    // wait for the k-tile about to be used, after it they issue the one two
-    // ahead into the stage every wave has just finished with.
-    GDN_ISSUE(0, 0);
-    if (KT > 1) GDN_ISSUE(1, 1);
+    // The load waves keep S - 1 k-tiles in flight: before each barrier they
+    // wait for the k-tile about to be used, after it they issue the one
+    // S - 1 ahead into the stage every wave has just finished with.
+    for (int t = 0; t < S - 1 && t < KT; ++t) GDN_ISSUE(t, t);
     int stage = 0;
     for (int kt = 0; kt < KT; ++kt) {
-      if (kt + 1 < KT)
-        wait_vm_barrier<kLoads>();
-      else
-        wait_vm_barrier<0>();
-      if (kt + 2 < KT) GDN_ISSUE(kt + 2, stage == 0 ? 2 : stage - 1);
-      stage = stage == kStages - 1 ? 0 : stage + 1;
+      wait_vm_barrier_tiles<kLoads, S>(min(S - 2, KT - 1 - kt));
+      if (kt + S - 1 < KT) GDN_ISSUE(kt + S - 1, stage == 0 ? S - 1 : stage - 1);
+      stage = stage == S - 1 ? 0 : stage + 1;
     }
     return;
   }
@@ -242,7 +250,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &p, uint8_t *smem, in
         for (int j = 0; j < WN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
     }
-    stage = stage == kStages - 1 ? 0 : stage + 1;
+    stage = stage == S - 1 ? 0 : stage + 1;
   }
 #undef GDN_ISSUE
 #undef GDN_DMA
@@ -256,11 +264,11 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &p, uint8_t *smem, in
 // groups of kGroupM row tiles. A launch whose last round of 256-row tiles
 // would leave most CUs idle runs its last column tiles as a second launch of
 // 128-row tiles instead (same operands, half the rows per tile).
-template <int TM, int WN>
+template <int TM, int WN, int S = kStages>
 __global__ __launch_bounds__(kGemmThreads) void gemm_dma_kernel(GemmParams p, int tiles_m, int tn0, int tiles_n,
                                                                 int per_xcd) {
   constexpr int BM = 32 * TM, BN = 32 * WN;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * (BM + BN) * kRowBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[S * (BM + BN) * kRowBytes];
   const int logical = (blockIdx.x % kGemmXcds) * per_xcd + blockIdx.x / kGemmXcds;
   if (logical >= tiles_m * tiles_n) return;
   const int group = logical / (kGroupM * tiles_n);
@@ -269,17 +277,15 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_dma_kernel(GemmParams p, in
   const int in_group = logical - group * kGroupM * tiles_n;
   const int tm = gm0 + in_group % gsize;
   const int tn = tn0 + in_group / gsize;
-  gemm_tile<TM, WN>(p, smem, tm * BM, tn * BN);
+  gemm_tile<TM, WN, S>(p, smem, tm * BM, tn * BN);
 }
 
-// Few rows (decode: M <= 64): the product is bound by streaming the weights
-// from HBM once, and there are too few row tiles to fill the chip. A block
-// owns 16 * NF output columns and 16 * MF rows (all of them, or one of two
-// row groups: blockIdx.y); its 8 waves split the contraction into contiguous
-// ranges of 32-wide steps and read both operands straight into MFMA
-// fragments (16 bytes per lane: the weights from HBM, the few activation rows
-// from L2), U steps of loads in flight before their MFMAs; the 8 partial sums
-// meet in LDS.
+// Up to 16 rows (single-sequence decode): a block owns 16 * NF output
+// columns and 16 * MF rows; its 8 waves split the contraction into
+// contiguous ranges of 32-wide steps and read both operands straight into
+// MFMA fragments (16 bytes per lane: the weights from HBM, the few activation
+// rows from L2), U steps of loads in flight before their MFMAs; the 8 partial
+// sums meet in LDS.
 constexpr int kSkWaves = 8;
 constexpr int kSkMaxNf = 5;
 constexpr int kSkCUs = 256;
@@ -381,45 +387,29 @@ hipError_t launch_skinny(const GemmParams &p, hipStream_t s, int row_groups) {
   return hipGetLastError();
 }
 
-// NF column fragments per block, and the rows either in one group or split
-// over two groups of blocks (blockIdx.y: each block then has half the rows
-// and half the activation loads). A block's time is a fixed part (its walk
+// NF column fragments per block. A block's time is a fixed part (its walk
 // of the contraction: a few round trips of loads, then the reduction through
-// LDS) plus a part per fragment, fitted at about 3.7 : 1, times about 0.65
-// when its rows are halved (the activation fragments are most of its loads);
-// blocks run in rounds of one per CU. The plan minimises
-// rounds x (3.7 + NF) x (0.65 if split).
-template <int MF, int NF>
-hipError_t launch_skinny_rg(const GemmParams &p, hipStream_t s, bool split) {
-  if constexpr (MF >= 2) {
-    if (split) return launch_skinny<MF / 2, NF>(p, s, 2);
-  }
-  return launch_skinny<MF, NF>(p, s, 1);
-}
+// LDS) plus a part per fragment, fitted at about 3.7 : 1; blocks run in
+// rounds of one per CU. The plan minimises rounds x (3.7 + NF).
 
 template <int MF>
 hipError_t launch_skinny_m(const GemmParams &p, hipStream_t s) {
   int best = 1;
-  bool best_split = false;
   double best_cost = -1.0;
   for (int nf = 1; nf <= kSkMaxNf; ++nf) {
     const int64_t blocks = (p.N + 16 * nf - 1) / (16 * nf);
-    for (int rg = 1; rg <= (MF >= 2 ? 2 : 1); ++rg) {
-      const double cost =
-          static_cast<double>((rg * blocks + kSkCUs - 1) / kSkCUs) * (3.7 + nf) * (rg == 2 ? 0.65 : 1.0);
-      if (best_cost < 0 || cost < best_cost - 1e-9) {
-        best_cost = cost;
-        best = nf;
-        best_split = rg == 2;
-      }
+    const double cost = static_cast<double>((blocks + kSkCUs - 1) / kSkCUs) * (3.7 + nf);
+    if (best_cost < 0 || cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best = nf;
     }
   }
   switch (best) {
-    case 1: return launch_skinny_rg<MF, 1>(p, s, best_split);
-    case 2: return launch_skinny_rg<MF, 2>(p, s, best_split);
-    case 3: return launch_skinny_rg<MF, 3>(p, s, best_split);
-    case 4: return launch_skinny_rg<MF, 4>(p, s, best_split);
-    default: return launch_skinny_rg<MF, 5>(p, s, best_split);
+    case 1: return launch_skinny<MF, 1>(p, s, 1);
+    case 2: return launch_skinny<MF, 2>(p, s, 1);
+    case 3: return launch_skinny<MF, 3>(p, s, 1);
+    case 4: return launch_skinny<MF, 4>(p, s, 1);
+    default: return launch_skinny<MF, 5>(p, s, 1);
   }
 }
 
@@ -480,11 +470,52 @@ static TilePlan gemm_tile_plan(int M, int N) {
   return best;
 }
 
+// 17 to 64 rows (decode batches): the DMA tiles with 32 or 64 rows (TM = 1
+// or 2) and 32, 64 or 96 columns (WN = 1 .. 3) and a ring of 4 k-tiles. The
+// product is bound by the bytes each CU pulls through its vector-memory path
+// (the operand rows of its tiles, once per k-tile; HBM is far from busy), so
+// the shape chosen is the one with the fewest bytes on the busiest CU:
+// ceil(tiles / 256) x (32 TM + 32 WN) operand rows per k-tile (ties: the
+// wider tile). Measured at 64 rows against the column-split kernel below:
+// 35B in-projection 19.1 -> 11.5 us, out-projection 13.0 -> 9.6 us; 27B
+// 45.0 -> 30.1 and 28.8 -> 16.4 us.
+constexpr int kDecodeStages = 4;
+template <int TM, int WN>
+hipError_t launch_decode_tile(const GemmParams &p, hipStream_t s) {
+  const int tiles_m = (p.M + 32 * TM - 1) / (32 * TM), tiles_n = (p.N + 32 * WN - 1) / (32 * WN);
+  const int per_xcd = (tiles_m * tiles_n + kGemmXcds - 1) / kGemmXcds;
+  hipLaunchKernelGGL((gemm_dma_kernel<TM, WN, kDecodeStages>), dim3(per_xcd * kGemmXcds), dim3(kGemmThreads), 0, s,
+                     p, tiles_m, 0, tiles_n, per_xcd);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const GemmParams &p, hipStream_t s) {
+  int best_tm = 1, best_wn = 1;
+  int64_t best_cost = -1;
+  for (int tm = 1; tm <= (p.M > 32 ? 2 : 1); ++tm)
+    for (int wn = 1; wn <= 3; ++wn) {
+      const int64_t tiles = static_cast<int64_t>((p.M + 32 * tm - 1) / (32 * tm)) * ((p.N + 32 * wn - 1) / (32 * wn));
+      const int64_t cost = (tiles + kCUs - 1) / kCUs * (32 * tm + 32 * wn);
+      if (best_cost < 0 || cost < best_cost || (cost == best_cost && wn > best_wn)) {
+        best_cost = cost;
+        best_tm = tm;
+        best_wn = wn;
+      }
+    }
+  if (best_tm == 2) {
+    if (best_wn == 1) return launch_decode_tile<2, 1>(p, s);
+    if (best_wn == 2) return launch_decode_tile<2, 2>(p, s);
+    return launch_decode_tile<2, 3>(p, s);
+  }
+  if (best_wn == 1) return launch_decode_tile<1, 1>(p, s);
+  if (best_wn == 2) return launch_decode_tile<1, 2>(p, s);
+  return launch_decode_tile<1, 3>(p, s);
+}
+
 hipError_t launch_gemm(const GemmParams &p, hipStream_t s) {
   if (p.M == 0 || p.N == 0) return hipSuccess;
   if (p.M <= 16) return launch_skinny_m<1>(p, s);
-  if (p.M <= 32) return launch_skinny_m<2>(p, s);
-  if (p.M <= 64) return launch_skinny_m<4>(p, s);
+  if (p.M <= 64) return launch_decode(p, s);
   const TilePlan plan = gemm_tile_plan(p.M, p.N);
   if (plan.wn == 4) return launch_wn<4>(p, plan.tail_n, s);
   return launch_wn<5>(p, plan.tail_n, s);

@@ -110,15 +110,16 @@ def _rows(T, seed):
     return sorted(r for r in base if 0 <= r < T)
 
 
-# Row counts up to 64 take the decode kernel (16, 32 or 64 rows per block;
-# 1 to 5 column fragments of 16 per block by width: 8224 columns take 3,
-# 12352 take 4, 16480 take 5), more the tiled one; 4096 rows
-# x 2576 columns run 256 tiles of 256 rows and the last 5 column tiles as
-# 128-row tiles.
+# Row counts up to 16 take the column-split kernel (1 to 5 column fragments
+# of 16 per block by width), 17 to 64 the tiled kernel with 32- or 64-row
+# tiles (32 to 96 columns; rows past the count are clamped on load and
+# masked on store), more its 256-row tiles; 4096 rows x 2576 columns run 256
+# tiles of 256 rows and the last 5 column tiles as 128-row tiles.
 @pytest.mark.parametrize("T,hidden,heads", [(1, 64, (1, 1)), (20, 128, (2, 6)), (40, 192, (2, 4)),
                                             (5, 64, (16, 64)), (64, 128, (16, 48)), (77, 128, (2, 6)),
                                             (300, 192, (2, 4)), (513, 256, (4, 4)), (256, 320, (1, 2)),
-                                            (4096, 256, (2, 8)), (64, 128, (16, 16))])
+                                            (4096, 256, (2, 8)), (64, 128, (16, 16)), (17, 64, (1, 2)),
+                                            (33, 192, (2, 4)), (48, 256, (16, 32))])
 def test_in_proj_small(T, hidden, heads):
     hqk, hv = heads
     w = wl.custom("prefill", 1, hqk, hv, "bf16", seed=400 + T, lengths=[T])
@@ -150,7 +151,8 @@ def _out_proj_gpu(cfg, x, hidden):
 
 @pytest.mark.parametrize("T,hidden,hv,full", [(1, 64, 1, False), (77, 200, 6, False), (513, 256, 4, False),
                                               (4096, 5120, 48, True), (64, 2048, 32, True),
-                                              (4096, 2720, 16, True), (64, 5120, 48, True)])
+                                              (4096, 2720, 16, True), (64, 5120, 48, True), (17, 128, 2, False),
+                                              (33, 192, 4, False), (48, 2048, 32, True)])
 def test_out_proj(T, hidden, hv, full):
     hqk = 16 if full else 1
     w = wl.custom("prefill", 1, hqk, hv, "bf16", seed=420 + T + hv, lengths=[T])
