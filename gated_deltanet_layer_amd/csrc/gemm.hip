@@ -471,7 +471,9 @@ static TilePlan gemm_tile_plan(int M, int N) {
 }
 
 // 17 to 64 rows (decode batches): the DMA tiles with 32 or 64 rows (TM = 1
-// or 2) and 32, 64 or 96 columns (WN = 1 .. 3) and a ring of 4 k-tiles. The
+// or 2) and 32, 64 or 96 columns (WN = 1 .. 3) and a ring of 4 k-tiles (5
+// for the wider tiles: 27B out-projection 17.9 -> 16.6 us, where 32-column
+// tiles lose 0.7 us with 5). The
 // product is bound by the bytes each CU pulls through its vector-memory path
 // (the operand rows of its tiles, once per k-tile; HBM is far from busy), so
 // the shape chosen is the one with the fewest bytes on the busiest CU:
@@ -479,9 +481,9 @@ static TilePlan gemm_tile_plan(int M, int N) {
 // wider tile). Measured at 64 rows against the column-split kernel below:
 // 35B in-projection 19.1 -> 11.5 us, out-projection 13.0 -> 9.6 us; 27B
 // 45.0 -> 30.1 and 28.8 -> 16.4 us.
-constexpr int kDecodeStages = 4;
 template <int TM, int WN>
 hipError_t launch_decode_tile(const GemmParams &p, hipStream_t s) {
+  constexpr int kDecodeStages = WN == 1 ? 4 : 5;
   const int tiles_m = (p.M + 32 * TM - 1) / (32 * TM), tiles_n = (p.N + 32 * WN - 1) / (32 * WN);
   const int per_xcd = (tiles_m * tiles_n + kGemmXcds - 1) / kGemmXcds;
   hipLaunchKernelGGL((gemm_dma_kernel<TM, WN, kDecodeStages>), dim3(per_xcd * kGemmXcds), dim3(kGemmThreads), 0, s,
