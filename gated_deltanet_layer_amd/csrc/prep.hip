@@ -51,15 +51,15 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void prep_kernel(PrepParams p) 
   // Raw rows tau0 - 3 .. tau0 + kTile - 1 of [state; x], all loaded before
   // any is used.
   // Rows before the sequence come from the conv state; rows past its end are
-  // clamped to its last row and never used.
+  // clamped to its last row and never used. An empty sequence reads state
+  // rows only, clamped to its 3 rows (those past row 2 are never used).
   constexpr int kRows = kTile + kConvK - 1;
   float2 xr[kRows];
 #pragma unroll
   for (int r = 0; r < kRows; ++r) {
     const int pos = tau0 - (kConvK - 1) + r;
-    // An empty sequence reads its state row 0 instead (never used).
     const bool from_state = pos < 0 || L == 0;
-    const TA *src = from_state ? st_in + st_base + static_cast<size_t>(max(pos + kConvK - 1, 0)) * C
+    const TA *src = from_state ? st_in + st_base + static_cast<size_t>(min(max(pos + kConvK - 1, 0), kConvK - 2)) * C
                                : qkv + static_cast<size_t>(seq0 + min(pos, L - 1)) * C;
     xr[r] = Act<TA>::load2(src, c);
   }
