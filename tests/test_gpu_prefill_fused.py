@@ -167,6 +167,52 @@ def test_fused_graph_replay_matches_eager(case):
         (t["z"].float() * 2.0).sum().item()
 
 
+def test_fused_concurrent_calls_on_two_streams():
+    """Two folded calls (the 4,096-token shape's head counts, shorter) on two
+    streams at once, each with its own workspace: the norm blocks of one
+    launch wait only for that launch's slab blocks, so interleaved launches
+    give the same bits as the calls run one after the other."""
+    import torch
+    from gated_deltanet_layer_amd import binding as B
+    from gated_deltanet_layer_amd import layer as Lyr
+    cfg = B.make_config(16, 48, "bf16")
+    assert _norm_folded(1, 48)
+    runs = []
+    for seed, T in ((520, 1000), (521, 777)):
+        w = wl.custom("prefill", 1, 16, 48, "bf16", seed=seed, lengths=[T], s0_std=0.02, conv0_std=1.0)
+        x = wl.generate(w)
+        t = {k: P.dev(v) for k, v in x.items()}
+        runs.append((t, Lyr.PrefillFused(cfg, 1, T), torch.empty_like(t["conv0"]), torch.empty_like(t["S0"])))
+
+    def call(r):
+        t, f, conv_o, S_o = r
+        f(t["cu_seqlens"], t["qkv"], t["z"], t["b"], t["a"], t["conv_w"], t["dt_bias"], t["A_log"], t["norm_w"],
+          t["conv0"], conv_o, t["S0"], S_o)
+
+    say("case fused concurrent calls: serial")
+    ref = []
+    for r in runs:
+        call(r)
+        torch.cuda.synchronize()
+        ref.append((P.bits(r[1].y).copy(), P.bits(r[3]).copy(), P.bits(r[2]).copy()))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rep in range(3):
+        say(f"  concurrent {rep}")
+        for r in runs:
+            r[1].y.zero_()
+            r[3].zero_()
+            r[2].zero_()
+        torch.cuda.synchronize()
+        for st, r in zip(streams, runs):
+            with torch.cuda.stream(st):
+                call(r)
+        torch.cuda.synchronize()
+        for k, r in enumerate(runs):
+            got = (P.bits(r[1].y), P.bits(r[3]), P.bits(r[2]))
+            for name, a, b in zip(("y", "S", "conv"), got, ref[k]):
+                assert np.array_equal(a, b), f"rep {rep}, call {k}: {name} differs from the serial call"
+
+
 def test_fused_l2_rsqrt_form():
     w = wl.custom("prefill", 2, 2, 4, "bf16", seed=506, lengths=[100, 37], s0_std=0.02, conv0_std=1.0)
     x = wl.generate(w)
