@@ -625,9 +625,13 @@ __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(PrefillParam
 // Counters sit 128 bytes apart: polls and adds of neighbouring pairs on one
 // line slowed the step by tens of us.
 // Norm blocks only ever wait for slab blocks, never the reverse, so the
-// launch drains in whatever order its blocks are placed; each wave's polls
-// are bounded in total (about a second), and rows whose counter never
-// completes (only cu_seqlens outside the contract leave one short) get NaN.
+// launch drains in whatever order its blocks are placed. A wave's items lie
+// G / (4 Hv) chunks apart (G = its launch's norm waves), so it waits for any
+// one of them at most about as long as the slab blocks take for that many
+// chunks, well under a millisecond however long the sequences. Each wait is
+// bounded (about a second); once one runs out the wave waits no more, and
+// rows whose counter is not complete (only cu_seqlens outside the contract
+// leave one short) get NaN.
 // The same norm waves write the new conv states: the V channels of head j
 // once the counter of the sequence's first chunk of j is full (the four slab
 // blocks of j read the old state only before that chunk, so the update can
@@ -636,7 +640,7 @@ __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(PrefillParam
 // sequences without tokens (which nothing else reads) first.
 constexpr uint32_t kFoldReady = 16;       // 4 slab blocks x 4 y-waves
 constexpr int kFoldSleep = 48;            // s_sleep units (64 cycles) between polls
-constexpr int kFoldSpins = 1 << 20;       // polls per wave, each a load and a sleep
+constexpr int kFoldSpins = 1 << 20;       // polls per item, each a load and a sleep
 
 __device__ __forceinline__ void fold_put4(bf16_t *o, size_t i, f32x4 a) {
   const uint64_t w = static_cast<uint64_t>(f32_to_bf16(a[0])) | (static_cast<uint64_t>(f32_to_bf16(a[1])) << 16) |
@@ -729,7 +733,7 @@ __device__ __forceinline__ void fold_norm(const PrefillParams &p, int64_t max_ch
   const float4 w0 = *reinterpret_cast<const float4 *>(p.norm_w + 8 * sub);
   const float4 w1 = *reinterpret_cast<const float4 *>(p.norm_w + 8 * sub + 4);
   const int64_t items = max_chunks * p.n_v * 4;
-  int spins = 0;   // over all of the wave's items
+  bool waiting = true;   // false once a wait has run out
   for (int64_t it = g; it < items; it += G) {
     const int64_t t = it >> 2;
     const int rb = 16 * static_cast<int>(it & 3);
@@ -744,10 +748,13 @@ __device__ __forceinline__ void fold_norm(const PrefillParams &p, int64_t max_ch
     if (rb >= len) continue;
     const uint32_t *rdy = p.ready + t * kReadyStride;
     uint32_t cnt = __hip_atomic_load(rdy, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    while (__builtin_amdgcn_readfirstlane(cnt) < kFoldReady && spins < kFoldSpins) {
+    for (int spins = 0; waiting && __builtin_amdgcn_readfirstlane(cnt) < kFoldReady; ++spins) {
+      if (spins == kFoldSpins) {
+        waiting = false;
+        break;
+      }
       __builtin_amdgcn_s_sleep(kFoldSleep);
       cnt = __hip_atomic_load(rdy, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      ++spins;
     }
     const bool ok = __builtin_amdgcn_readfirstlane(cnt) >= kFoldReady;
     float4 o0[4], o1[4], z0[4], z1[4];
