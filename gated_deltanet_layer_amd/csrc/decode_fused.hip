@@ -74,33 +74,57 @@ __global__ __launch_bounds__(kFusedThreads) void decode_tokens_kernel(FusedDecod
       S[r] = *reinterpret_cast<const float4 *>(Sin + (row0 + r) * kHeadDim + col0);
   }
 
+  // 2. The inputs of token 0, in flight with the state rows: waves 0..2 hold
+  // the conv window, rows -3 .. 0 of [conv state; the sequence's tokens], of
+  // two adjacent channels per lane of q (wave 0), k (wave 1) or v (wave 2);
+  // wave 0 also z and the norm weights, one lane of wave 3 the two logits.
+  // Each token then issues the next token's loads first, so that they land
+  // during its step, and shifts the window by one row at its end.
+  const int hb = wave == 0 ? hk : (wave == 1 ? p.n_qk + hk : 2 * p.n_qk + j);
+  const int ch = hb * kHeadDim + 2 * lane;   // channel pair of waves 0..2
+  const TA *xq = static_cast<const TA *>(p.qkv) + static_cast<size_t>(n) * K * C;
+  const TA *zp = static_cast<const TA *>(p.z);
+  const TA *bp = static_cast<const TA *>(p.b);
+  const TA *ap = static_cast<const TA *>(p.a);
+  float2 xr[kConvK], xn = make_float2(0.f, 0.f);
+  float4 w0 = make_float4(0.f, 0.f, 0.f, 0.f), w1 = w0, zv = w0, zn = w0, wv = w0;
+  float bl = 0.f, al = 0.f, bn = 0.f, an = 0.f;
+  if (K > 0) {
+    const size_t e0 = static_cast<size_t>(n) * K * p.n_v + j;   // row of z and the logits, token 0
+    if (wave < 3) {
+      const TA *st = static_cast<const TA *>(p.st_in) + static_cast<size_t>(n) * (kConvK - 1) * C;
+#pragma unroll
+      for (int i = 0; i < kConvK - 1; ++i) xr[i] = Act<TA>::load2(st, static_cast<size_t>(i) * C + ch);
+      xr[kConvK - 1] = Act<TA>::load2(xq, ch);
+      w0 = reinterpret_cast<const float4 *>(p.conv_w)[ch];
+      w1 = reinterpret_cast<const float4 *>(p.conv_w)[ch + 1];
+    }
+    if (wave == 0) {
+      zv = Act<TA>::load4(zp, e0 * kHeadDim + col0);
+      wv = *reinterpret_cast<const float4 *>(p.norm_w + col0);
+    } else if (tid == 3 * kWave) {
+      bl = Act<TA>::load(bp, e0);
+      al = Act<TA>::load(ap, e0);
+    }
+  }
+
   for (int tau = 0; tau < K; ++tau) {
     const size_t tok = static_cast<size_t>(n) * K + tau;      // row of qkv, z, y, logits
     const size_t e = tok * p.n_v + j;
     const int plane = K - 1 - tau;                             // snapshot plane (most recent first)
     if (tau > 0) __syncthreads();                              // the last token's LDS reads are done
-    float4 zv = make_float4(0.f, 0.f, 0.f, 0.f), wv = zv;
-    if (wave == 0) {
-      zv = Act<TA>::load4(static_cast<const TA *>(p.z), e * kHeadDim + col0);
-      wv = *reinterpret_cast<const float4 *>(p.norm_w + col0);
+    if (tau + 1 < K) {
+      if (wave < 3) xn = Act<TA>::load2(xq, static_cast<size_t>(tau + 1) * C + ch);
+      if (wave == 0) {
+        zn = Act<TA>::load4(zp, (e + p.n_v) * kHeadDim + col0);
+      } else if (tid == 3 * kWave) {
+        bn = Act<TA>::load(bp, e + p.n_v);
+        an = Act<TA>::load(ap, e + p.n_v);
+      }
     }
 
-    // 2. The token's q (wave 0), k (wave 1), v (wave 2); gates (wave 3).
+    // 3. The token's q (wave 0), k (wave 1), v (wave 2); gates (wave 3).
     if (wave < 3) {
-      const int hb = wave == 0 ? hk : (wave == 1 ? p.n_qk + hk : 2 * p.n_qk + j);
-      const int c = hb * kHeadDim + 2 * lane;
-      // Rows tau-3 .. tau of [conv state; the sequence's tokens].
-      const TA *st = static_cast<const TA *>(p.st_in) + static_cast<size_t>(n) * (kConvK - 1) * C;
-      const TA *xq = static_cast<const TA *>(p.qkv) + static_cast<size_t>(n) * K * C;
-      float2 xr[kConvK];
-#pragma unroll
-      for (int i = 0; i < kConvK; ++i) {
-        const int r = tau - (kConvK - 1) + i;
-        xr[i] = r < 0 ? Act<TA>::load2(st, static_cast<size_t>(kConvK - 1 + r) * C + c)
-                      : Act<TA>::load2(xq, static_cast<size_t>(r) * C + c);
-      }
-      const float4 w0 = reinterpret_cast<const float4 *>(p.conv_w)[c];
-      const float4 w1 = reinterpret_cast<const float4 *>(p.conv_w)[c + 1];
       float y0 = w0.x * xr[0].x + w0.y * xr[1].x + w0.z * xr[2].x + w0.w * xr[3].x;
       float y1 = w1.x * xr[0].y + w1.y * xr[1].y + w1.z * xr[2].y + w1.w * xr[3].y;
       y0 = siluf_(y0);
@@ -116,17 +140,17 @@ __global__ __launch_bounds__(kFusedThreads) void decode_tokens_kernel(FusedDecod
       // Conv state after this token: rows tau-2, tau-1, tau.
       if (wave == 2 || j == hk) {
         TA *so = static_cast<TA *>(p.st_out) + (static_cast<size_t>(n) * K + plane) * (kConvK - 1) * C;
-        Act<TA>::store2(so, c, xr[1]);
-        Act<TA>::store2(so, c + C, xr[2]);
-        Act<TA>::store2(so, c + 2 * C, xr[3]);
+        Act<TA>::store2(so, ch, xr[1]);
+        Act<TA>::store2(so, ch + C, xr[2]);
+        Act<TA>::store2(so, ch + 2 * C, xr[3]);
       }
     } else if (tid == 3 * kWave) {
-      gate[0] = sigmoidf_(Act<TA>::load(static_cast<const TA *>(p.b), e));
-      gate[1] = -expf(p.A_log[j]) * softplusf_(Act<TA>::load(static_cast<const TA *>(p.a), e) + p.dt_bias[j]);
+      gate[0] = sigmoidf_(bl);
+      gate[1] = -expf(p.A_log[j]) * softplusf_(al + p.dt_bias[j]);
     }
     __syncthreads();
 
-    // 3. Column sums S^T k, S^T q over this thread's rows, and k.q.
+    // 4. Column sums S^T k, S^T q over this thread's rows, and k.q.
     float kr[kRowsPerThread], qr[kRowsPerThread];
 #pragma unroll
     for (int h = 0; h < kRowsPerThread / 4; ++h) {
@@ -164,7 +188,7 @@ __global__ __launch_bounds__(kFusedThreads) void decode_tokens_kernel(FusedDecod
     }
     __syncthreads();
 
-    // 4. Delta, readout, state update; the updated state is this token's
+    // 5. Delta, readout, state update; the updated state is this token's
     // snapshot plane.
     const float bt = gate[0];
     const float eg = expf(gate[1]);
@@ -188,7 +212,7 @@ __global__ __launch_bounds__(kFusedThreads) void decode_tokens_kernel(FusedDecod
       *reinterpret_cast<float4 *>(Sout + (row0 + r) * kHeadDim + col0) = S[r];
     }
 
-    // 5. Gated RMSNorm of the 128 readout values: each 32-lane half of wave 0
+    // 6. Gated RMSNorm of the 128 readout values: each 32-lane half of wave 0
     // holds all of them (4 per lane).
     if (wave == 0) {
       float ss = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
@@ -204,6 +228,14 @@ __global__ __launch_bounds__(kFusedThreads) void decode_tokens_kernel(FusedDecod
         Act<TA>::store4(static_cast<TA *>(p.y), e * kHeadDim + col0, y);
       }
     }
+
+    // The next token's window and inputs.
+#pragma unroll
+    for (int i = 0; i < kConvK - 1; ++i) xr[i] = xr[i + 1];
+    xr[kConvK - 1] = xn;
+    zv = zn;
+    bl = bn;
+    al = an;
   }
 }
 
