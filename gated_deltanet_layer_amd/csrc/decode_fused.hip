@@ -40,6 +40,46 @@ constexpr int kFusedWaves = kFusedThreads / kWave;
 constexpr int kRowsPerThread = 8;
 constexpr int kColQuads = kHeadDim / 4;   // 32 lanes span a row
 
+// Activation inputs in flight travel as their raw bits and are widened to
+// fp32 where they are used. Widened at the load, the wave would wait for
+// the load right there, and with it (one counter covers loads and stores)
+// for every store it issued before, such as the previous token's 64 KiB
+// snapshot plane.
+template <typename TA> struct Bits;
+template <> struct Bits<bf16_t> {
+  using X1 = uint32_t;   // one value
+  using X2 = uint32_t;   // two adjacent values
+  using X4 = uint2;      // four
+  static __device__ __forceinline__ X1 get1(const bf16_t *p, size_t i) { return p[i].bits; }
+  static __device__ __forceinline__ X2 get2(const bf16_t *p, size_t i) {
+    return *reinterpret_cast<const uint32_t *>(p + i);
+  }
+  static __device__ __forceinline__ X4 get4(const bf16_t *p, size_t i) {
+    return *reinterpret_cast<const uint2 *>(p + i);
+  }
+  static __device__ __forceinline__ void put2(bf16_t *p, size_t i, X2 x) { *reinterpret_cast<uint32_t *>(p + i) = x; }
+  static __device__ __forceinline__ float f1(X1 x) { return __uint_as_float(x << 16); }
+  static __device__ __forceinline__ float2 f2(X2 w) {
+    return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+  }
+  static __device__ __forceinline__ float4 f4(X4 w) {
+    return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                       __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
+  }
+};
+template <> struct Bits<float> {
+  using X1 = float;
+  using X2 = float2;
+  using X4 = float4;
+  static __device__ __forceinline__ X1 get1(const float *p, size_t i) { return p[i]; }
+  static __device__ __forceinline__ X2 get2(const float *p, size_t i) { return *reinterpret_cast<const float2 *>(p + i); }
+  static __device__ __forceinline__ X4 get4(const float *p, size_t i) { return *reinterpret_cast<const float4 *>(p + i); }
+  static __device__ __forceinline__ void put2(float *p, size_t i, X2 x) { *reinterpret_cast<float2 *>(p + i) = x; }
+  static __device__ __forceinline__ float f1(X1 x) { return x; }
+  static __device__ __forceinline__ float2 f2(X2 x) { return x; }
+  static __device__ __forceinline__ float4 f4(X4 x) { return x; }
+};
+
 // kOne: a single token per sequence (gdn_decode_fused), with K = 1 known at
 // compile time so that the step keeps the register budget of six waves per
 // SIMD.
@@ -74,38 +114,38 @@ __global__ __launch_bounds__(kFusedThreads) void decode_tokens_kernel(FusedDecod
       S[r] = *reinterpret_cast<const float4 *>(Sin + (row0 + r) * kHeadDim + col0);
   }
 
-  // 2. The inputs of token 0, in flight with the state rows: waves 0..2 hold
-  // the conv window, rows -3 .. 0 of [conv state; the sequence's tokens], of
-  // two adjacent channels per lane of q (wave 0), k (wave 1) or v (wave 2);
-  // wave 0 also z and the norm weights, one lane of wave 3 the two logits.
-  // Each token then issues the next token's loads first, so that they land
-  // during its step, and shifts the window by one row at its end.
+  // 2. The inputs of token 0, in flight with the state rows: the 4-row conv
+  // window, rows -3 .. 0 of [conv state; the sequence's tokens], of two
+  // adjacent channels per lane of q (wave 0), k (wave 1) or v (waves 2 and
+  // up; only wave 2 uses them), z and the two logits. Every wave loads all of
+  // them (same addresses within a wave), so that no load sits in a branch
+  // whose end would wait for it. A verify call then issues the next token's
+  // loads at the start of each token, the last token reloading its own, and
+  // shifts the window by one row at its end.
+  using BI = Bits<TA>;
   const int hb = wave == 0 ? hk : (wave == 1 ? p.n_qk + hk : 2 * p.n_qk + j);
-  const int ch = hb * kHeadDim + 2 * lane;   // channel pair of waves 0..2
+  const int ch = hb * kHeadDim + 2 * lane;   // this lane's channel pair
   const TA *xq = static_cast<const TA *>(p.qkv) + static_cast<size_t>(n) * K * C;
   const TA *zp = static_cast<const TA *>(p.z);
   const TA *bp = static_cast<const TA *>(p.b);
   const TA *ap = static_cast<const TA *>(p.a);
-  float2 xr[kConvK], xn = make_float2(0.f, 0.f);
-  float4 w0 = make_float4(0.f, 0.f, 0.f, 0.f), w1 = w0, zv = w0, zn = w0, wv = w0;
-  float bl = 0.f, al = 0.f, bn = 0.f, an = 0.f;
+  typename BI::X2 xr[kConvK] = {}, xn = {};
+  typename BI::X4 zr = {}, zn = {};
+  typename BI::X1 br = {}, ar = {}, bn = {}, an = {};
+  float4 w0 = make_float4(0.f, 0.f, 0.f, 0.f), w1 = w0, wv = w0;
+  const float neg_a = -expf(p.A_log[j]), dtb = p.dt_bias[j];   // the V-head's gate parameters
   if (K > 0) {
     const size_t e0 = static_cast<size_t>(n) * K * p.n_v + j;   // row of z and the logits, token 0
-    if (wave < 3) {
-      const TA *st = static_cast<const TA *>(p.st_in) + static_cast<size_t>(n) * (kConvK - 1) * C;
+    const TA *st = static_cast<const TA *>(p.st_in) + static_cast<size_t>(n) * (kConvK - 1) * C;
 #pragma unroll
-      for (int i = 0; i < kConvK - 1; ++i) xr[i] = Act<TA>::load2(st, static_cast<size_t>(i) * C + ch);
-      xr[kConvK - 1] = Act<TA>::load2(xq, ch);
-      w0 = reinterpret_cast<const float4 *>(p.conv_w)[ch];
-      w1 = reinterpret_cast<const float4 *>(p.conv_w)[ch + 1];
-    }
-    if (wave == 0) {
-      zv = Act<TA>::load4(zp, e0 * kHeadDim + col0);
-      wv = *reinterpret_cast<const float4 *>(p.norm_w + col0);
-    } else if (tid == 3 * kWave) {
-      bl = Act<TA>::load(bp, e0);
-      al = Act<TA>::load(ap, e0);
-    }
+    for (int i = 0; i < kConvK - 1; ++i) xr[i] = BI::get2(st, static_cast<size_t>(i) * C + ch);
+    xr[kConvK - 1] = BI::get2(xq, ch);
+    zr = BI::get4(zp, e0 * kHeadDim + col0);
+    br = BI::get1(bp, e0);
+    ar = BI::get1(ap, e0);
+    w0 = reinterpret_cast<const float4 *>(p.conv_w)[ch];
+    w1 = reinterpret_cast<const float4 *>(p.conv_w)[ch + 1];
+    wv = *reinterpret_cast<const float4 *>(p.norm_w + col0);
   }
 
   for (int tau = 0; tau < K; ++tau) {
@@ -113,20 +153,20 @@ __global__ __launch_bounds__(kFusedThreads) void decode_tokens_kernel(FusedDecod
     const size_t e = tok * p.n_v + j;
     const int plane = K - 1 - tau;                             // snapshot plane (most recent first)
     if (tau > 0) __syncthreads();                              // the last token's LDS reads are done
-    if (tau + 1 < K) {
-      if (wave < 3) xn = Act<TA>::load2(xq, static_cast<size_t>(tau + 1) * C + ch);
-      if (wave == 0) {
-        zn = Act<TA>::load4(zp, (e + p.n_v) * kHeadDim + col0);
-      } else if (tid == 3 * kWave) {
-        bn = Act<TA>::load(bp, e + p.n_v);
-        an = Act<TA>::load(ap, e + p.n_v);
-      }
+    if constexpr (!kOne) {
+      const int tn = min(tau + 1, K - 1);
+      const size_t en = (static_cast<size_t>(n) * K + tn) * p.n_v + j;
+      xn = BI::get2(xq, static_cast<size_t>(tn) * C + ch);
+      zn = BI::get4(zp, en * kHeadDim + col0);
+      bn = BI::get1(bp, en);
+      an = BI::get1(ap, en);
     }
 
     // 3. The token's q (wave 0), k (wave 1), v (wave 2); gates (wave 3).
     if (wave < 3) {
-      float y0 = w0.x * xr[0].x + w0.y * xr[1].x + w0.z * xr[2].x + w0.w * xr[3].x;
-      float y1 = w1.x * xr[0].y + w1.y * xr[1].y + w1.z * xr[2].y + w1.w * xr[3].y;
+      const float2 x0 = BI::f2(xr[0]), x1 = BI::f2(xr[1]), x2 = BI::f2(xr[2]), x3 = BI::f2(xr[3]);
+      float y0 = w0.x * x0.x + w0.y * x1.x + w0.z * x2.x + w0.w * x3.x;
+      float y1 = w1.x * x0.y + w1.y * x1.y + w1.z * x2.y + w1.w * x3.y;
       y0 = siluf_(y0);
       y1 = siluf_(y1);
       if (wave < 2) {
@@ -137,16 +177,16 @@ __global__ __launch_bounds__(kFusedThreads) void decode_tokens_kernel(FusedDecod
       }
       float *dst = wave == 0 ? qs : (wave == 1 ? ks : vs);
       *reinterpret_cast<float2 *>(dst + 2 * lane) = make_float2(y0, y1);
-      // Conv state after this token: rows tau-2, tau-1, tau.
+      // Conv state after this token: rows tau-2, tau-1, tau, as stored.
       if (wave == 2 || j == hk) {
         TA *so = static_cast<TA *>(p.st_out) + (static_cast<size_t>(n) * K + plane) * (kConvK - 1) * C;
-        Act<TA>::store2(so, ch, xr[1]);
-        Act<TA>::store2(so, ch + C, xr[2]);
-        Act<TA>::store2(so, ch + 2 * C, xr[3]);
+        BI::put2(so, ch, xr[1]);
+        BI::put2(so, ch + C, xr[2]);
+        BI::put2(so, ch + 2 * C, xr[3]);
       }
     } else if (tid == 3 * kWave) {
-      gate[0] = sigmoidf_(bl);
-      gate[1] = -expf(p.A_log[j]) * softplusf_(al + p.dt_bias[j]);
+      gate[0] = sigmoidf_(BI::f1(br));
+      gate[1] = neg_a * softplusf_(BI::f1(ar) + dtb);
     }
     __syncthreads();
 
@@ -221,6 +261,7 @@ __global__ __launch_bounds__(kFusedThreads) void decode_tokens_kernel(FusedDecod
       const float inv = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + p.norm_eps);
       if (lane < kColQuads) {
         float4 y;
+        const float4 zv = BI::f4(zr);
         y.x = o[0] * inv * wv.x * siluf_(zv.x);
         y.y = o[1] * inv * wv.y * siluf_(zv.y);
         y.z = o[2] * inv * wv.z * siluf_(zv.z);
@@ -230,12 +271,14 @@ __global__ __launch_bounds__(kFusedThreads) void decode_tokens_kernel(FusedDecod
     }
 
     // The next token's window and inputs.
+    if constexpr (!kOne) {
 #pragma unroll
-    for (int i = 0; i < kConvK - 1; ++i) xr[i] = xr[i + 1];
-    xr[kConvK - 1] = xn;
-    zv = zn;
-    bl = bn;
-    al = an;
+      for (int i = 0; i < kConvK - 1; ++i) xr[i] = xr[i + 1];
+      xr[kConvK - 1] = xn;
+      zr = zn;
+      br = bn;
+      ar = an;
+    }
   }
 }
 
