@@ -210,6 +210,16 @@ __global__ __launch_bounds__(kFusedThreads) void decode_tokens_kernel(FusedDecod
       part[6] += S[r].z * qr[r]; part[7] += S[r].w * qr[r];
       part[8] += kr[r] * qr[r];
     }
+    if constexpr (!kOne) {
+      // The state after token tau - 1 is still in S: its snapshot plane goes
+      // out here, among this token's reductions, rather than as a burst
+      // before the next barrier (the last token's plane follows its update).
+      if (tau > 0) {
+        float *Sp = p.S_out + ((static_cast<size_t>(n) * K + plane + 1) * p.n_v + j) * hd2;
+#pragma unroll
+        for (int r = 0; r < kRowsPerThread; ++r) *reinterpret_cast<float4 *>(Sp + (row0 + r) * kHeadDim + col0) = S[r];
+      }
+    }
     // The two row groups of a wave (lanes l and l + 32 share columns), then
     // the waves through LDS.
 #pragma unroll
@@ -249,7 +259,7 @@ __global__ __launch_bounds__(kFusedThreads) void decode_tokens_kernel(FusedDecod
       S[r].y = eg * S[r].y + kr[r] * d[1];
       S[r].z = eg * S[r].z + kr[r] * d[2];
       S[r].w = eg * S[r].w + kr[r] * d[3];
-      *reinterpret_cast<float4 *>(Sout + (row0 + r) * kHeadDim + col0) = S[r];
+      if (kOne || tau == K - 1) *reinterpret_cast<float4 *>(Sout + (row0 + r) * kHeadDim + col0) = S[r];
     }
 
     // 6. Gated RMSNorm of the 128 readout values: each 32-lane half of wave 0
