@@ -51,7 +51,6 @@ namespace {
 constexpr int kLocalThreads = 256;        // chunk_local: 4 waves
 constexpr int kStateThreads = 512;        // chunk_state: 8 waves
 constexpr int kSlab = 32;                 // state columns per chunk_state block
-constexpr int kChunkMat = kChunk * kChunk;
 constexpr int kXcds = 8;                  // accelerator complex dies on MI355X
 // Row pitches (bytes) of blocked operands in LDS: 128 or 64 contraction
 // indices (16 or 8 blocks of 32 bytes) plus 16 bytes to spread LDS banks.
@@ -748,7 +747,8 @@ __device__ __forceinline__ void fold_norm(const PrefillParams &p, int64_t max_ch
     if (rb >= len) continue;
     const uint32_t *rdy = p.ready + t * kReadyStride;
     uint32_t cnt = __hip_atomic_load(rdy, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (int spins = 0; waiting && __builtin_amdgcn_readfirstlane(cnt) < kFoldReady; ++spins) {
+    // readfirstlane returns int: back to the counter's unsigned type.
+    for (int spins = 0; waiting && static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(cnt)) < kFoldReady; ++spins) {
       if (spins == kFoldSpins) {
         waiting = false;
         break;
@@ -756,7 +756,7 @@ __device__ __forceinline__ void fold_norm(const PrefillParams &p, int64_t max_ch
       __builtin_amdgcn_s_sleep(kFoldSleep);
       cnt = __hip_atomic_load(rdy, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    const bool ok = __builtin_amdgcn_readfirstlane(cnt) >= kFoldReady;
+    const bool ok = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(cnt)) >= kFoldReady;
     float4 o0[4], o1[4], z0[4], z1[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
